@@ -1,0 +1,13 @@
+"""CPU oracle for paged-KV decode (float64, NumPy).
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py``.  The product package never
+imports it, and it shares no code with the GPU kernels.
+"""
+from .paged_attention import (gather_contiguous, kv_head_of, merge_partitions, partition_stats,
+                              read_k_row, read_v_row, ref_decode_sequence, ref_paged_attention_decode,
+                              ref_reshape_and_cache, slot_of_position, softmax_attention, widen)
+
+__all__ = ["gather_contiguous", "kv_head_of", "merge_partitions", "partition_stats", "read_k_row",
+           "read_v_row", "ref_decode_sequence", "ref_paged_attention_decode", "ref_reshape_and_cache",
+           "slot_of_position", "softmax_attention", "widen"]

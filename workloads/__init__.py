@@ -1,0 +1,410 @@
+"""Seeded synthetic inputs for paged-KV decode.
+
+This module only *draws inputs*: random values, context lengths, block
+placement and the slots of the tokens to be written.  It holds none of the
+attention or cache-write arithmetic; both the GPU path and the CPU oracle
+consume what it returns.
+
+Five workloads are defined, shaped like the serving scenarios the pages
+discuss (GQA decode, mixed lengths under continuous batching, a shared system
+prompt, a long context):
+
+=====================  =========================================================
+``tiny_fp32``          4 sequences, context lengths {1, 15, 16, 37}, 4 q / 4 KV
+                       heads, head_dim 64, fp32, a 16-block pool assigned by a
+                       seeded permutation.
+``llama3_8b_decode``   64 sequences, 32 q / 8 KV heads, head_dim 128, bf16,
+                       lengths uniform on [128, 4096], blocks drawn in random
+                       order from a pool 1.5x the total need.
+``continuous_batching`` 256 sequences, lengths log-uniform on [16, 8192]; every
+                       step retires 5% of the sequences, admits new ones
+                       (their prompt KV is written through the cache-write
+                       call) and appends one token to every sequence.
+``shared_prefix``      128 sequences whose tables start with the same 128
+                       physical blocks (2048 tokens), then a private suffix of
+                       1..512 tokens.
+``long_context``       8 sequences of 131072 tokens, 64 q / 8 KV heads, a
+                       65536-block pool permuted at random, split-K partitions
+                       of 512 tokens.
+=====================  =========================================================
+
+Conventions (shared with the C-ABI):
+
+* Values are N(0, 1).  bf16 data is carried as ``uint16`` bit patterns, cast
+  once from fp32 with round-to-nearest-even, so that every consumer sees the
+  same bits.
+* Pool layout, per (physical block, KV head) tile:
+  K ``[num_blocks, Hkv, D/x, block_size, x]`` with ``x = 16 / element_size``;
+  V ``[num_blocks, Hkv, D, block_size]``.
+* ``context_lens`` counts the token written this step: a sequence of length
+  L has its new token at position L-1, and ``slot_mapping`` points there.
+* Every pool element that does not hold a cached token -- unused blocks, the
+  tail of a sequence's last block and the slot of the token about to be
+  written -- holds a quiet NaN, so that any read of it shows in the output.
+* Table entries past a sequence's last block point at an unused (NaN) block.
+"""
+from __future__ import annotations
+
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional, Sequence as Seq
+
+import numpy as np
+
+from paged_kv_cache_372_amd.blocks import (BlockPool, Sequence, blocks_needed,
+                                           pack_block_tables, pack_context_lens)
+
+F32_NAN_BITS = np.uint32(0x7FC00000)
+BF16_NAN_BITS = np.uint16(0x7FC0)
+
+CONFIG_NAMES = ("tiny_fp32", "llama3_8b_decode", "continuous_batching",
+                "shared_prefix", "long_context")
+# seed of configuration i (0-based) is 372 * 10 + i + 1
+DEFAULT_SEEDS = {name: 3721 + i for i, name in enumerate(CONFIG_NAMES)}
+
+_CHUNK = 1 << 22
+_STREAMS = {"k_pool": 1, "v_pool": 2, "q": 3, "k_new": 4, "v_new": 5, "k_prompt": 6, "v_prompt": 7}
+
+
+def element_size(dtype: str) -> int:
+    return {"f32": 4, "bf16": 2}[dtype]
+
+
+def chunk_elems(dtype: str) -> int:
+    """x: elements per 16-byte chunk of a K row."""
+    return 16 // element_size(dtype)
+
+
+def pool_shapes(num_blocks: int, num_kv_heads: int, head_dim: int, block_size: int, dtype: str):
+    x = chunk_elems(dtype)
+    if head_dim % x:
+        raise ValueError("head_dim must be a multiple of the 16-byte chunk")
+    return ((num_blocks, num_kv_heads, head_dim // x, block_size, x),
+            (num_blocks, num_kv_heads, head_dim, block_size))
+
+
+def np_storage_dtype(dtype: str):
+    return {"f32": np.float32, "bf16": np.uint16}[dtype]
+
+
+def bf16_bits_rne(a: np.ndarray) -> np.ndarray:
+    """Round finite fp32 values to bf16 (nearest, ties to even); returns uint16 bits."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    return ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
+
+
+def _workers() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def normal_values(n: int, dtype: str, seed: int, stream: int, substream: int = 0) -> np.ndarray:
+    """``n`` N(0,1) draws as f32, or as bf16 bits.
+
+    The draw is cut into fixed chunks, each with its own generator keyed by
+    (seed, stream, substream, chunk index), so the result does not depend on
+    the number of threads that fill it.
+    """
+    out = np.empty(n, dtype=np_storage_dtype(dtype))
+    nchunks = -(-n // _CHUNK)
+
+    def fill(c: int) -> None:
+        lo, hi = c * _CHUNK, min(n, (c + 1) * _CHUNK)
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, stream, substream, c])))
+        v = g.standard_normal(hi - lo, dtype=np.float32)
+        out[lo:hi] = v if dtype == "f32" else bf16_bits_rne(v)
+
+    if nchunks <= 1:
+        for c in range(nchunks):
+            fill(c)
+    else:
+        with ThreadPoolExecutor(_workers()) as ex:
+            list(ex.map(fill, range(nchunks)))
+    return out
+
+
+def nan_bits(dtype: str):
+    return F32_NAN_BITS if dtype == "f32" else BF16_NAN_BITS
+
+
+def poison_slots(k_pool: np.ndarray, v_pool: np.ndarray, blocks: np.ndarray, offsets: np.ndarray, dtype: str) -> None:
+    """Write NaN into every element of the given (block, offset) slots of both pools."""
+    if len(blocks) == 0:
+        return
+    kb = k_pool.view(np.uint32 if dtype == "f32" else np.uint16)
+    vb = v_pool.view(np.uint32 if dtype == "f32" else np.uint16)
+    kb[blocks, :, :, offsets, :] = nan_bits(dtype)
+    vb[blocks, :, :, offsets] = nan_bits(dtype)
+
+
+def log_uniform_lengths(rng: np.random.Generator, n: int, lo: int, hi: int) -> np.ndarray:
+    """clip(round(exp(U(ln lo, ln hi))), lo, hi)."""
+    x = np.exp(rng.uniform(math.log(lo), math.log(hi), size=n))
+    return np.clip(np.rint(x), lo, hi).astype(np.int64)
+
+
+@dataclass
+class DecodeBatch:
+    """Everything one decode step consumes.
+
+    ``k_pool``/``v_pool`` are the pools *before* this step's cache write: the
+    slots in ``slot_mapping`` still hold NaN.  ``k_new``/``v_new`` are the
+    rows to write there (``[num_tokens, Hkv, D]``).
+    """
+
+    name: str
+    seed: int
+    dtype: str
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    q: np.ndarray
+    k_new: np.ndarray
+    v_new: np.ndarray
+    slot_mapping: np.ndarray
+    k_pool: np.ndarray
+    v_pool: np.ndarray
+    block_tables: np.ndarray
+    context_lens: np.ndarray
+    scale: float
+    partition_size: int = 0
+    pad_block: int = -1
+    info: Dict[str, object] = field(default_factory=dict)
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.context_lens.shape[0])
+
+    @property
+    def max_context_len(self) -> int:
+        return int(self.context_lens.max()) if self.context_lens.size else 0
+
+    def kv_bytes(self) -> int:
+        """KV bytes decode must read: every cached token of every sequence, K and V, all KV heads."""
+        return int(self.context_lens.astype(np.int64).sum()) * 2 * self.num_kv_heads * self.head_dim * element_size(self.dtype)
+
+
+def _fill_pools(num_blocks: int, Hkv: int, D: int, bs: int, dtype: str, seed: int, substream: int = 0):
+    ks, vs = pool_shapes(num_blocks, Hkv, D, bs, dtype)
+    n = int(np.prod(ks))
+    k_pool = normal_values(n, dtype, seed, _STREAMS["k_pool"], substream).reshape(ks)
+    v_pool = normal_values(n, dtype, seed, _STREAMS["v_pool"], substream).reshape(vs)
+    return k_pool, v_pool
+
+
+def _poison_all_but(k_pool, v_pool, seqs: Seq[Sequence], upto: Seq[int], bs: int, dtype: str) -> None:
+    """NaN every slot except positions [0, upto[i]) of sequence i."""
+    nb = k_pool.shape[0]
+    valid = np.zeros((nb, bs), dtype=bool)
+    for s, n in zip(seqs, upto):
+        if n <= 0:
+            continue
+        pos = np.arange(n)
+        blk = np.asarray(s.blocks, dtype=np.int64)[pos // bs]
+        valid[blk, pos % bs] = True
+    b, o = np.nonzero(~valid)
+    poison_slots(k_pool, v_pool, b, o, dtype)
+
+
+def build_static(name: str, seed: int, dtype: str, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                 lengths: Seq[int], num_blocks: int, block_size: int = 16, scale: Optional[float] = None,
+                 shared_prefix_tokens: int = 0, table_width: Optional[int] = None,
+                 partition_size: int = 0, order_rng: Optional[np.random.Generator] = None) -> DecodeBatch:
+    """Build one decode step over sequences of the given context lengths.
+
+    Blocks are handed out by a ``BlockPool`` whose free list is a seeded
+    permutation of the pool.  With ``shared_prefix_tokens`` > 0 (a multiple
+    of the block size) every table starts with the same physical blocks.
+    """
+    bs = block_size
+    lengths = [int(L) for L in lengths]
+    if order_rng is None:
+        order_rng = np.random.default_rng([seed, 100])
+    pool = BlockPool(num_blocks, bs, order=order_rng.permutation(num_blocks))
+    if shared_prefix_tokens % bs:
+        raise ValueError("shared prefix must be whole blocks")
+    prefix_blocks: List[int] = pool.allocate(shared_prefix_tokens // bs) if shared_prefix_tokens else []
+    seqs: List[Sequence] = []
+    slots = np.empty(len(lengths), dtype=np.int64)
+    for i, L in enumerate(lengths):
+        if L < 1:
+            raise ValueError("every sequence carries its new token (context_len >= 1)")
+        s = Sequence(i)
+        if prefix_blocks:
+            if L <= shared_prefix_tokens:
+                raise ValueError("the new token must fall past the shared prefix")
+            if i > 0:
+                pool.share(prefix_blocks)
+            s.blocks = list(prefix_blocks)
+            s.num_tokens = shared_prefix_tokens
+        s.reserve(pool, L - s.num_tokens)
+        slots[i] = s.slot_of(L - 1, bs)
+        seqs.append(s)
+
+    k_pool, v_pool = _fill_pools(num_blocks, num_kv_heads, head_dim, bs, dtype, seed)
+    _poison_all_but(k_pool, v_pool, seqs, [L - 1 for L in lengths], bs, dtype)
+
+    width = table_width if table_width is not None else max(blocks_needed(L, bs) for L in lengths)
+    free = pool.free_ids()
+    pad = free[0] if free else -1
+    if pad < 0 and any(len(s.blocks) < width for s in seqs):
+        raise ValueError("table padding needs an unused (poisoned) block")
+    bt = pack_block_tables(seqs, width, pad if pad >= 0 else 0)
+
+    B = len(lengths)
+    q = normal_values(B * num_q_heads * head_dim, dtype, seed, _STREAMS["q"]).reshape(B, num_q_heads, head_dim)
+    k_new = normal_values(B * num_kv_heads * head_dim, dtype, seed, _STREAMS["k_new"]).reshape(B, num_kv_heads, head_dim)
+    v_new = normal_values(B * num_kv_heads * head_dim, dtype, seed, _STREAMS["v_new"]).reshape(B, num_kv_heads, head_dim)
+    return DecodeBatch(name=name, seed=seed, dtype=dtype, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
+                       head_dim=head_dim, block_size=bs, num_blocks=num_blocks, q=q, k_new=k_new, v_new=v_new,
+                       slot_mapping=slots, k_pool=k_pool, v_pool=v_pool, block_tables=bt,
+                       context_lens=pack_context_lens(seqs),
+                       scale=float(scale if scale is not None else 1.0 / math.sqrt(head_dim)),
+                       partition_size=partition_size, pad_block=pad,
+                       info={"refcount": pool.refcount.copy(), "prefix_blocks": list(prefix_blocks)})
+
+
+def pool_blocks_for(lengths: Seq[int], bs: int, factor: float = 1.5, extra_blocks: int = 0) -> int:
+    return int(math.ceil(factor * (sum(blocks_needed(L, bs) for L in lengths) + extra_blocks)))
+
+
+def tiny_fp32(seed: int = DEFAULT_SEEDS["tiny_fp32"]) -> DecodeBatch:
+    """4 sequences {1, 15, 16, 37}, 4/4 heads, D = 64, fp32, 16-block pool."""
+    return build_static("tiny_fp32", seed, "f32", 4, 4, 64, [1, 15, 16, 37], num_blocks=16,
+                        scale=1.0 / math.sqrt(64.0))
+
+
+def llama3_8b_decode(seed: int = DEFAULT_SEEDS["llama3_8b_decode"], num_seqs: int = 64,
+                     lmin: int = 128, lmax: int = 4096, partition_size: int = 0) -> DecodeBatch:
+    rng = np.random.default_rng([seed, 0])
+    lengths = rng.integers(lmin, lmax, size=num_seqs, endpoint=True)
+    nb = pool_blocks_for(lengths, 16)
+    return build_static("llama3_8b_decode", seed, "bf16", 32, 8, 128, lengths, num_blocks=nb,
+                        table_width=blocks_needed(lmax, 16), partition_size=partition_size)
+
+
+def shared_prefix(seed: int = DEFAULT_SEEDS["shared_prefix"], num_seqs: int = 128, prefix_blocks: int = 128,
+                  suffix_max: int = 512, partition_size: int = 0) -> DecodeBatch:
+    rng = np.random.default_rng([seed, 0])
+    suffix = rng.integers(1, suffix_max, size=num_seqs, endpoint=True)
+    prefix = prefix_blocks * 16
+    lengths = prefix + suffix
+    unique = prefix_blocks + sum(blocks_needed(int(s), 16) for s in suffix)
+    nb = int(math.ceil(1.5 * unique))
+    return build_static("shared_prefix", seed, "bf16", 32, 8, 128, lengths, num_blocks=nb,
+                        shared_prefix_tokens=prefix, table_width=blocks_needed(prefix + suffix_max, 16),
+                        partition_size=partition_size)
+
+
+def long_context(seed: int = DEFAULT_SEEDS["long_context"], num_seqs: int = 8, context_len: int = 131072,
+                 num_q_heads: int = 64, partition_size: int = 512) -> DecodeBatch:
+    nb = num_seqs * blocks_needed(context_len, 16)
+    return build_static("long_context", seed, "bf16", num_q_heads, 8, 128, [context_len] * num_seqs,
+                        num_blocks=nb, partition_size=partition_size)
+
+
+@dataclass
+class BatchingStep:
+    """Inputs of one continuous-batching step.
+
+    The cache write of the step covers the prompts of the sequences admitted
+    this step followed by the one appended token of every live sequence;
+    ``k_write``/``v_write``/``slot_mapping`` hold them in that order.
+    """
+
+    step: int
+    retired: List[int]
+    admitted: List[int]
+    k_write: np.ndarray
+    v_write: np.ndarray
+    slot_mapping: np.ndarray
+    q: np.ndarray
+    block_tables: np.ndarray
+    context_lens: np.ndarray
+    num_prompt_tokens: int
+
+
+class ContinuousBatching:
+    """Continuous-batching mix: retire, admit, append one token, decode.
+
+    ``initial_pools()`` returns the pools holding the prompts of the starting
+    sequences; ``step(i)`` advances the host block manager and returns the
+    step's inputs.  Steps must be taken in order 0, 1, 2, ...
+    """
+
+    name = "continuous_batching"
+
+    def __init__(self, seed: int = DEFAULT_SEEDS["continuous_batching"], num_seqs: int = 256,
+                 num_q_heads: int = 32, num_kv_heads: int = 8, head_dim: int = 128, block_size: int = 16,
+                 steps: int = 10, replace_frac: float = 0.05, lmin: int = 16, lmax: int = 8192,
+                 dtype: str = "bf16", partition_size: int = 0):
+        self.seed, self.dtype = seed, dtype
+        self.B, self.Hq, self.Hkv, self.D, self.bs = num_seqs, num_q_heads, num_kv_heads, head_dim, block_size
+        self.steps, self.lmin, self.lmax = steps, lmin, lmax
+        self.n_replace = int(round(replace_frac * num_seqs))
+        self.partition_size = partition_size
+        self.scale = 1.0 / math.sqrt(head_dim)
+        self.rng = np.random.default_rng([seed, 0])
+        L0 = log_uniform_lengths(self.rng, num_seqs, lmin, lmax)
+        self.num_blocks = pool_blocks_for(L0, block_size)
+        self.table_width = blocks_needed(lmax + steps, block_size)
+        self.pool = BlockPool(self.num_blocks, block_size,
+                              order=np.random.default_rng([seed, 100]).permutation(self.num_blocks))
+        self.seqs: List[Sequence] = []
+        self._next_id = 0
+        for L in L0:
+            s = Sequence(self._next_id)
+            self._next_id += 1
+            s.reserve(self.pool, int(L))
+            self.seqs.append(s)
+        self._initial_lengths = [int(L) for L in L0]
+        self._step = 0
+
+    def initial_pools(self):
+        k_pool, v_pool = _fill_pools(self.num_blocks, self.Hkv, self.D, self.bs, self.dtype, self.seed)
+        _poison_all_but(k_pool, v_pool, self.seqs, self._initial_lengths, self.bs, self.dtype)
+        return k_pool, v_pool
+
+    def step(self, i: int) -> BatchingStep:
+        if i != self._step:
+            raise ValueError(f"steps must be taken in order (expected {self._step})")
+        self._step += 1
+        rng = np.random.default_rng([self.seed, 1, i])
+        idx = sorted(rng.choice(self.B, size=self.n_replace, replace=False).tolist())
+        retired = [self.seqs[j].seq_id for j in idx]
+        for j in idx:
+            self.seqs[j].release(self.pool)
+        new_L = log_uniform_lengths(rng, len(idx), self.lmin, self.lmax)
+        prompt_slots = []
+        admitted = []
+        for j, L in zip(idx, new_L):
+            s = Sequence(self._next_id)
+            self._next_id += 1
+            prompt_slots.append(s.reserve(self.pool, int(L)))
+            self.seqs[j] = s
+            admitted.append(s.seq_id)
+        n_prompt = int(sum(len(p) for p in prompt_slots))
+        append_slots = np.array([s.append_slot(self.pool) for s in self.seqs], dtype=np.int64)
+        slots = np.concatenate(prompt_slots + [append_slots]) if prompt_slots else append_slots
+        T = slots.shape[0]
+        row = self.Hkv * self.D
+        k_write = normal_values(T * row, self.dtype, self.seed, _STREAMS["k_prompt"], 1000 + i).reshape(T, self.Hkv, self.D)
+        v_write = normal_values(T * row, self.dtype, self.seed, _STREAMS["v_prompt"], 1000 + i).reshape(T, self.Hkv, self.D)
+        q = normal_values(self.B * self.Hq * self.D, self.dtype, self.seed, _STREAMS["q"], 1000 + i).reshape(self.B, self.Hq, self.D)
+        free = self.pool.free_ids()
+        bt = pack_block_tables(self.seqs, self.table_width, free[0] if free else 0)
+        return BatchingStep(step=i, retired=retired, admitted=admitted, k_write=k_write, v_write=v_write,
+                            slot_mapping=slots, q=q, block_tables=bt, context_lens=pack_context_lens(self.seqs),
+                            num_prompt_tokens=n_prompt)
+
+
+def build(name: str, seed: Optional[int] = None, **kw):
+    """Static workloads by name (``continuous_batching`` returns the simulator)."""
+    seed = DEFAULT_SEEDS[name] if seed is None else seed
+    if name == "continuous_batching":
+        return ContinuousBatching(seed=seed, **kw)
+    return {"tiny_fp32": tiny_fp32, "llama3_8b_decode": llama3_8b_decode, "shared_prefix": shared_prefix,
+            "long_context": long_context}[name](seed=seed, **kw)
