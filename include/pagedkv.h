@@ -1,0 +1,182 @@
+/*
+ * pagedkv.h -- C ABI of libpagedkv.so: paged-KV cache write and decode
+ * attention on AMD MI355X (gfx950).
+ *
+ * The problem statement comes from the pages on PagedAttention:
+ *   - the KV cache of a sequence is cut into fixed-size blocks that live in
+ *     one large pool allocated once at start-up (architvora, "Just a python
+ *     process"; runbyai, section 3 "The core idea of PagedAttention");
+ *   - a per-sequence block table maps logical blocks to physical ones
+ *     (ai-hpc, "2.1 Algorithm Principle");
+ *   - each decode step the engine packs the tables into tensors and sends
+ *     them to the GPU, where the kernel follows that map to gather the blocks
+ *     (architvora, "Just a python process" and "Paged Attention");
+ *   - decode: the one new token of each sequence attends over the keys and
+ *     values of all its earlier tokens (runbyai, section 1).
+ *
+ * Conventions for every call:
+ *   - Pointers marked [device] are device addresses (e.g. from a torch CUDA
+ *     tensor); the caller owns all memory.  The library never allocates,
+ *     frees or synchronises, and keeps no state between calls.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream).  A returned PKV_OK means the work was enqueued.
+ *   - Problems visible on the host (null pointer, bad size, unsupported
+ *     shape or dtype, workspace too small) return an error status before any
+ *     GPU work is enqueued; the message is in pkv_last_error().  A failed
+ *     launch returns PKV_ERR_HIP.  No C++ exception crosses the ABI.
+ *   - Values that live on the device are never validated on the host (that
+ *     would need a synchronisation).  Kernels guard every address instead:
+ *     a slot or physical block id outside the pool is skipped, and context
+ *     lengths are clamped to [0, min(max_context_len,
+ *     max_blocks_per_seq * block_size)].
+ *   - Thread-safe: calls may come from several host threads at once.
+ *
+ * Element types: PKV_F32 (IEEE binary32) or PKV_BF16 (bfloat16, 16-bit).
+ * Tensors are dense, row-major, with the shapes given below.
+ *
+ * KV pool layout (one K pool and one V pool, shape fixed at allocation):
+ *   k_cache [num_blocks][num_kv_heads][head_dim/x][block_size][x],
+ *           x = 16 / element_size (4 for f32, 8 for bf16): the head_dim
+ *           values of a token are split into 16-byte chunks, and the chunks
+ *           of the 16 tokens of a block are stored chunk-major;
+ *   v_cache [num_blocks][num_kv_heads][head_dim][block_size]: for each dim,
+ *           the block's tokens are contiguous.
+ * A flat slot index is  physical_block * block_size + offset_in_block.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pkv_status {
+    PKV_OK = 0,
+    PKV_ERR_INVALID_ARG = 1,  /* null pointer, negative or inconsistent size */
+    PKV_ERR_UNSUPPORTED = 2,  /* shape or dtype this build does not handle   */
+    PKV_ERR_WORKSPACE = 3,    /* workspace missing or too small              */
+    PKV_ERR_HIP = 4           /* the HIP runtime reported an error           */
+} pkv_status;
+
+typedef enum pkv_dtype {
+    PKV_F32 = 0,
+    PKV_BF16 = 1
+} pkv_dtype;
+
+/* Version of this ABI (bumped on any incompatible change). */
+int32_t pkv_abi_version(void);
+
+/*
+ * Cache write: for every token t in [0, num_tokens) with slot_mapping[t] >= 0,
+ * copy k_new[t][h][:] and v_new[t][h][:] for every KV head h into the pool
+ * slot slot_mapping[t] (block = slot / block_size, offset = slot % block_size),
+ * bit for bit.  This is the "cache the key/value of every token" step of
+ * runbyai section 1 / section 2, addressed through the paged layout.
+ *
+ *   k_new, v_new   [device] [num_tokens][num_kv_heads][head_dim], dtype
+ *   slot_mapping   [device] int64 [num_tokens]; negative = skip (padding);
+ *                  slots >= num_blocks * block_size are skipped as well
+ *   k_cache, v_cache [device] pools in the layout above, num_blocks blocks
+ *   head_dim       64 or 128;  block_size 16;  dtype PKV_F32 or PKV_BF16
+ * Two tokens must not name the same slot (the write order between them is
+ * unspecified).  num_tokens == 0 is a no-op.
+ */
+pkv_status pkv_reshape_and_cache(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                                 void* k_cache, void* v_cache, int64_t num_tokens, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int64_t num_blocks, pkv_dtype dtype,
+                                 void* stream);
+
+/*
+ * Partition size (in tokens) the decode uses when it is passed 0.  The
+ * result is a multiple of block_size in [block_size, 1024]; when
+ * max_context_len fits in one partition there is no split.
+ */
+int32_t pkv_decode_auto_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t max_context_len);
+
+/*
+ * Bytes of device workspace the decode needs for these sizes (0 when the
+ * context fits in one partition).  partition_size 0 = automatic, as above.
+ * Layout (all fp32): o[num_seqs][num_q_heads][P][head_dim], then
+ * m[num_seqs][num_q_heads][P], then l[num_seqs][num_q_heads][P], with
+ * P = ceil(max_context_len / partition_size).  Returns 0 for invalid sizes.
+ */
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t max_context_len, int32_t partition_size);
+
+/*
+ * Decode attention over the paged cache (runbyai sections 1 and 3;
+ * ai-hpc 2.1; architvora "Paged Attention": the kernel follows each
+ * sequence's block table to gather its blocks).  For sequence s and query
+ * head h, with L = context_lens[s] and g = h / (num_q_heads / num_kv_heads):
+ *     out[s][h][:] = sum_i softmax_i(scale * <q[s][h], K_i>) * V_i,
+ * over the tokens i < L of sequence s, K_i / V_i the KV-head-g rows of token
+ * i read through block_tables[s][i / block_size] at offset i % block_size.
+ * L == 0 gives zeros.  Accumulation is fp32; with bf16 KV the products of
+ * the softmax weights with V use the weights split into two bf16 terms.
+ *
+ *   q              [device] [num_seqs][num_q_heads][head_dim], kv_dtype
+ *   k_cache, v_cache [device] pools (layout above), kv_dtype
+ *   block_tables   [device] int32 [num_seqs][max_blocks_per_seq]; entries
+ *                  past a sequence's last block are never read
+ *   context_lens   [device] int32 [num_seqs], counting the token written
+ *                  this step
+ *   out            [device] [num_seqs][num_q_heads][head_dim], out_dtype
+ *                  (PKV_F32 or PKV_BF16, rounded to nearest even)
+ *   num_q_heads    a multiple of num_kv_heads
+ *   head_dim 64 or 128; block_size 16; num_blocks = pool size in blocks
+ *   max_context_len  host-known upper bound of context_lens (sizes the grid)
+ *   partition_size   0 (auto) or a multiple of block_size in [16, 1024]
+ *   workspace      [device] >= pkv_decode_workspace_bytes(...) bytes,
+ *                  256-byte aligned; may be NULL when that is 0
+ * Long contexts are split into partitions of partition_size tokens whose
+ * partial softmax statistics are merged by a second kernel on the same
+ * stream (log-sum-exp rescaling).  Results are deterministic: the order of
+ * every sum depends only on logical token positions, never on where blocks
+ * sit in the pool.
+ */
+pkv_status pkv_paged_attention_decode(const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* block_tables, const int32_t* context_lens, float scale,
+                                      void* out, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                      int32_t max_blocks_per_seq, int32_t max_context_len,
+                                      int32_t partition_size, void* workspace, size_t workspace_bytes,
+                                      pkv_dtype kv_dtype, pkv_dtype out_dtype, void* stream);
+
+/*
+ * The two launches of pkv_paged_attention_decode, callable one at a time
+ * (same arguments and meaning).  _partitions runs the block-table walk and
+ * writes `out` for sequences that fit in one partition and the fp32
+ * partials for the others; _reduce merges those partials into `out` and
+ * must follow _partitions on the same stream with the same arguments.
+ * _reduce is a no-op when no split is needed.
+ */
+pkv_status pkv_paged_attention_decode_partitions(const void* q, const void* k_cache, const void* v_cache,
+                                                 const int32_t* block_tables, const int32_t* context_lens,
+                                                 float scale, void* out, int32_t num_seqs, int32_t num_q_heads,
+                                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                                 int64_t num_blocks, int32_t max_blocks_per_seq,
+                                                 int32_t max_context_len, int32_t partition_size, void* workspace,
+                                                 size_t workspace_bytes, pkv_dtype kv_dtype, pkv_dtype out_dtype,
+                                                 void* stream);
+
+pkv_status pkv_paged_attention_decode_reduce(const int32_t* context_lens, void* out, int32_t num_seqs,
+                                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                             int32_t block_size, int32_t max_blocks_per_seq,
+                                             int32_t max_context_len, int32_t partition_size, void* workspace,
+                                             size_t workspace_bytes, pkv_dtype out_dtype, void* stream);
+
+/* Static description of a status code.  Never NULL. */
+const char* pkv_status_string(pkv_status status);
+
+/* Message of the last failed call on this host thread ("" if none). */
+const char* pkv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -1,0 +1,236 @@
+// Paged decode attention, bf16 KV, on the gfx950 matrix cores.
+//
+// What is computed: for one sequence, one KV head and the query heads that
+// share it (grouped-query attention), walk the sequence's block table over
+// one partition of its context, and produce softmax(scale q K^T) V for that
+// partition (runbyai section 1: decode attends over the cached KV of all
+// earlier tokens; architvora "Paged Attention": the kernel follows the block
+// table to gather the blocks).  Long contexts are split into partitions
+// whose (max, sum, unnormalised output) statistics are merged by
+// splitk_reduce.hip.
+//
+// Work decomposition: one wave64 per unit (partition, sequence, head group,
+// KV head).  The unit id puts the KV head in the lowest digit, so with 8 KV
+// heads consecutive workgroups -- dealt round-robin to the 8 XCDs -- keep
+// each KV head on one XCD and its L2 (shared-prefix blocks stay resident).
+//
+// Per 16-token block, per wave:
+//   S[16 tok x 16 heads] = K[16 x D] . Q^T[D x 16]  D/32 x mfma_f32_16x16x32_bf16
+//   online softmax on S (exp2 domain, scale*log2e folded in)
+//   O^T[D x 16 heads]  += V^T[D x 16] . P^T[16 x 16]   D/16 x 2 x mfma_f32_16x16x16_bf16
+// P is fed as two bf16 terms (hi + lo), so the PV product carries about 16
+// mantissa bits of the fp32 weights.  Unused head columns (group < 16) cost
+// matrix-core cycles only; the kernel is bound by HBM, not by the MFMA pipe.
+//
+// Why the pool layout is what it is: the MFMA A operand wants, in lane l,
+// 8 consecutive K values of token (l % 16); with K stored as 16-byte chunks
+// chunk-major inside a block ([D/8][16][8]), load kk of a wave reads one
+// contiguous 1 KiB run.  The PV A operand wants 4 consecutive tokens of one
+// dim; with V stored dim-major ([D][16]) each load reads a contiguous 512 B
+// run.  The QK result layout (lane: head l%16, tokens 4(l/16)..+3) is
+// exactly the PV B-operand layout, so no data moves between the two.
+#include "kernels.h"
+
+namespace pkv {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+template <int D>
+struct BlockRegs {
+    uint4 k[D / 32];   // K chunks: load kk holds chunk 4kk + lane/16 of token lane%16
+    uint2 v[D / 16];   // V^T: load c holds dim 16c + lane%16, tokens 4(lane/16)..+3
+};
+
+template <int D>
+__device__ __forceinline__ void load_block(BlockRegs<D>& r, const uint16_t* __restrict__ k_head,
+                                           const uint16_t* __restrict__ v_head, int64_t block_stride,
+                                           int pb, int lane) {
+    const uint4* kt = reinterpret_cast<const uint4*>(k_head + (int64_t)pb * block_stride);
+    const uint2* vt = reinterpret_cast<const uint2*>(v_head + (int64_t)pb * block_stride);
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) r.k[kk] = kt[kk * 64 + lane];
+    const int vo = (lane & 15) * 4 + (lane >> 4);
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) r.v[c] = vt[c * 64 + vo];
+}
+
+struct SoftmaxState {
+    float m;   // running max (log2 units), same in all lanes of a head column
+    float l;   // this lane's share of sum 2^(s - m)
+};
+
+template <int D>
+__device__ __forceinline__ void compute_block(const BlockRegs<D>& r, const bf16x8_t* qop, float4_t* acc,
+                                              SoftmaxState& st, int valid_n, float scale_log2, int g) {
+    // S = K . Q^T: lane holds S[token 4g + i][head lane%16], i = 0..3
+    float4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk)
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.k[kk]), qop[kk], sacc, 0, 0, 0);
+
+    float sv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sv[i] = (4 * g + i < valid_n) ? sacc[i] * scale_log2 : -INFINITY;
+    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(st.m, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = exp2_fast(st.m - m_use);
+    float pr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pr[i] = exp2_fast(sv[i] - m_use);
+    st.l = st.l * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+    st.m = m_new;
+
+    // P^T as B operand, split into bf16 hi + lo terms
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        hi[i] = f32_to_bf16_bits(pr[i]);
+        lo[i] = f32_to_bf16_bits(pr[i] - bf16_bits_to_f32(hi[i]));
+    }
+    const short4_t p_hi = __builtin_bit_cast(short4_t, make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)));
+    const short4_t p_lo = __builtin_bit_cast(short4_t, make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)));
+
+    // tokens past the end hold stale or NaN data: zero them (0 * NaN = NaN)
+    uint32_t vm0 = 0xFFFFFFFFu, vm1 = 0xFFFFFFFFu;
+    if (valid_n < 16) {
+        const int nv = valid_n - 4 * g;
+        vm0 = nv >= 2 ? 0xFFFFFFFFu : (nv == 1 ? 0x0000FFFFu : 0u);
+        vm1 = nv >= 4 ? 0xFFFFFFFFu : (nv == 3 ? 0x0000FFFFu : 0u);
+    }
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+        acc[c] *= alpha;
+        const short4_t a = __builtin_bit_cast(short4_t, make_uint2(r.v[c].x & vm0, r.v[c].y & vm1));
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, p_hi, acc[c], 0, 0, 0);
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, p_lo, acc[c], 0, 0, 0);
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void decode_bf16_mfma_kernel(DecodeParams p) {
+    const int lane = threadIdx.x;
+    const int col = lane & 15;  // head column of the MFMA tiles
+    const int g = lane >> 4;    // lane group
+
+    int64_t u = blockIdx.x;
+    const int kvh = (int)(u % p.num_kv_heads);
+    u /= p.num_kv_heads;
+    const int hg = (int)(u % p.n_head_groups);
+    u /= p.n_head_groups;
+    const int s = (int)(u % p.num_seqs);
+    const int part = (int)(u / p.num_seqs);
+
+    const int L = clamp_ctx(p.context_lens[s], p.ctx_cap);
+    const int n_blk = (L + kBlockSize - 1) / kBlockSize;
+    const int n_parts = (n_blk + p.part_blocks - 1) / p.part_blocks;
+    const int h0 = kvh * p.group + hg * kMfmaHeadsPerUnit;
+    const int nh = min(kMfmaHeadsPerUnit, p.group - hg * kMfmaHeadsPerUnit);
+    const int Hq = p.num_q_heads;
+
+    if (n_parts == 0) {  // empty context: zeros
+        if (part != 0) return;
+        for (int idx = lane; idx < nh * D; idx += 64) {
+            const int64_t o = ((int64_t)s * Hq + h0) * D + idx;
+            if (p.out_bf16) reinterpret_cast<uint16_t*>(p.out)[o] = 0;
+            else reinterpret_cast<float*>(p.out)[o] = 0.f;
+        }
+        return;
+    }
+    if (part >= n_parts) return;
+
+    const int blk0 = part * p.part_blocks;
+    const int nb = min(p.part_blocks, n_blk - blk0);
+
+    // Q^T as the B operand: column = head, k-group g holds chunk 4kk + g
+    bf16x8_t qop[D / 32];
+    {
+        const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) + ((int64_t)s * Hq + h0 + col) * D;
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk) {
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (col < nh) v = reinterpret_cast<const uint4*>(qrow)[4 * kk + g];
+            qop[kk] = __builtin_bit_cast(bf16x8_t, v);
+        }
+    }
+
+    // this partition's slice of the block table, one entry per lane
+    const int32_t* bt = p.block_tables + (int64_t)s * p.max_blocks_per_seq + blk0;
+    const int bt_lane = lane < nb ? bt[lane] : 0;
+
+    const int64_t block_stride = (int64_t)p.num_kv_heads * D * kBlockSize;
+    const uint16_t* k_head = reinterpret_cast<const uint16_t*>(p.k_cache) + (int64_t)kvh * D * kBlockSize;
+    const uint16_t* v_head = reinterpret_cast<const uint16_t*>(p.v_cache) + (int64_t)kvh * D * kBlockSize;
+
+    float4_t acc[D / 16];
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) acc[c] = {0.f, 0.f, 0.f, 0.f};
+    SoftmaxState st{-INFINITY, 0.f};
+
+    auto block_of = [&](int j, int& valid_n) {
+        const int pb = __builtin_amdgcn_readlane(bt_lane, j);
+        const bool ok = pb >= 0 && (int64_t)pb < p.num_blocks;
+        valid_n = ok ? L - (blk0 + j) * kBlockSize : 0;
+        return ok ? pb : 0;
+    };
+
+    BlockRegs<D> ra, rb;
+    int va, vb;
+    load_block<D>(ra, k_head, v_head, block_stride, block_of(0, va), lane);
+    for (int j = 0; j < nb; j += 2) {
+        if (j + 1 < nb) load_block<D>(rb, k_head, v_head, block_stride, block_of(j + 1, vb), lane);
+        compute_block<D>(ra, qop, acc, st, va, p.scale_log2, g);
+        if (j + 1 >= nb) break;
+        if (j + 2 < nb) load_block<D>(ra, k_head, v_head, block_stride, block_of(j + 2, va), lane);
+        compute_block<D>(rb, qop, acc, st, vb, p.scale_log2, g);
+    }
+
+    float l_tot = st.l + __shfl_xor(st.l, 16);
+    l_tot = l_tot + __shfl_xor(l_tot, 32);
+    if (col >= nh) return;
+    const int h = h0 + col;
+
+    if (n_parts == 1) {
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        const int64_t ob = ((int64_t)s * Hq + h) * D + 4 * g;
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) {
+            const float o0 = acc[c][0] * inv, o1 = acc[c][1] * inv, o2 = acc[c][2] * inv, o3 = acc[c][3] * inv;
+            if (p.out_bf16) {
+                const uint2 w = make_uint2(f32_to_bf16_bits(o0) | (f32_to_bf16_bits(o1) << 16),
+                                           f32_to_bf16_bits(o2) | (f32_to_bf16_bits(o3) << 16));
+                *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + ob + 16 * c) = w;
+            } else {
+                *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + ob + 16 * c) = make_float4(o0, o1, o2, o3);
+            }
+        }
+    } else {
+        const int64_t row = ((int64_t)s * Hq + h) * p.num_parts + part;
+        float* o = p.o_part + row * D + 4 * g;
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c)
+            *reinterpret_cast<float4*>(o + 16 * c) = make_float4(acc[c][0], acc[c][1], acc[c][2], acc[c][3]);
+        if (g == 0) {
+            p.m_part[row] = st.m;
+            p.l_part[row] = l_tot;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_decode_bf16_mfma(const DecodeParams& p, hipStream_t stream) {
+    const int64_t units = decode_units(p);
+    if (units == 0) return hipSuccess;
+    const dim3 grid((unsigned)units), block(64);
+    if (p.head_dim == 128) hipLaunchKernelGGL(decode_bf16_mfma_kernel<128>, grid, block, 0, stream, p);
+    else hipLaunchKernelGGL(decode_bf16_mfma_kernel<64>, grid, block, 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace pkv

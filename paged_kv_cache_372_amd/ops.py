@@ -1,0 +1,217 @@
+"""Python binding of libpagedkv.so (ctypes).
+
+Argument marshalling only: every step of the cache write and of decode
+attention runs in the library's HIP kernels.  Torch provides device memory
+and the current stream; the functions check device, dtype, shape and
+contiguity, then pass raw pointers to the C ABI declared in
+``include/pagedkv.h``.  There is no fallback: if the library is not built,
+or a call fails, a ``RuntimeError`` is raised.
+
+Pool layout (see the header): ``k_cache [num_blocks, Hkv, D/x, 16, x]`` with
+``x = 16 / element_size`` and ``v_cache [num_blocks, Hkv, D, 16]``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
+BLOCK_SIZE = 16
+
+PKV_F32, PKV_BF16 = 0, 1
+_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace", 4: "HIP error"}
+
+_lib = None
+
+_vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+
+_SIGNATURES = {
+    "pkv_abi_version": (_i32, []),
+    "pkv_reshape_and_cache": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _i32, _vp]),
+    "pkv_decode_auto_partition_size": (_i32, [_i32, _i32, _i32, _i32, _i32]),
+    "pkv_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "pkv_paged_attention_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _f32, _vp, _i32, _i32, _i32, _i32, _i32, _i64,
+                                          _i32, _i32, _i32, _vp, _sz, _i32, _i32, _vp]),
+    "pkv_paged_attention_decode_partitions": (_i32, [_vp, _vp, _vp, _vp, _vp, _f32, _vp, _i32, _i32, _i32, _i32, _i32,
+                                                     _i64, _i32, _i32, _i32, _vp, _sz, _i32, _i32, _vp]),
+    "pkv_paged_attention_decode_reduce": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _sz,
+                                                 _i32, _vp]),
+    "pkv_status_string": (ctypes.c_char_p, [_i32]),
+    "pkv_last_error": (ctypes.c_char_p, []),
+}
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libpagedkv.so (after torch, so it binds to torch's HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run `python -m paged_kv_cache_372_amd.build` "
+                           "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        lib = load_library()
+        msg = lib.pkv_last_error().decode(errors="replace")
+        raise RuntimeError(f"{what} failed: {_STATUS.get(status, status)}: {msg}")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return PKV_F32
+    if t.dtype == torch.bfloat16:
+        return PKV_BF16
+    raise ValueError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _ptr(t: torch.Tensor) -> int:
+    return t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _require(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check_tensor(t: torch.Tensor, name: str, device: torch.device) -> None:
+    _require(isinstance(t, torch.Tensor), f"{name} must be a tensor")
+    _require(t.device == device, f"{name} is on {t.device}, expected {device}")
+    _require(t.is_contiguous(), f"{name} must be contiguous")
+
+
+def pool_shapes(num_blocks: int, num_kv_heads: int, head_dim: int, dtype: torch.dtype) -> Tuple[tuple, tuple]:
+    """Shapes of the K and V pools for this library's layout."""
+    x = 16 // torch.empty((), dtype=dtype).element_size()
+    return ((num_blocks, num_kv_heads, head_dim // x, BLOCK_SIZE, x), (num_blocks, num_kv_heads, head_dim, BLOCK_SIZE))
+
+
+def _pool_dims(k_cache: torch.Tensor, v_cache: torch.Tensor) -> Tuple[int, int, int]:
+    _require(k_cache.dim() == 5 and v_cache.dim() == 4, "k_cache must be 5-D and v_cache 4-D (see pool_shapes)")
+    nb, hkv, nch, bs, x = k_cache.shape
+    D = nch * x
+    _require(bs == BLOCK_SIZE, f"block_size must be {BLOCK_SIZE}")
+    _require(x * k_cache.element_size() == 16, "k_cache last dim must span 16 bytes")
+    _require(tuple(v_cache.shape) == (nb, hkv, D, bs), f"v_cache shape {tuple(v_cache.shape)} != {(nb, hkv, D, bs)}")
+    _require(k_cache.dtype == v_cache.dtype, "k_cache and v_cache dtypes differ")
+    return nb, hkv, D
+
+
+def reshape_and_cache(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
+                      k_cache: torch.Tensor, v_cache: torch.Tensor) -> None:
+    """Write k_new/v_new ``[T, Hkv, D]`` into the pools at ``slot_mapping`` (int64 ``[T]``)."""
+    lib = load_library()
+    dev = k_cache.device
+    for t, n in ((k_new, "k_new"), (v_new, "v_new"), (slot_mapping, "slot_mapping"), (k_cache, "k_cache"),
+                 (v_cache, "v_cache")):
+        _check_tensor(t, n, dev)
+    nb, hkv, D = _pool_dims(k_cache, v_cache)
+    _require(k_new.dim() == 3 and tuple(k_new.shape[1:]) == (hkv, D), f"k_new must be [T, {hkv}, {D}]")
+    _require(v_new.shape == k_new.shape, "v_new shape must match k_new")
+    _require(k_new.dtype == k_cache.dtype and v_new.dtype == k_cache.dtype, "new K/V dtype must match the pools")
+    _require(slot_mapping.dtype == torch.int64 and slot_mapping.shape == (k_new.shape[0],),
+             "slot_mapping must be int64 [T]")
+    st = lib.pkv_reshape_and_cache(_ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(k_cache), _ptr(v_cache),
+                                   k_new.shape[0], hkv, D, BLOCK_SIZE, nb, _dtype_code(k_cache), _stream(dev))
+    _check(st, "reshape_and_cache")
+
+
+def decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                           max_context_len: int, partition_size: int = 0) -> int:
+    return int(load_library().pkv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                         max_context_len, partition_size))
+
+
+def auto_partition_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                        max_context_len: int) -> int:
+    return int(load_library().pkv_decode_auto_partition_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                              max_context_len))
+
+
+class _DecodeArgs:
+    """Validated decode arguments, reused by the one-call and two-phase entry points."""
+
+    def __init__(self, q, k_cache, v_cache, block_tables, context_lens, scale, out, partition_size,
+                 max_context_len, workspace):
+        dev = q.device
+        for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (block_tables, "block_tables"),
+                     (context_lens, "context_lens"), (out, "out")):
+            _check_tensor(t, n, dev)
+        nb, hkv, D = _pool_dims(k_cache, v_cache)
+        _require(q.dim() == 3 and q.shape[2] == D, f"q must be [B, Hq, {D}]")
+        B, hq = q.shape[0], q.shape[1]
+        _require(q.dtype == k_cache.dtype, "q dtype must match the pools")
+        _require(tuple(out.shape) == tuple(q.shape), "out must have q's shape")
+        _require(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and block_tables.shape[0] == B,
+                 "block_tables must be int32 [B, max_blocks_per_seq]")
+        _require(context_lens.dtype == torch.int32 and tuple(context_lens.shape) == (B,), "context_lens must be int32 [B]")
+        if max_context_len is None:  # costs a device->host synchronisation
+            max_context_len = int(context_lens.max().item()) if B else 0
+        self.max_context_len = int(max_context_len)
+        self.B, self.hq, self.hkv, self.D, self.nb = B, hq, hkv, D, nb
+        self.partition_size = int(partition_size)
+        need = decode_workspace_bytes(B, hq, hkv, D, self.max_context_len, self.partition_size)
+        if need and workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        if workspace is not None:
+            _check_tensor(workspace, "workspace", dev)
+        self.workspace = workspace
+        self.ws_ptr = _ptr(workspace) if workspace is not None else None
+        self.ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        self.args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), float(scale),
+                     _ptr(out), B, hq, hkv, D, BLOCK_SIZE, nb, block_tables.shape[1], self.max_context_len,
+                     self.partition_size, self.ws_ptr, self.ws_bytes, _dtype_code(k_cache), _dtype_code(out),
+                     _stream(dev))
+        self.reduce_args = (_ptr(context_lens), _ptr(out), B, hq, hkv, D, BLOCK_SIZE, block_tables.shape[1],
+                            self.max_context_len, self.partition_size, self.ws_ptr, self.ws_bytes, _dtype_code(out),
+                            _stream(dev))
+
+
+def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                           block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                           out: torch.Tensor, *, partition_size: int = 0, max_context_len: Optional[int] = None,
+                           workspace: Optional[torch.Tensor] = None) -> None:
+    """Decode attention of ``q [B, Hq, D]`` over the paged cache into ``out``.
+
+    ``max_context_len`` (host-known bound of ``context_lens``) avoids a
+    device-to-host sync; ``workspace`` (uint8, >= ``decode_workspace_bytes``)
+    avoids an allocation when the context is split.
+    """
+    a = _DecodeArgs(q, k_cache, v_cache, block_tables, context_lens, scale, out, partition_size, max_context_len,
+                    workspace)
+    _check(load_library().pkv_paged_attention_decode(*a.args), "paged_attention_decode")
+
+
+def prepare_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out, *, partition_size=0,
+                   max_context_len=None, workspace=None) -> _DecodeArgs:
+    """Validate once; the returned object drives ``run_partitions`` / ``run_reduce`` repeatedly."""
+    return _DecodeArgs(q, k_cache, v_cache, block_tables, context_lens, scale, out, partition_size, max_context_len,
+                       workspace)
+
+
+def run_decode(a: _DecodeArgs) -> None:
+    _check(load_library().pkv_paged_attention_decode(*a.args), "paged_attention_decode")
+
+
+def run_partitions(a: _DecodeArgs) -> None:
+    _check(load_library().pkv_paged_attention_decode_partitions(*a.args), "paged_attention_decode_partitions")
+
+
+def run_reduce(a: _DecodeArgs) -> None:
+    _check(load_library().pkv_paged_attention_decode_reduce(*a.reduce_args), "paged_attention_decode_reduce")

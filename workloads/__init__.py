@@ -340,7 +340,7 @@ class ContinuousBatching:
     def __init__(self, seed: int = DEFAULT_SEEDS["continuous_batching"], num_seqs: int = 256,
                  num_q_heads: int = 32, num_kv_heads: int = 8, head_dim: int = 128, block_size: int = 16,
                  steps: int = 10, replace_frac: float = 0.05, lmin: int = 16, lmax: int = 8192,
-                 dtype: str = "bf16", partition_size: int = 0):
+                 dtype: str = "bf16", partition_size: int = 0, pool_factor: float = 1.5):
         self.seed, self.dtype = seed, dtype
         self.B, self.Hq, self.Hkv, self.D, self.bs = num_seqs, num_q_heads, num_kv_heads, head_dim, block_size
         self.steps, self.lmin, self.lmax = steps, lmin, lmax
@@ -349,7 +349,7 @@ class ContinuousBatching:
         self.scale = 1.0 / math.sqrt(head_dim)
         self.rng = np.random.default_rng([seed, 0])
         L0 = log_uniform_lengths(self.rng, num_seqs, lmin, lmax)
-        self.num_blocks = pool_blocks_for(L0, block_size)
+        self.num_blocks = pool_blocks_for(L0, block_size, factor=pool_factor)
         self.table_width = blocks_needed(lmax + steps, block_size)
         self.pool = BlockPool(self.num_blocks, block_size,
                               order=np.random.default_rng([seed, 100]).permutation(self.num_blocks))
