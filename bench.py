@@ -1,0 +1,288 @@
+"""Benchmark: paged-KV decode on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config NAME] [--partition-size PS]
+
+One step is one pass of the whole hot path over one batch: the cache write of
+every sequence's new token (reshape_and_cache), the block-table-driven decode
+partitions, and the split-K reduce.  The default workload is the
+Llama-3-8B-shaped decode layer (64 sequences, 32 q / 8 KV heads, head_dim 128,
+bf16 KV, context lengths uniform on [128, 4096]).  Inputs are resident in HBM
+before timing starts.  To keep the 256 MB Infinity Cache from serving KV
+across steps, several copies of the pool are used in rotation, so a step never
+reads data a recent step read.
+
+Printed: one JSON line with the KV-read bandwidth (algorithmic KV bytes per
+step / wall time per step), decode tokens/s, the dominant kernel's roofline
+(HIP events around its launches), and the CPU oracle's rate on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "paged-attn decode: achieved KV-read HBM GB/s (% of peak) + decode tokens/s"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partitions_traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_372_amd", "csrc", f) for f in ("decode_mfma.hip", "kernels.h")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, partition_size: int):
+    """Per-launch HBM bytes of the decode kernel from committed rocprofv3 counters.
+
+    Null unless the counters were taken on this exact kernel source and
+    workload configuration.
+    """
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != kernel_source_hash():
+        return None
+    if rec.get("workload") != workload or rec.get("partition_size") != partition_size:
+        return None
+    fetch = rec["fetch_kib_per_dispatch"] * 1024 * rec["fetch_copy_factor"]
+    write = rec["write_kib_per_dispatch"] * 1024 * rec["write_copy_factor"]
+    return int(round(fetch + write))
+
+
+def build_workload(name: str, ps: int):
+    import workloads as W
+    if name == "llama3_8b_decode":
+        return W.llama3_8b_decode(partition_size=ps)
+    if name == "long_context":
+        return W.long_context(partition_size=ps or 512)
+    if name == "shared_prefix":
+        return W.shared_prefix(partition_size=ps)
+    if name == "tiny_fp32":
+        return W.tiny_fp32()
+    raise SystemExit(f"unknown --config {name}")
+
+
+def cpu_baseline(b, budget_s: float = 12.0):
+    """The oracle, as it stands, on the first sequences of the workload until the budget runs out."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    kp, vp = oracle.ref_reshape_and_cache(b.k_new, b.v_new, b.slot_mapping, b.k_pool, b.v_pool)
+    t0 = time.perf_counter()
+    done, kv_bytes = 0, 0
+    es = 2 if b.dtype == "bf16" else 4
+    for s in range(b.num_seqs):
+        oracle.ref_paged_attention_decode(b.q, kp, vp, b.block_tables, b.context_lens, b.scale, b.dtype, seqs=[s])
+        done += 1
+        kv_bytes += int(b.context_lens[s]) * 2 * b.num_kv_heads * b.head_dim * es
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(kv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {b.num_seqs} sequences of the {b.name} workload (float64 decode after the oracle's cache write, "
+                      f"all {b.num_q_heads} q heads), {dt:.1f} s",
+            "tokens_per_s": round(done / dt, 3), "cpu_model": _cpu_model(), "os_cpu_count": os.cpu_count()}
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def host_pack_ms(b, reps: int = 20):
+    """Time to pack the step's tables on the host and copy them to the GPU (pinned, async + sync)."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_372_amd.blocks import pack_block_tables, Sequence
+    seqs = []
+    for s in range(b.num_seqs):
+        L = int(b.context_lens[s])
+        n = -(-L // b.block_size)
+        seqs.append(Sequence(s, b.block_tables[s, :n].tolist(), L))
+    width = b.block_tables.shape[1]
+    pin_bt = torch.empty((b.num_seqs, width), dtype=torch.int32, pin_memory=True)
+    pin_len = torch.empty((b.num_seqs,), dtype=torch.int32, pin_memory=True)
+    pin_slot = torch.empty((b.num_seqs,), dtype=torch.int64, pin_memory=True)
+    d_bt = torch.empty_like(pin_bt, device="cuda")
+    d_len = torch.empty_like(pin_len, device="cuda")
+    d_slot = torch.empty_like(pin_slot, device="cuda")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        pin_bt.numpy()[:] = pack_block_tables(seqs, width, b.pad_block if b.pad_block >= 0 else 0)
+        pin_len.numpy()[:] = [s.num_tokens for s in seqs]
+        pin_slot.numpy()[:] = [s.slot_of(s.num_tokens - 1, b.block_size) for s in seqs]
+        d_bt.copy_(pin_bt, non_blocking=True)
+        d_len.copy_(pin_len, non_blocking=True)
+        d_slot.copy_(pin_slot, non_blocking=True)
+        torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / reps * 1e3
+
+
+def calibrate_copy(mib: int, reps: int):
+    """A plain device copy of known size, for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    n = mib * 1024 * 1024 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read": n * 4, "bytes_written": n * 4, "reps": reps}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="llama3_8b_decode")
+    ap.add_argument("--partition-size", type=int, default=0, help="0 = the library's automatic choice")
+    ap.add_argument("--replicas", type=int, default=0, help="pool copies in rotation (0 = enough for >= 2 GiB of KV)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from paged_kv_cache_372_amd import ops
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    ops.load_library()
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy, max(1, args.steps))
+        return
+
+    t_gen = time.perf_counter()
+    b = build_workload(args.config, args.partition_size)
+    gen_s = time.perf_counter() - t_gen
+    dtype = torch.bfloat16 if b.dtype == "bf16" else torch.float32
+
+    def dev(a):
+        if b.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    kv_bytes = b.kv_bytes()
+    pool_bytes = b.k_pool.nbytes + b.v_pool.nbytes
+    R = args.replicas or max(2, math.ceil(2 * 2**30 / max(1, kv_bytes)))
+    k0, v0 = dev(b.k_pool), dev(b.v_pool)
+    kcs = [k0] + [k0.clone() for _ in range(R - 1)]
+    vcs = [v0] + [v0.clone() for _ in range(R - 1)]
+    q, k_new, v_new = dev(b.q), dev(b.k_new), dev(b.v_new)
+    slots = torch.from_numpy(b.slot_mapping).cuda()
+    bt = torch.from_numpy(b.block_tables).cuda()
+    lens = torch.from_numpy(b.context_lens).cuda()
+    out = torch.empty(q.shape, dtype=dtype, device="cuda")
+    ps = args.partition_size or (b.partition_size or 0)
+    plans = [ops.prepare_decode(q, kcs[r], vcs[r], bt, lens, b.scale, out, partition_size=ps,
+                                max_context_len=b.max_context_len) for r in range(R)]
+    ws = plans[0].workspace
+    plans = [ops.prepare_decode(q, kcs[r], vcs[r], bt, lens, b.scale, out, partition_size=ps,
+                                max_context_len=b.max_context_len, workspace=ws) for r in range(R)]
+    resolved_ps = ps or ops.auto_partition_size(b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim,
+                                                b.max_context_len)
+    split = ops.decode_workspace_bytes(b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim, b.max_context_len,
+                                       resolved_ps) > 0
+
+    def step(i, ev=None):
+        r = i % R
+        if ev is not None:
+            ev[0].record()
+        ops.reshape_and_cache(k_new, v_new, slots, kcs[r], vcs[r])
+        if ev is not None:
+            ev[1].record()
+        ops.run_partitions(plans[r])
+        if ev is not None:
+            ev[2].record()
+        ops.run_reduce(plans[r])
+        if ev is not None:
+            ev[3].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    cw = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    dec = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+    red = sum(e[2].elapsed_time(e[3]) for e in events) / args.steps
+    ms_per_step = wall / args.steps * 1e3
+    value = kv_bytes / (ms_per_step / 1e3) / 1e9
+    achieved = kv_bytes / (dec / 1e3) / 1e9
+    traffic = measured_traffic(b.name, resolved_ps)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": b.dtype,
+        "data": "synthetic",
+        "config": {"workload": b.name, "seed": b.seed, "num_seqs": b.num_seqs, "num_q_heads": b.num_q_heads,
+                   "num_kv_heads": b.num_kv_heads, "head_dim": b.head_dim, "block_size": b.block_size,
+                   "context_len_mean": round(float(b.context_lens.mean()), 1),
+                   "context_len_max": b.max_context_len, "partition_size": resolved_ps, "split_k": split,
+                   "kv_bytes_per_step": kv_bytes, "pool_bytes": pool_bytes, "pool_replicas": R},
+        "frac_of_peak": round(value / PEAK_HBM_GBS, 4),
+        "tokens_per_s": round(b.num_seqs / (ms_per_step / 1e3), 1),
+        "kernels_ms": {"reshape_and_cache": round(cw, 5), "decode_partitions": round(dec, 5),
+                       "splitk_reduce": round(red, 5)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+                     "kernel": "decode_bf16_mfma_kernel" if b.dtype == "bf16" else "decode_valu_kernel",
+                     "bytes_per_launch": kv_bytes},
+        "input_generation_s": round(gen_s, 2),
+    }
+    try:
+        rec["host_pack_h2d_ms"] = round(host_pack_ms(b), 4)
+    except Exception as e:  # aux figure only
+        rec["host_pack_h2d_ms"] = f"unavailable: {e}"
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(b, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

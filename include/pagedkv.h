@@ -100,9 +100,10 @@ int32_t pkv_decode_auto_partition_size(int32_t num_seqs, int32_t num_q_heads, in
 /*
  * Bytes of device workspace the decode needs for these sizes (0 when the
  * context fits in one partition).  partition_size 0 = automatic, as above.
- * Layout (all fp32): o[num_seqs][num_q_heads][P][head_dim], then
- * m[num_seqs][num_q_heads][P], then l[num_seqs][num_q_heads][P], with
- * P = ceil(max_context_len / partition_size).  Returns 0 for invalid sizes.
+ * Layout (all fp32): o[num_seqs][P][num_q_heads][head_dim], then
+ * m[num_seqs][P][num_q_heads], then l[num_seqs][P][num_q_heads], with
+ * P = ceil(max_context_len / partition_size): the partials of one
+ * (sequence, partition) are contiguous.  Returns 0 for invalid sizes.
  */
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                   int32_t head_dim, int32_t max_context_len, int32_t partition_size);

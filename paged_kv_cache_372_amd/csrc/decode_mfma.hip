@@ -34,6 +34,11 @@
 namespace pkv {
 namespace {
 
+#ifndef PKV_PREFETCH_BLOCKS
+#define PKV_PREFETCH_BLOCKS 3
+#endif
+constexpr int kPrefetchBlocks = PKV_PREFETCH_BLOCKS;  // KV blocks each wave keeps in flight
+
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
@@ -58,9 +63,17 @@ __device__ __forceinline__ void load_block(BlockRegs<D>& r, const uint16_t* __re
 }
 
 struct SoftmaxState {
-    float m;   // running max (log2 units), same in all lanes of a head column
+    float m;   // reference max (log2 units), same in all lanes of a head column
     float l;   // this lane's share of sum 2^(s - m)
 };
+
+// The reference max is raised only when a block's max exceeds it by more
+// than 2^kRescaleSlack: until then the weights 2^(s - m) stay below 2^8,
+// which fp32 holds exactly as well as weights below 1, and the accumulator
+// rescale (a full pass over the output registers) is skipped.  The result is
+// the same softmax; only the common reference of numerator and denominator
+// moves less often.
+constexpr float kRescaleSlack = 8.f;
 
 template <int D>
 __device__ __forceinline__ void compute_block(const BlockRegs<D>& r, const bf16x8_t* qop, float4_t* acc,
@@ -77,14 +90,19 @@ __device__ __forceinline__ void compute_block(const BlockRegs<D>& r, const bf16x
     float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(st.m, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = exp2_fast(st.m - m_use);
+    const bool raise = mx > st.m + kRescaleSlack;
+    if (__any(raise)) {
+        const float alpha = raise ? exp2_fast(st.m - mx) : 1.f;   // st.m = -inf -> 0
+        st.l *= alpha;
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) acc[c] *= alpha;
+        st.m = raise ? mx : st.m;
+    }
+    const float m_use = (st.m == -INFINITY) ? 0.f : st.m;
     float pr[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) pr[i] = exp2_fast(sv[i] - m_use);
-    st.l = st.l * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-    st.m = m_new;
+    st.l += (pr[0] + pr[1]) + (pr[2] + pr[3]);
 
     // P^T as B operand, split into bf16 hi + lo terms
     uint32_t hi[4], lo[4];
@@ -105,14 +123,13 @@ __device__ __forceinline__ void compute_block(const BlockRegs<D>& r, const bf16x
     }
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
-        acc[c] *= alpha;
         const short4_t a = __builtin_bit_cast(short4_t, make_uint2(r.v[c].x & vm0, r.v[c].y & vm1));
         acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, p_hi, acc[c], 0, 0, 0);
         acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, p_lo, acc[c], 0, 0, 0);
     }
 }
 
-template <int D>
+template <int D, int kDepth>
 __global__ __launch_bounds__(64) void decode_bf16_mfma_kernel(DecodeParams p) {
     const int lane = threadIdx.x;
     const int col = lane & 15;  // head column of the MFMA tiles
@@ -179,45 +196,60 @@ __global__ __launch_bounds__(64) void decode_bf16_mfma_kernel(DecodeParams p) {
         return ok ? pb : 0;
     };
 
-    BlockRegs<D> ra, rb;
-    int va, vb;
-    load_block<D>(ra, k_head, v_head, block_stride, block_of(0, va), lane);
-    for (int j = 0; j < nb; j += 2) {
-        if (j + 1 < nb) load_block<D>(rb, k_head, v_head, block_stride, block_of(j + 1, vb), lane);
-        compute_block<D>(ra, qop, acc, st, va, p.scale_log2, g);
-        if (j + 1 >= nb) break;
-        if (j + 2 < nb) load_block<D>(ra, k_head, v_head, block_stride, block_of(j + 2, va), lane);
-        compute_block<D>(rb, qop, acc, st, vb, p.scale_log2, g);
+    // Ring of kDepth blocks in flight.  The refill of a slot is issued
+    // unconditionally (past the end it re-reads the partition's last block,
+    // an L2 hit), so the number of loads in flight is the same on every path
+    // and the wait before a block covers only that block's loads.
+    BlockRegs<D> ring[kDepth];
+    int vn[kDepth];
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) load_block<D>(ring[d], k_head, v_head, block_stride, block_of(min(d, nb - 1), vn[d]), lane);
+    for (int j = 0; j < nb; j += kDepth) {
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d) {
+            if (j + d < nb) compute_block<D>(ring[d], qop, acc, st, vn[d], p.scale_log2, g);
+            load_block<D>(ring[d], k_head, v_head, block_stride, block_of(min(j + d + kDepth, nb - 1), vn[d]), lane);
+        }
     }
 
     float l_tot = st.l + __shfl_xor(st.l, 16);
     l_tot = l_tot + __shfl_xor(l_tot, 32);
-    if (col >= nh) return;
-    const int h = h0 + col;
 
-    if (n_parts == 1) {
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        const int64_t ob = ((int64_t)s * Hq + h) * D + 4 * g;
+    // Epilogue.  The unit's results are nh consecutive rows of D values in
+    // either destination (out[s][h0..][:], or the partial block of
+    // (s, part) laid out [part][head][dim]), so they are written as one
+    // contiguous run: the accumulator tiles (lane: head col, dims 16c+4g..)
+    // go through LDS and come back as row-major 16-byte pieces.
+    __shared__ float tile[kMfmaHeadsPerUnit][D + 4];
+    const bool single = n_parts == 1;
+    const float scale = single ? (l_tot > 0.f ? 1.f / l_tot : 0.f) : 1.f;
 #pragma unroll
-        for (int c = 0; c < D / 16; ++c) {
-            const float o0 = acc[c][0] * inv, o1 = acc[c][1] * inv, o2 = acc[c][2] * inv, o3 = acc[c][3] * inv;
+    for (int c = 0; c < D / 16; ++c)
+        *reinterpret_cast<float4*>(&tile[col][16 * c + 4 * g]) =
+            make_float4(acc[c][0] * scale, acc[c][1] * scale, acc[c][2] * scale, acc[c][3] * scale);
+    __syncthreads();
+    constexpr int kQuads = D / 4;  // 16-byte pieces per fp32 row
+    const int n4 = nh * kQuads;
+    if (single) {
+        const int64_t ob = ((int64_t)s * Hq + h0) * D;
+        for (int f = lane; f < n4; f += 64) {
+            const float4 v = *reinterpret_cast<const float4*>(&tile[f / kQuads][4 * (f % kQuads)]);
             if (p.out_bf16) {
-                const uint2 w = make_uint2(f32_to_bf16_bits(o0) | (f32_to_bf16_bits(o1) << 16),
-                                           f32_to_bf16_bits(o2) | (f32_to_bf16_bits(o3) << 16));
-                *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + ob + 16 * c) = w;
+                const uint2 w = make_uint2(f32_to_bf16_bits(v.x) | (f32_to_bf16_bits(v.y) << 16),
+                                           f32_to_bf16_bits(v.z) | (f32_to_bf16_bits(v.w) << 16));
+                *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + ob + 4 * f) = w;
             } else {
-                *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + ob + 16 * c) = make_float4(o0, o1, o2, o3);
+                *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + ob + 4 * f) = v;
             }
         }
     } else {
-        const int64_t row = ((int64_t)s * Hq + h) * p.num_parts + part;
-        float* o = p.o_part + row * D + 4 * g;
-#pragma unroll
-        for (int c = 0; c < D / 16; ++c)
-            *reinterpret_cast<float4*>(o + 16 * c) = make_float4(acc[c][0], acc[c][1], acc[c][2], acc[c][3]);
-        if (g == 0) {
-            p.m_part[row] = st.m;
-            p.l_part[row] = l_tot;
+        const int64_t row0 = ((int64_t)s * p.num_parts + part) * Hq + h0;
+        float* o = p.o_part + row0 * D;
+        for (int f = lane; f < n4; f += 64)
+            *reinterpret_cast<float4*>(o + 4 * f) = *reinterpret_cast<const float4*>(&tile[f / kQuads][4 * (f % kQuads)]);
+        if (g == 0 && col < nh) {
+            p.m_part[row0 + col] = st.m;
+            p.l_part[row0 + col] = l_tot;
         }
     }
 }
@@ -228,8 +260,8 @@ hipError_t launch_decode_bf16_mfma(const DecodeParams& p, hipStream_t stream) {
     const int64_t units = decode_units(p);
     if (units == 0) return hipSuccess;
     const dim3 grid((unsigned)units), block(64);
-    if (p.head_dim == 128) hipLaunchKernelGGL(decode_bf16_mfma_kernel<128>, grid, block, 0, stream, p);
-    else hipLaunchKernelGGL(decode_bf16_mfma_kernel<64>, grid, block, 0, stream, p);
+    if (p.head_dim == 128) hipLaunchKernelGGL((decode_bf16_mfma_kernel<128, kPrefetchBlocks>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((decode_bf16_mfma_kernel<64, kPrefetchBlocks>), grid, block, 0, stream, p);
     return hipGetLastError();
 }
 

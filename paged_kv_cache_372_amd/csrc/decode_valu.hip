@@ -196,7 +196,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
                 else reinterpret_cast<float*>(p.out)[o] = val;
             }
         } else {
-            const int64_t row = ((int64_t)s * Hq + qh) * p.num_parts + part;
+            const int64_t row = ((int64_t)s * p.num_parts + part) * Hq + qh;
 #pragma unroll
             for (int k = 0; k < DPL; ++k) p.o_part[row * D + lane + 64 * k] = acc[h][k];
             if (lane == 0) {

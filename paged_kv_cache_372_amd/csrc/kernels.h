@@ -21,9 +21,9 @@ struct DecodeParams {
     const int32_t* block_tables; // [B][max_blocks_per_seq]
     const int32_t* context_lens; // [B]
     void* out;                   // [B][Hq][D]
-    float* o_part;               // [B][Hq][P][D]   (split only)
-    float* m_part;               // [B][Hq][P]      running max, log2 units
-    float* l_part;               // [B][Hq][P]      sum of 2^(s - m)
+    float* o_part;               // [B][P][Hq][D]   (split only)
+    float* m_part;               // [B][P][Hq]      reference max, log2 units
+    float* l_part;               // [B][P][Hq]      sum of 2^(s - m)
     float scale_log2;            // scale * log2(e)
     int32_t num_seqs;
     int32_t num_q_heads;

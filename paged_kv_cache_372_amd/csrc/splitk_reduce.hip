@@ -58,18 +58,19 @@ __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(DecodeParams p)
     if (n_parts > p.num_parts) n_parts = p.num_parts;
     if (n_parts <= 1) return;
 
-    const int64_t base = ((int64_t)s * Hq + h) * p.num_parts;
+    // partials of (s, partition i, head h) sit at row (s * P + i) * Hq + h
+    const int64_t base = (int64_t)s * p.num_parts * Hq + h;
     const float* m = p.m_part + base;
     const float* l = p.l_part + base;
     const int tid = threadIdx.x;
 
     float mx = -INFINITY;
-    for (int i = tid; i < n_parts; i += kThreads) mx = fmaxf(mx, m[i]);
+    for (int i = tid; i < n_parts; i += kThreads) mx = fmaxf(mx, m[(int64_t)i * Hq]);
     const float M = block_max(mx, red);
     const float M_use = (M == -INFINITY) ? 0.f : M;
 
     float den = 0.f;
-    for (int i = tid; i < n_parts; i += kThreads) den += exp2_fast(m[i] - M_use) * l[i];
+    for (int i = tid; i < n_parts; i += kThreads) den += exp2_fast(m[(int64_t)i * Hq] - M_use) * l[(int64_t)i * Hq];
     den = block_sum(den, red);
 
     const int slot = tid / LPR;
@@ -78,8 +79,8 @@ __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(DecodeParams p)
     const float4* o = reinterpret_cast<const float4*>(p.o_part + base * D);
 #pragma unroll 4
     for (int i = slot; i < n_parts; i += SLOTS) {
-        const float w = exp2_fast(m[i] - M_use);
-        const float4 v = o[(int64_t)i * LPR + c4];
+        const float w = exp2_fast(m[(int64_t)i * Hq] - M_use);
+        const float4 v = o[(int64_t)i * Hq * LPR + c4];
         a.x = fmaf(w, v.x, a.x);
         a.y = fmaf(w, v.y, a.y);
         a.z = fmaf(w, v.z, a.z);
