@@ -38,6 +38,10 @@ namespace {
 #define PKV_PREFETCH_BLOCKS 3
 #endif
 constexpr int kPrefetchBlocks = PKV_PREFETCH_BLOCKS;  // KV blocks each wave keeps in flight
+#ifndef PKV_WAVES_PER_UNIT
+#define PKV_WAVES_PER_UNIT 4
+#endif
+constexpr int kWavesPerUnit = PKV_WAVES_PER_UNIT;  // waves sharing one unit's blocks
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
@@ -129,9 +133,10 @@ __device__ __forceinline__ void compute_block(const BlockRegs<D>& r, const bf16x
     }
 }
 
-template <int D, int kDepth>
-__global__ __launch_bounds__(64) void decode_bf16_mfma_kernel(DecodeParams p) {
-    const int lane = threadIdx.x;
+template <int D, int kDepth, int kWaves>
+__global__ __launch_bounds__(64 * kWaves) void decode_bf16_mfma_kernel(DecodeParams p) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
     const int col = lane & 15;  // head column of the MFMA tiles
     const int g = lane >> 4;    // lane group
 
@@ -152,7 +157,7 @@ __global__ __launch_bounds__(64) void decode_bf16_mfma_kernel(DecodeParams p) {
 
     if (n_parts == 0) {  // empty context: zeros
         if (part != 0) return;
-        for (int idx = lane; idx < nh * D; idx += 64) {
+        for (int idx = threadIdx.x; idx < nh * D; idx += 64 * kWaves) {
             const int64_t o = ((int64_t)s * Hq + h0) * D + idx;
             if (p.out_bf16) reinterpret_cast<uint16_t*>(p.out)[o] = 0;
             else reinterpret_cast<float*>(p.out)[o] = 0.f;
@@ -163,6 +168,9 @@ __global__ __launch_bounds__(64) void decode_bf16_mfma_kernel(DecodeParams p) {
 
     const int blk0 = part * p.part_blocks;
     const int nb = min(p.part_blocks, n_blk - blk0);
+    // the waves of the workgroup take the partition's blocks in turn:
+    // wave w handles blocks w, w + kWaves, w + 2 kWaves, ...
+    const int nbw = nb > wave ? (nb - wave + kWaves - 1) / kWaves : 0;
 
     // Q^T as the B operand: column = head, k-group g holds chunk 4kk + g
     bf16x8_t qop[D / 32];
@@ -189,67 +197,95 @@ __global__ __launch_bounds__(64) void decode_bf16_mfma_kernel(DecodeParams p) {
     for (int c = 0; c < D / 16; ++c) acc[c] = {0.f, 0.f, 0.f, 0.f};
     SoftmaxState st{-INFINITY, 0.f};
 
-    auto block_of = [&](int j, int& valid_n) {
+    // i-th block of this wave -> physical block and number of valid tokens
+    auto block_of = [&](int i, int& valid_n) {
+        const int j = wave + kWaves * i;
         const int pb = __builtin_amdgcn_readlane(bt_lane, j);
         const bool ok = pb >= 0 && (int64_t)pb < p.num_blocks;
         valid_n = ok ? L - (blk0 + j) * kBlockSize : 0;
         return ok ? pb : 0;
     };
 
-    // Ring of kDepth blocks in flight.  The refill of a slot is issued
-    // unconditionally (past the end it re-reads the partition's last block,
-    // an L2 hit), so the number of loads in flight is the same on every path
-    // and the wait before a block covers only that block's loads.
-    BlockRegs<D> ring[kDepth];
-    int vn[kDepth];
+    if (nbw > 0) {
+        // Ring of kDepth blocks in flight.  The refill of a slot is issued
+        // unconditionally (past the end it re-reads the wave's last block,
+        // an L2 hit), so the number of loads in flight is the same on every
+        // path and the wait before a block covers only that block's loads.
+        BlockRegs<D> ring[kDepth];
+        int vn[kDepth];
 #pragma unroll
-    for (int d = 0; d < kDepth; ++d) load_block<D>(ring[d], k_head, v_head, block_stride, block_of(min(d, nb - 1), vn[d]), lane);
-    for (int j = 0; j < nb; j += kDepth) {
+        for (int d = 0; d < kDepth; ++d)
+            load_block<D>(ring[d], k_head, v_head, block_stride, block_of(min(d, nbw - 1), vn[d]), lane);
+        for (int i = 0; i < nbw; i += kDepth) {
 #pragma unroll
-        for (int d = 0; d < kDepth; ++d) {
-            if (j + d < nb) compute_block<D>(ring[d], qop, acc, st, vn[d], p.scale_log2, g);
-            load_block<D>(ring[d], k_head, v_head, block_stride, block_of(min(j + d + kDepth, nb - 1), vn[d]), lane);
+            for (int d = 0; d < kDepth; ++d) {
+                if (i + d < nbw) compute_block<D>(ring[d], qop, acc, st, vn[d], p.scale_log2, g);
+                load_block<D>(ring[d], k_head, v_head, block_stride, block_of(min(i + d + kDepth, nbw - 1), vn[d]),
+                              lane);
+            }
         }
     }
 
     float l_tot = st.l + __shfl_xor(st.l, 16);
     l_tot = l_tot + __shfl_xor(l_tot, 32);
 
-    // Epilogue.  The unit's results are nh consecutive rows of D values in
-    // either destination (out[s][h0..][:], or the partial block of
-    // (s, part) laid out [part][head][dim]), so they are written as one
-    // contiguous run: the accumulator tiles (lane: head col, dims 16c+4g..)
-    // go through LDS and come back as row-major 16-byte pieces.
-    __shared__ float tile[kMfmaHeadsPerUnit][D + 4];
-    const bool single = n_parts == 1;
-    const float scale = single ? (l_tot > 0.f ? 1.f / l_tot : 0.f) : 1.f;
+    // Epilogue.  Each wave parks its unnormalised accumulator tiles (lane:
+    // head col, dims 16c+4g..) and its (m, l) per head in LDS; the
+    // workgroup then merges the waves with the log-sum-exp weights
+    // 2^(m_w - M) in wave order and writes the unit's nh rows of D values
+    // -- contiguous in either destination (out[s][h0..][:], or the partial
+    // block of (s, part) laid out [part][head][dim]) -- as 16-byte pieces.
+    __shared__ float tile[kWaves][kMfmaHeadsPerUnit][D + 4];
+    __shared__ float m_w[kWaves][kMfmaHeadsPerUnit];
+    __shared__ float l_w[kWaves][kMfmaHeadsPerUnit];
 #pragma unroll
     for (int c = 0; c < D / 16; ++c)
-        *reinterpret_cast<float4*>(&tile[col][16 * c + 4 * g]) =
-            make_float4(acc[c][0] * scale, acc[c][1] * scale, acc[c][2] * scale, acc[c][3] * scale);
+        *reinterpret_cast<float4*>(&tile[wave][col][16 * c + 4 * g]) = make_float4(acc[c][0], acc[c][1], acc[c][2], acc[c][3]);
+    if (g == 0) {
+        m_w[wave][col] = st.m;
+        l_w[wave][col] = l_tot;
+    }
     __syncthreads();
     constexpr int kQuads = D / 4;  // 16-byte pieces per fp32 row
     const int n4 = nh * kQuads;
-    if (single) {
-        const int64_t ob = ((int64_t)s * Hq + h0) * D;
-        for (int f = lane; f < n4; f += 64) {
-            const float4 v = *reinterpret_cast<const float4*>(&tile[f / kQuads][4 * (f % kQuads)]);
-            if (p.out_bf16) {
-                const uint2 w = make_uint2(f32_to_bf16_bits(v.x) | (f32_to_bf16_bits(v.y) << 16),
-                                           f32_to_bf16_bits(v.z) | (f32_to_bf16_bits(v.w) << 16));
-                *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + ob + 4 * f) = w;
-            } else {
-                *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + ob + 4 * f) = v;
-            }
+    const bool single = n_parts == 1;
+    for (int f = threadIdx.x; f < n4; f += 64 * kWaves) {
+        const int row = f / kQuads;
+        const int c4 = f % kQuads;
+        float M = m_w[0][row];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, m_w[w][row]);
+        const float M_use = (M == -INFINITY) ? 0.f : M;
+        float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+        float den = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float a = kWaves == 1 ? 1.f : exp2_fast(m_w[w][row] - M_use);
+            const float4 v = *reinterpret_cast<const float4*>(&tile[w][row][4 * c4]);
+            num.x = fmaf(a, v.x, num.x);
+            num.y = fmaf(a, v.y, num.y);
+            num.z = fmaf(a, v.z, num.z);
+            num.w = fmaf(a, v.w, num.w);
+            den = fmaf(a, l_w[w][row], den);
         }
-    } else {
-        const int64_t row0 = ((int64_t)s * p.num_parts + part) * Hq + h0;
-        float* o = p.o_part + row0 * D;
-        for (int f = lane; f < n4; f += 64)
-            *reinterpret_cast<float4*>(o + 4 * f) = *reinterpret_cast<const float4*>(&tile[f / kQuads][4 * (f % kQuads)]);
-        if (g == 0 && col < nh) {
-            p.m_part[row0 + col] = st.m;
-            p.l_part[row0 + col] = l_tot;
+        if (single) {
+            const float inv = den > 0.f ? 1.f / den : 0.f;
+            const int64_t o = ((int64_t)s * Hq + h0) * D + 4 * f;
+            if (p.out_bf16) {
+                const uint2 w2 = make_uint2(f32_to_bf16_bits(num.x * inv) | (f32_to_bf16_bits(num.y * inv) << 16),
+                                            f32_to_bf16_bits(num.z * inv) | (f32_to_bf16_bits(num.w * inv) << 16));
+                *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + o) = w2;
+            } else {
+                *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + o) =
+                    make_float4(num.x * inv, num.y * inv, num.z * inv, num.w * inv);
+            }
+        } else {
+            const int64_t row0 = ((int64_t)s * p.num_parts + part) * Hq + h0;
+            *reinterpret_cast<float4*>(p.o_part + row0 * D + 4 * f) = num;
+            if (c4 == 0) {
+                p.m_part[row0 + row] = M;
+                p.l_part[row0 + row] = den;
+            }
         }
     }
 }
@@ -259,9 +295,11 @@ __global__ __launch_bounds__(64) void decode_bf16_mfma_kernel(DecodeParams p) {
 hipError_t launch_decode_bf16_mfma(const DecodeParams& p, hipStream_t stream) {
     const int64_t units = decode_units(p);
     if (units == 0) return hipSuccess;
-    const dim3 grid((unsigned)units), block(64);
-    if (p.head_dim == 128) hipLaunchKernelGGL((decode_bf16_mfma_kernel<128, kPrefetchBlocks>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((decode_bf16_mfma_kernel<64, kPrefetchBlocks>), grid, block, 0, stream, p);
+    const dim3 grid((unsigned)units), block(64 * kWavesPerUnit);
+    if (p.head_dim == 128)
+        hipLaunchKernelGGL((decode_bf16_mfma_kernel<128, kPrefetchBlocks, kWavesPerUnit>), grid, block, 0, stream, p);
+    else
+        hipLaunchKernelGGL((decode_bf16_mfma_kernel<64, kPrefetchBlocks, kWavesPerUnit>), grid, block, 0, stream, p);
     return hipGetLastError();
 }
 

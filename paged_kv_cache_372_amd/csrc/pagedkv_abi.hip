@@ -37,12 +37,15 @@ int32_t context_cap(int32_t max_context_len, int32_t max_blocks_per_seq, int32_t
 }
 
 int32_t auto_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len) {
+    (void)num_seqs;
+    (void)num_kv_heads;
     const int32_t bs = pkv::kBlockSize;
+    const int32_t cap = pkv::kMaxPartBlocks * bs;
     if (max_context_len <= 0) return bs;
-    if (max_context_len <= 512) return ceil_div(max_context_len, bs) * bs;  // one partition, no reduce
-    // enough waves to cover the chip several times over, without tiny partitions
-    const int64_t units512 = (int64_t)num_seqs * num_kv_heads * ceil_div(max_context_len, 512);
-    return units512 >= 8192 ? 512 : 256;
+    if (max_context_len <= cap) return ceil_div(max_context_len, bs) * bs;  // one partition, no reduce
+    // the waves of a decode workgroup split a partition's blocks among
+    // themselves, so long partitions keep every wave busy with few partials
+    return cap;
 }
 
 struct Resolved {

@@ -80,7 +80,7 @@ def test_reshape_and_cache_validation(lib):
 
 def dec(lib, **kw):
     a = dict(q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, lens=FAKE, scale=0.1, out=FAKE, B=4, hq=32, hkv=8, D=128, bs=16,
-             nb=100, maxblk=64, maxctx=1000, ps=0, ws=FAKE, wsb=0, kvd=BF16, outd=BF16)
+             nb=100, maxblk=128, maxctx=2000, ps=0, ws=FAKE, wsb=0, kvd=BF16, outd=BF16)
     a.update(kw)
     return lib.pkv_paged_attention_decode(a["q"], a["kc"], a["vc"], a["bt"], a["lens"], a["scale"], a["out"], a["B"],
                                           a["hq"], a["hkv"], a["D"], a["bs"], a["nb"], a["maxblk"], a["maxctx"],
@@ -101,8 +101,8 @@ def test_decode_validation(lib):
     assert dec(lib, nb=0) == INVALID
     assert dec(lib, scale=math.inf) == INVALID
     assert dec(lib, scale=math.nan) == INVALID
-    # split needed (1000 tokens > one partition): workspace missing / short / misaligned
-    need = lib.pkv_decode_workspace_bytes(4, 32, 8, 128, 1000, 0)
+    # split needed (2000 tokens > one partition): workspace missing / short / misaligned
+    need = lib.pkv_decode_workspace_bytes(4, 32, 8, 128, 2000, 0)
     assert need > 0
     assert dec(lib, ws=None, wsb=need) == WORKSPACE
     assert dec(lib, wsb=need - 1) == WORKSPACE
@@ -110,7 +110,7 @@ def test_decode_validation(lib):
     assert dec(lib, ws=FAKE + 16, wsb=need) == WORKSPACE
     # nothing to do: no launch
     assert dec(lib, B=0, q=None, kc=None, vc=None, bt=None, lens=None, out=None, ws=None) == OK
-    red = lib.pkv_paged_attention_decode_reduce(FAKE, FAKE, 4, 32, 8, 128, 16, 64, 1000, 0, None, 0, BF16, None)
+    red = lib.pkv_paged_attention_decode_reduce(FAKE, FAKE, 4, 32, 8, 128, 16, 128, 2000, 0, None, 0, BF16, None)
     assert red == WORKSPACE
 
 
@@ -123,7 +123,7 @@ def test_workspace_size_and_auto_partition(lib):
         P = -(-ctx // ps)
         assert lib.pkv_decode_workspace_bytes(B, hq, hkv, D, ctx, ps) == B * hq * P * (D + 2) * 4
     ps = lib.pkv_decode_auto_partition_size(64, 32, 8, 128, 4096)
-    assert ps in (256, 512) and ps % 16 == 0
+    assert ps == 1024
     assert lib.pkv_decode_workspace_bytes(64, 32, 8, 128, 4096, 0) == 64 * 32 * (-(-4096 // ps)) * 130 * 4
     assert lib.pkv_decode_workspace_bytes(64, 30, 8, 128, 4096, 0) == 0   # invalid sizes
     assert lib.pkv_decode_workspace_bytes(64, 32, 8, 128, 4096, 40) == 0
