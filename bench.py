@@ -75,8 +75,8 @@ def build_workload(name: str, ps: int):
 
 
 def cpu_baseline(b, budget_s: float = 12.0):
-    """The oracle, as it stands, on the first sequences of the workload until the budget runs out."""
-    import numpy as np
+    """The oracle, as it stands, over the sequences of the same workload, pass
+    after pass, until about ``budget_s`` seconds of CPU work are done."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -85,18 +85,20 @@ def cpu_baseline(b, budget_s: float = 12.0):
         threads = 1
     kp, vp = oracle.ref_reshape_and_cache(b.k_new, b.v_new, b.slot_mapping, b.k_pool, b.v_pool)
     t0 = time.perf_counter()
-    done, kv_bytes = 0, 0
+    done, kv_bytes, passes = 0, 0, 0
     es = 2 if b.dtype == "bf16" else 4
-    for s in range(b.num_seqs):
-        oracle.ref_paged_attention_decode(b.q, kp, vp, b.block_tables, b.context_lens, b.scale, b.dtype, seqs=[s])
-        done += 1
-        kv_bytes += int(b.context_lens[s]) * 2 * b.num_kv_heads * b.head_dim * es
-        if time.perf_counter() - t0 >= budget_s:
-            break
+    while time.perf_counter() - t0 < budget_s:
+        for s in range(b.num_seqs):
+            oracle.ref_paged_attention_decode(b.q, kp, vp, b.block_tables, b.context_lens, b.scale, b.dtype, seqs=[s])
+            done += 1
+            kv_bytes += int(b.context_lens[s]) * 2 * b.num_kv_heads * b.head_dim * es
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        passes += 1
     dt = time.perf_counter() - t0
     return {"value": round(kv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} of {b.num_seqs} sequences of the {b.name} workload (float64 decode after the oracle's cache write, "
-                      f"all {b.num_q_heads} q heads), {dt:.1f} s",
+            "sample": f"{done} sequence decodes ({passes} pass(es) over the {b.num_seqs} sequences of the {b.name} "
+                      f"workload; float64, all {b.num_q_heads} q heads, after the oracle's cache write), {dt:.1f} s",
             "tokens_per_s": round(done / dt, 3), "cpu_model": _cpu_model(), "os_cpu_count": os.cpu_count()}
 
 
@@ -152,6 +154,74 @@ def calibrate_copy(mib: int, reps: int):
     print(json.dumps({"calibration": "copy", "bytes_read": n * 4, "bytes_written": n * 4, "reps": reps}))
 
 
+DECODE_KERNEL_PREFIX = "void pkv::(anonymous namespace)::decode_bf16_balanced_kernel"
+
+
+def _read_counter(dirpath: str, counter: str):
+    """Mean per-dispatch value of ``counter`` for each kernel in a rocprofv3 csv run."""
+    import csv
+    import glob
+    sums = {}
+    for f in glob.glob(os.path.join(dirpath, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter:
+                continue
+            sums.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in sums.items()}
+
+
+def _short_kernel_name(k: str) -> str:
+    k = k[5:] if k.startswith("void ") else k
+    return k.replace("pkv::(anonymous namespace)::", "").split("(")[0]
+
+
+def summarize_profile(prefix: str, workload: str, partition_size, copy_mib: int, out_md: str, out_json: str,
+                      commands: str) -> None:
+    """Turn rocprofv3 csv output (``<prefix>_trace``, ``_fetch``, ``_write``,
+    ``_cal_fetch``, ``_cal_write``) into a short markdown summary and the
+    per-launch traffic record ``measured_traffic`` reads."""
+    import csv
+    import glob
+    stats = []
+    for f in glob.glob(os.path.join(prefix + "_trace", "**", "*kernel_stats.csv"), recursive=True):
+        stats += list(csv.DictReader(open(f)))
+    fetch = _read_counter(prefix + "_fetch", "FETCH_SIZE")
+    write = _read_counter(prefix + "_write", "WRITE_SIZE")
+    copy_kib = copy_mib * 1024.0
+    cal_f = _read_counter(prefix + "_cal_fetch", "FETCH_SIZE")
+    cal_w = _read_counter(prefix + "_cal_write", "WRITE_SIZE")
+    copy_name = "__amd_rocclr_copyBuffer"
+    f_factor = copy_kib / cal_f[copy_name]
+    w_factor = copy_kib / cal_w[copy_name]
+    dec = [k for k in fetch if k.startswith(DECODE_KERNEL_PREFIX)][0]
+    lines = [f"# rocprofv3: decode kernels on the {workload} workload", "",
+             "Commands (run from the repository root; `cd /tmp && export TMPDIR=/tmp` first):", "", "```",
+             commands.strip(), "```", "", "## Kernel trace (`--kernel-trace --stats`)", "",
+             "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+    for r in stats:
+        name = _short_kernel_name(r["Name"])
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    lines += ["", "## HBM traffic per dispatch (`--pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`)", "",
+              f"Calibration: a {copy_mib} MiB device copy (`{copy_name}`) reads FETCH_SIZE = {cal_f[copy_name]:.0f} KiB "
+              f"and WRITE_SIZE = {cal_w[copy_name]:.0f} KiB, so the counters are scaled by {f_factor:.4f} (fetch) and "
+              f"{w_factor:.4f} (write).", "",
+              "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled read MB | scaled write MB |", "|---|---|---|---|---|"]
+    for k in fetch:
+        if k.startswith("__amd_rocclr"):
+            continue
+        name = _short_kernel_name(k)
+        lines.append(f"| `{name}` | {fetch[k]:.0f} | {write.get(k, 0):.0f} | {fetch[k] * 1024 * f_factor / 1e6:.1f} | "
+                     f"{write.get(k, 0) * 1024 * w_factor / 1e6:.2f} |")
+    rec = {"source_sha256": kernel_source_hash(), "workload": workload, "partition_size": partition_size,
+           "kernel": dec, "fetch_kib_per_dispatch": fetch[dec], "write_kib_per_dispatch": write.get(dec, 0.0),
+           "fetch_copy_factor": f_factor, "write_copy_factor": w_factor}
+    os.makedirs(os.path.dirname(out_md), exist_ok=True)
+    open(out_md, "w").write("\n".join(lines) + "\n")
+    json.dump(rec, open(out_json, "w"), indent=1)
+    print(f"wrote {out_md} and {out_json}")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -163,7 +233,18 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB")
+    ap.add_argument("--summarize-profile", metavar="PREFIX", help="summarize rocprofv3 csv runs <PREFIX>_trace, "
+                    "_fetch, _write, _cal_fetch, _cal_write into profiles/ (no GPU needed)")
+    ap.add_argument("--profile-copy-mib", type=int, default=1024)
+    ap.add_argument("--profile-commands", default="")
     args = ap.parse_args()
+
+    if args.summarize_profile:
+        ps = args.partition_size or "balanced"
+        summarize_profile(args.summarize_profile, args.config, ps, args.profile_copy_mib,
+                          os.path.join(ROOT, "profiles", f"decode_{args.config}.md"), TRAFFIC_FILE,
+                          open(args.profile_commands).read() if args.profile_commands else "")
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -208,10 +289,7 @@ def main():
     ws = plans[0].workspace
     plans = [ops.prepare_decode(q, kcs[r], vcs[r], bt, lens, b.scale, out, partition_size=ps,
                                 max_context_len=b.max_context_len, workspace=ws) for r in range(R)]
-    resolved_ps = ps or ops.auto_partition_size(b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim,
-                                                b.max_context_len)
-    split = ops.decode_workspace_bytes(b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim, b.max_context_len,
-                                       resolved_ps) > 0
+    resolved_ps = ps if ps else ("balanced" if b.dtype == "bf16" else "auto")
 
     def step(i, ev=None):
         r = i % R
@@ -263,7 +341,7 @@ def main():
         "config": {"workload": b.name, "seed": b.seed, "num_seqs": b.num_seqs, "num_q_heads": b.num_q_heads,
                    "num_kv_heads": b.num_kv_heads, "head_dim": b.head_dim, "block_size": b.block_size,
                    "context_len_mean": round(float(b.context_lens.mean()), 1),
-                   "context_len_max": b.max_context_len, "partition_size": resolved_ps, "split_k": split,
+                   "context_len_max": b.max_context_len, "partition_size": resolved_ps,
                    "kv_bytes_per_step": kv_bytes, "pool_bytes": pool_bytes, "pool_replicas": R},
         "frac_of_peak": round(value / PEAK_HBM_GBS, 4),
         "tokens_per_s": round(b.num_seqs / (ms_per_step / 1e3), 1),
@@ -271,7 +349,7 @@ def main():
                        "splitk_reduce": round(red, 5)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-                     "kernel": "decode_bf16_mfma_kernel" if b.dtype == "bf16" else "decode_valu_kernel",
+                     "kernel": "decode_bf16_balanced_kernel" if b.dtype == "bf16" else "decode_valu_kernel",
                      "bytes_per_launch": kv_bytes},
         "input_generation_s": round(gen_s, 2),
     }

@@ -17,7 +17,8 @@
  * Conventions for every call:
  *   - Pointers marked [device] are device addresses (e.g. from a torch CUDA
  *     tensor); the caller owns all memory.  The library never allocates,
- *     frees or synchronises, and keeps no state between calls.
+ *     frees or synchronises, and keeps no state between calls (it reads
+ *     the current device's compute-unit count to plan a launch).
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
  *     stream).  A returned PKV_OK means the work was enqueued.
  *   - Problems visible on the host (null pointer, bad size, unsupported
@@ -90,23 +91,16 @@ pkv_status pkv_reshape_and_cache(const void* k_new, const void* v_new, const int
                                  void* stream);
 
 /*
- * Partition size (in tokens) the decode uses when it is passed 0.  The
- * result is a multiple of block_size in [block_size, 1024]; when
- * max_context_len fits in one partition there is no split.
- */
-int32_t pkv_decode_auto_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                                       int32_t head_dim, int32_t max_context_len);
-
-/*
- * Bytes of device workspace the decode needs for these sizes (0 when the
- * context fits in one partition).  partition_size 0 = automatic, as above.
- * Layout (all fp32): o[num_seqs][P][num_q_heads][head_dim], then
- * m[num_seqs][P][num_q_heads], then l[num_seqs][P][num_q_heads], with
- * P = ceil(max_context_len / partition_size): the partials of one
- * (sequence, partition) are contiguous.  Returns 0 for invalid sizes.
+ * Bytes of device workspace pkv_paged_attention_decode needs for these sizes
+ * on the current HIP device (the bf16 plan depends on its compute-unit
+ * count; with no usable device a 256-CU part is assumed).  Returns 0 for
+ * invalid sizes, and 0 when none is needed (fp32 KV whose contexts fit in one
+ * partition).  bf16 KV always needs some: the flattened block offsets of the
+ * batch and the partial results of sequences split across ranges.
  */
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                                  int32_t head_dim, int32_t max_context_len, int32_t partition_size);
+                                  int32_t head_dim, int32_t max_context_len, int32_t partition_size,
+                                  pkv_dtype kv_dtype);
 
 /*
  * Decode attention over the paged cache (runbyai sections 1 and 3;
@@ -129,15 +123,26 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  *                  (PKV_F32 or PKV_BF16, rounded to nearest even)
  *   num_q_heads    a multiple of num_kv_heads
  *   head_dim 64 or 128; block_size 16; num_blocks = pool size in blocks
- *   max_context_len  host-known upper bound of context_lens (sizes the grid)
- *   partition_size   0 (auto) or a multiple of block_size in [16, 1024]
+ *   max_context_len  host-known upper bound of context_lens (sizes the
+ *                  workspace; larger lengths are clamped to it)
+ *   partition_size   0 or a multiple of block_size in [16, 2^24]: the
+ *                  longest piece of a context reduced before the split-K
+ *                  merge (see below); 0 = let the library choose
  *   workspace      [device] >= pkv_decode_workspace_bytes(...) bytes,
  *                  256-byte aligned; may be NULL when that is 0
- * Long contexts are split into partitions of partition_size tokens whose
- * partial softmax statistics are merged by a second kernel on the same
- * stream (log-sum-exp rescaling).  Results are deterministic: the order of
- * every sum depends only on logical token positions, never on where blocks
- * sit in the pool.
+ * Work split.  bf16 KV: the blocks of all sequences, taken in order, form
+ * one flattened list that is cut into equal ranges, one per workgroup the
+ * device holds at once (or shorter, at most partition_size tokens each), so
+ * every workgroup streams the same number of KV bytes whatever the mix of
+ * context lengths.  A sequence inside one range is finished where it is
+ * read; the pieces of a sequence spread over several ranges leave partial
+ * softmax statistics that a second kernel merges (log-sum-exp rescaling).
+ * fp32 KV: each sequence is cut into partitions of partition_size tokens
+ * (1024 when 0 is passed and the longest context exceeds that), merged the
+ * same way.  Batches of more than 4096 sequences are run as consecutive
+ * launches of up to 4096.  Results are deterministic: the order of every
+ * sum depends only on logical token positions and on the sizes of the
+ * call, never on where blocks sit in the pool or on timing.
  */
 pkv_status pkv_paged_attention_decode(const void* q, const void* k_cache, const void* v_cache,
                                       const int32_t* block_tables, const int32_t* context_lens, float scale,
@@ -149,11 +154,13 @@ pkv_status pkv_paged_attention_decode(const void* q, const void* k_cache, const 
 
 /*
  * The two launches of pkv_paged_attention_decode, callable one at a time
- * (same arguments and meaning).  _partitions runs the block-table walk and
- * writes `out` for sequences that fit in one partition and the fp32
- * partials for the others; _reduce merges those partials into `out` and
- * must follow _partitions on the same stream with the same arguments.
- * _reduce is a no-op when no split is needed.
+ * (same arguments and meaning; the reduce takes the subset it reads).
+ * _partitions runs the block-table walk and writes `out` for the sequences
+ * it finishes and fp32 partials for the others; _reduce merges those
+ * partials into `out` (and, with bf16 KV, writes the zeros of empty
+ * contexts).  _reduce must follow _partitions on the same stream with the
+ * same arguments and workspace.  With fp32 KV it is a no-op when no split
+ * is needed.
  */
 pkv_status pkv_paged_attention_decode_partitions(const void* q, const void* k_cache, const void* v_cache,
                                                  const int32_t* block_tables, const int32_t* context_lens,
@@ -168,7 +175,8 @@ pkv_status pkv_paged_attention_decode_reduce(const int32_t* context_lens, void* 
                                              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                              int32_t block_size, int32_t max_blocks_per_seq,
                                              int32_t max_context_len, int32_t partition_size, void* workspace,
-                                             size_t workspace_bytes, pkv_dtype out_dtype, void* stream);
+                                             size_t workspace_bytes, pkv_dtype kv_dtype, pkv_dtype out_dtype,
+                                             void* stream);
 
 /* Static description of a status code.  Never NULL. */
 const char* pkv_status_string(pkv_status status);

@@ -1,18 +1,29 @@
-// Paged decode attention, bf16 KV, on the gfx950 matrix cores.
+// Paged decode attention, bf16 KV, on the gfx950 matrix cores, with the
+// work balanced over the whole batch.
 //
-// What is computed: for one sequence, one KV head and the query heads that
-// share it (grouped-query attention), walk the sequence's block table over
-// one partition of its context, and produce softmax(scale q K^T) V for that
-// partition (runbyai section 1: decode attends over the cached KV of all
-// earlier tokens; architvora "Paged Attention": the kernel follows the block
-// table to gather the blocks).  Long contexts are split into partitions
-// whose (max, sum, unnormalised output) statistics are merged by
-// splitk_reduce.hip.
+// What is computed: for every sequence and query head, softmax(scale q K^T) V
+// over the sequence's cached tokens, which the kernel reaches by following
+// the sequence's block table (runbyai section 1: decode attends over the
+// cached KV of all earlier tokens; architvora "Paged Attention": the kernel
+// follows the block table to gather the blocks).
 //
-// Work decomposition: one wave64 per unit (partition, sequence, head group,
-// KV head).  The unit id puts the KV head in the lowest digit, so with 8 KV
-// heads consecutive workgroups -- dealt round-robin to the 8 XCDs -- keep
-// each KV head on one XCD and its L2 (shared-prefix blocks stay resident).
+// Work decomposition.  Take the blocks of all sequences in order, sequence
+// after sequence: a flattened list of T blocks (the same list for every KV
+// head).  It is cut into ranges of equal length and range r goes to
+// workgroup column r mod W, so every workgroup walks the same number of
+// blocks whatever the mix of context lengths -- no tail of long sequences.
+// A range may start or end inside a sequence.  A sequence that lies wholly
+// inside one range is finished in place (out = o / l); the pieces of a
+// sequence that straddles ranges leave their (max, sum, unnormalised
+// output) and a second kernel (splitk_reduce.hip) merges them with
+// log-sum-exp weights.
+//
+// A workgroup holds one wave per KV head (up to 8); all its waves walk the
+// same blocks, so at any moment they read the neighbouring 4 KiB tiles of
+// the same physical block.  Each wave is persistent over its walk: the
+// block-table window, the query rows and the next KV blocks are fetched
+// ahead of use, across sequence and range boundaries, so a wave stalls on
+// memory only once, at its start.
 //
 // Per 16-token block, per wave:
 //   S[16 tok x 16 heads] = K[16 x D] . Q^T[D x 16]  D/32 x mfma_f32_16x16x32_bf16
@@ -29,6 +40,10 @@
 // dim; with V stored dim-major ([D][16]) each load reads a contiguous 512 B
 // run.  The QK result layout (lane: head l%16, tokens 4(l/16)..+3) is
 // exactly the PV B-operand layout, so no data moves between the two.
+//
+// Results depend only on logical token positions and the range split (a
+// function of the context lengths and the launch width), never on where
+// blocks sit in the pool.
 #include "kernels.h"
 
 namespace pkv {
@@ -38,32 +53,44 @@ namespace {
 #define PKV_PREFETCH_BLOCKS 3
 #endif
 constexpr int kPrefetchBlocks = PKV_PREFETCH_BLOCKS;  // KV blocks each wave keeps in flight
-#ifndef PKV_WAVES_PER_UNIT
-#define PKV_WAVES_PER_UNIT 4
-#endif
-constexpr int kWavesPerUnit = PKV_WAVES_PER_UNIT;  // waves sharing one unit's blocks
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
+// One ring slot: a block's K and V tiles of this wave's KV head and the
+// query rows of the block's sequence.
 template <int D>
-struct BlockRegs {
-    uint4 k[D / 32];   // K chunks: load kk holds chunk 4kk + lane/16 of token lane%16
-    uint2 v[D / 16];   // V^T: load c holds dim 16c + lane%16, tokens 4(lane/16)..+3
+struct SlotRegs {
+    uint4 k[D / 32];       // K chunks: load kk holds chunk 4kk + lane/16 of token lane%16
+    uint2 v[D / 16];       // V^T: load c holds dim 16c + lane%16, tokens 4(lane/16)..+3
+    bf16x8_t q[D / 32];    // Q^T as the B operand: column = head, k-group lane/16 holds chunk 4kk + lane/16
 };
 
-template <int D>
-__device__ __forceinline__ void load_block(BlockRegs<D>& r, const uint16_t* __restrict__ k_head,
-                                           const uint16_t* __restrict__ v_head, int64_t block_stride,
-                                           int pb, int lane) {
-    const uint4* kt = reinterpret_cast<const uint4*>(k_head + (int64_t)pb * block_stride);
-    const uint2* vt = reinterpret_cast<const uint2*>(v_head + (int64_t)pb * block_stride);
-#pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) r.k[kk] = kt[kk * 64 + lane];
-    const int vo = (lane & 15) * 4 + (lane >> 4);
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c) r.v[c] = vt[c * 64 + vo];
+// Uniform facts about the block a ring slot holds.
+struct SlotInfo {
+    int seq;    // sequence
+    int meta;   // valid tokens (0..16) | kSegLast
+    int slot;   // partial row pair index, or -1 when the sequence completes here
+};
+
+constexpr int kSegLast = 1 << 5;  // this block ends a segment (sequence or range)
+
+// Reductions over the four lane groups of a head column (lanes l, l^16,
+// l^32, l^48) with the gfx950 lane-swap instructions: plain VALU work, no
+// LDS traffic, so nothing in the block loop waits on the LDS counter.
+__device__ __forceinline__ float max_over_groups(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float sum_over_groups(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 struct SoftmaxState {
@@ -80,20 +107,18 @@ struct SoftmaxState {
 constexpr float kRescaleSlack = 8.f;
 
 template <int D>
-__device__ __forceinline__ void compute_block(const BlockRegs<D>& r, const bf16x8_t* qop, float4_t* acc,
-                                              SoftmaxState& st, int valid_n, float scale_log2, int g) {
+__device__ __forceinline__ void compute_block(const SlotRegs<D>& r, float4_t* acc, SoftmaxState& st, int valid_n,
+                                              float scale_log2, int g) {
     // S = K . Q^T: lane holds S[token 4g + i][head lane%16], i = 0..3
     float4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk)
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.k[kk]), qop[kk], sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.k[kk]), r.q[kk], sacc, 0, 0, 0);
 
     float sv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) sv[i] = (4 * g + i < valid_n) ? sacc[i] * scale_log2 : -INFINITY;
-    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mx = max_over_groups(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
     const bool raise = mx > st.m + kRescaleSlack;
     if (__any(raise)) {
         const float alpha = raise ? exp2_fast(st.m - mx) : 1.f;   // st.m = -inf -> 0
@@ -133,173 +158,264 @@ __device__ __forceinline__ void compute_block(const BlockRegs<D>& r, const bf16x
     }
 }
 
-template <int D, int kDepth, int kWaves>
-__global__ __launch_bounds__(64 * kWaves) void decode_bf16_mfma_kernel(DecodeParams p) {
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+// Walk-position window: lane i describes position base + i of the wave's
+// walk.  Built from the LDS tables only; the block-table entry itself is
+// read later through the scalar cache.
+struct Window {
+    int seq;    // sequence
+    int blk;    // logical block within the sequence
+    int meta;   // valid tokens (1..16) | kSegLast
+    int slot;   // partial row pair index, -1 = the sequence completes in this range
+};
+
+// A block-table entry fetched ahead of its ring refill, with the facts
+// about its block.
+struct Pending {
+    int raw;    // physical block id as read from the table (validated at use)
+    SlotInfo info;
+};
+
+typedef const int32_t __attribute__((address_space(4)))* scalar_i32_ptr;
+
+template <int D, int kDepth>
+__global__ __launch_bounds__(64 * kMaxWavesPerGroup) void decode_bf16_balanced_kernel(DecodeParams p) {
+    extern __shared__ int32_t tables[];
+    __shared__ int32_t wave_total[kMaxWavesPerGroup];
+    const int B = p.num_seqs;
+    int32_t* s_off = tables;          // [B + 1] first flattened block of each sequence
+    int32_t* s_len = tables + B + 1;  // [B] clamped context length
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int nthr = blockDim.x;
+    const int walker = blockIdx.x / p.head_unit_groups;
+    const int hug = blockIdx.x - walker * p.head_unit_groups;
+
+    // ---- flattened block offsets of the batch (exclusive prefix sums)
+    {
+        const int per = (B + nthr - 1) / nthr;
+        const int i0 = min(B, tid * per);
+        const int i1 = min(B, i0 + per);
+        int sum = 0;
+        for (int i = i0; i < i1; ++i) {
+            const int L = clamp_ctx(p.context_lens[i], p.ctx_cap);
+            s_len[i] = L;
+            sum += (L + kBlockSize - 1) / kBlockSize;
+        }
+        int x = sum;  // inclusive scan over the wave
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int y = __shfl_up(x, d);
+            if (lane >= d) x += y;
+        }
+        if (lane == 63) wave_total[wave] = x;
+        __syncthreads();
+        int run = x - sum;
+        for (int w = 0; w < wave; ++w) run += wave_total[w];
+        for (int i = i0; i < i1; ++i) {
+            s_off[i] = run;
+            run += (s_len[i] + kBlockSize - 1) / kBlockSize;
+        }
+        if (tid == nthr - 1) s_off[B] = run;
+        __syncthreads();
+    }
+    if (walker == 0 && hug == 0)
+        for (int i = tid; i <= B; i += nthr) p.seq_off[i] = s_off[i];
+
+    const int T = s_off[B];
+    const int NG = p.walkers;
+    int CS, NR;
+    range_geometry(T, NG, p.range_cap, CS, NR);
+    if (walker >= NR) return;
+    const int n_ranges = (NR - 1 - walker) / NG + 1;
+    const int r_final = walker + NG * (n_ranges - 1);
+    const int K = (n_ranges - 1) * CS + min(CS, T - r_final * CS);  // blocks this workgroup walks
+
+    const int hu = hug * p.waves_per_group + wave;
+    if (hu >= p.head_units) return;
+    const int kvh = hu % p.num_kv_heads;
+    const int hg = hu / p.num_kv_heads;
     const int col = lane & 15;  // head column of the MFMA tiles
     const int g = lane >> 4;    // lane group
-
-    int64_t u = blockIdx.x;
-    const int kvh = (int)(u % p.num_kv_heads);
-    u /= p.num_kv_heads;
-    const int hg = (int)(u % p.n_head_groups);
-    u /= p.n_head_groups;
-    const int s = (int)(u % p.num_seqs);
-    const int part = (int)(u / p.num_seqs);
-
-    const int L = clamp_ctx(p.context_lens[s], p.ctx_cap);
-    const int n_blk = (L + kBlockSize - 1) / kBlockSize;
-    const int n_parts = (n_blk + p.part_blocks - 1) / p.part_blocks;
+    const int Hq = p.num_q_heads;
     const int h0 = kvh * p.group + hg * kMfmaHeadsPerUnit;
     const int nh = min(kMfmaHeadsPerUnit, p.group - hg * kMfmaHeadsPerUnit);
-    const int Hq = p.num_q_heads;
-
-    if (n_parts == 0) {  // empty context: zeros
-        if (part != 0) return;
-        for (int idx = threadIdx.x; idx < nh * D; idx += 64 * kWaves) {
-            const int64_t o = ((int64_t)s * Hq + h0) * D + idx;
-            if (p.out_bf16) reinterpret_cast<uint16_t*>(p.out)[o] = 0;
-            else reinterpret_cast<float*>(p.out)[o] = 0.f;
-        }
-        return;
-    }
-    if (part >= n_parts) return;
-
-    const int blk0 = part * p.part_blocks;
-    const int nb = min(p.part_blocks, n_blk - blk0);
-    // the waves of the workgroup take the partition's blocks in turn:
-    // wave w handles blocks w, w + kWaves, w + 2 kWaves, ...
-    const int nbw = nb > wave ? (nb - wave + kWaves - 1) / kWaves : 0;
-
-    // Q^T as the B operand: column = head, k-group g holds chunk 4kk + g
-    bf16x8_t qop[D / 32];
-    {
-        const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) + ((int64_t)s * Hq + h0 + col) * D;
-#pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk) {
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (col < nh) v = reinterpret_cast<const uint4*>(qrow)[4 * kk + g];
-            qop[kk] = __builtin_bit_cast(bf16x8_t, v);
-        }
-    }
-
-    // this partition's slice of the block table, one entry per lane
-    const int32_t* bt = p.block_tables + (int64_t)s * p.max_blocks_per_seq + blk0;
-    const int bt_lane = lane < nb ? bt[lane] : 0;
+    // columns past the group repeat the group's last head: finite values,
+    // never stored, and the softmax never mixes head columns
+    const int qcol = min(col, nh - 1);
 
     const int64_t block_stride = (int64_t)p.num_kv_heads * D * kBlockSize;
     const uint16_t* k_head = reinterpret_cast<const uint16_t*>(p.k_cache) + (int64_t)kvh * D * kBlockSize;
     const uint16_t* v_head = reinterpret_cast<const uint16_t*>(p.v_cache) + (int64_t)kvh * D * kBlockSize;
+    const uint16_t* q_base = reinterpret_cast<const uint16_t*>(p.q) + (int64_t)(h0 + qcol) * D;
+
+    // Describe walk positions [base, base + 64).
+    auto build_window = [&](int base, Window& w) {
+        const int k = base + lane;
+        w.seq = 0;
+        w.blk = 0;
+        w.meta = 0;
+        w.slot = -1;
+        if (k < K) {
+            const int ri = k / CS;
+            const int r = walker + NG * ri;
+            const int rs = r * CS;
+            const int re = min(rs + CS, T);
+            const int f = rs + (k - ri * CS);
+            int lo = 0, hi = B - 1;  // last sequence starting at or before f (it holds block f)
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (s_off[mid] <= f) lo = mid;
+                else hi = mid - 1;
+            }
+            const int o0 = s_off[lo];
+            const int o1 = s_off[lo + 1];
+            const int j = f - o0;
+            w.seq = lo;
+            w.blk = j;
+            w.meta = min(kBlockSize, s_len[lo] - j * kBlockSize) | ((f == re - 1 || f == o1 - 1) ? kSegLast : 0);
+            w.slot = (o0 >= rs && o1 <= re) ? -1 : range_slot(r, CS, o0);
+        }
+    };
+
+    Window cur, nxt;
+    int win_base = 0;
+    build_window(0, cur);
+    build_window(64, nxt);
+    const scalar_i32_ptr bt = (scalar_i32_ptr)p.block_tables;
+
+    // Table entry and facts of walk position k (clamped to the last one).
+    // Positions are asked for in increasing order, one at a time.
+    auto fetch = [&](int k, Pending& e) {
+        const int kc = min(k, K - 1);
+        if (kc >= win_base + 64) {
+            win_base += 64;
+            cur = nxt;
+            build_window(win_base + 64, nxt);
+        }
+        const int li = kc - win_base;
+        const int seq = __builtin_amdgcn_readlane(cur.seq, li);
+        const int blk = __builtin_amdgcn_readlane(cur.blk, li);
+        e.raw = bt[(int64_t)seq * p.max_blocks_per_seq + blk];
+        e.info.seq = seq;
+        e.info.meta = __builtin_amdgcn_readlane(cur.meta, li);
+        e.info.slot = __builtin_amdgcn_readlane(cur.slot, li);
+    };
+
+    SlotRegs<D> ring[kDepth];
+    SlotInfo info[kDepth];
+    Pending pend[kDepth];
+
+    // Fill ring slot d from its pending entry, then fetch the entry of walk
+    // position k_next, the one this slot takes after that.  Every refill
+    // issues the same vector loads, so the wait before a block covers only
+    // that block's loads.
+    auto load_slot = [&](int d, int k_next) {
+        const int raw = pend[d].raw;
+        const bool ok = raw >= 0 && (int64_t)raw < p.num_blocks;
+        const int pb = ok ? raw : 0;
+        info[d] = pend[d].info;
+        if (!ok) info[d].meta &= kSegLast;
+        const uint4* kt = reinterpret_cast<const uint4*>(k_head + (int64_t)pb * block_stride);
+        const uint2* vt = reinterpret_cast<const uint2*>(v_head + (int64_t)pb * block_stride);
+        const uint4* qr = reinterpret_cast<const uint4*>(q_base + (int64_t)info[d].seq * Hq * D);
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk) ring[d].k[kk] = kt[kk * 64 + lane];
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk) ring[d].q[kk] = __builtin_bit_cast(bf16x8_t, qr[4 * kk + g]);
+        const int vo = (lane & 15) * 4 + (lane >> 4);
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) ring[d].v[c] = vt[c * 64 + vo];
+        fetch(k_next, pend[d]);
+    };
 
     float4_t acc[D / 16];
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) acc[c] = {0.f, 0.f, 0.f, 0.f};
     SoftmaxState st{-INFINITY, 0.f};
 
-    // i-th block of this wave -> physical block and number of valid tokens
-    auto block_of = [&](int i, int& valid_n) {
-        const int j = wave + kWaves * i;
-        const int pb = __builtin_amdgcn_readlane(bt_lane, j);
-        const bool ok = pb >= 0 && (int64_t)pb < p.num_blocks;
-        valid_n = ok ? L - (blk0 + j) * kBlockSize : 0;
-        return ok ? pb : 0;
+    // End of a segment: finish the sequence (out = o / l) or leave the
+    // piece's statistics for the merge, then start afresh.
+    auto finish_segment = [&](int seq, int slot) {
+        const float l_tot = sum_over_groups(st.l);
+        if (col < nh) {
+            if (slot < 0) {
+                const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+                const int64_t o = ((int64_t)seq * Hq + h0 + col) * D + 4 * g;
+                if (p.out_bf16) {
+                    uint16_t* ob = reinterpret_cast<uint16_t*>(p.out) + o;
+#pragma unroll
+                    for (int c = 0; c < D / 16; ++c)
+                        *reinterpret_cast<uint2*>(ob + 16 * c) =
+                            make_uint2(f32_to_bf16_bits(acc[c][0] * inv) | (f32_to_bf16_bits(acc[c][1] * inv) << 16),
+                                       f32_to_bf16_bits(acc[c][2] * inv) | (f32_to_bf16_bits(acc[c][3] * inv) << 16));
+                } else {
+                    float* of = reinterpret_cast<float*>(p.out) + o;
+#pragma unroll
+                    for (int c = 0; c < D / 16; ++c)
+                        *reinterpret_cast<float4*>(of + 16 * c) =
+                            make_float4(acc[c][0] * inv, acc[c][1] * inv, acc[c][2] * inv, acc[c][3] * inv);
+                }
+            } else {
+                const int64_t row = (int64_t)slot * Hq + h0 + col;
+                float* of = p.o_part + row * D + 4 * g;
+#pragma unroll
+                for (int c = 0; c < D / 16; ++c)
+                    *reinterpret_cast<float4*>(of + 16 * c) = make_float4(acc[c][0], acc[c][1], acc[c][2], acc[c][3]);
+                if (g == 0) {
+                    p.m_part[row] = st.m;
+                    p.l_part[row] = l_tot;
+                }
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) acc[c] = {0.f, 0.f, 0.f, 0.f};
+        st.m = -INFINITY;
+        st.l = 0.f;
     };
 
-    if (nbw > 0) {
-        // Ring of kDepth blocks in flight.  The refill of a slot is issued
-        // unconditionally (past the end it re-reads the wave's last block,
-        // an L2 hit), so the number of loads in flight is the same on every
-        // path and the wait before a block covers only that block's loads.
-        BlockRegs<D> ring[kDepth];
-        int vn[kDepth];
+    // The scheduling barriers keep each refill's loads together and in slot
+    // order, in the prologue as in the loop, so the count of loads issued
+    // after a slot's loads is the same on every path into the loop and the
+    // compiler waits for exactly that slot.
 #pragma unroll
-        for (int d = 0; d < kDepth; ++d)
-            load_block<D>(ring[d], k_head, v_head, block_stride, block_of(min(d, nbw - 1), vn[d]), lane);
-        for (int i = 0; i < nbw; i += kDepth) {
+    for (int d = 0; d < kDepth; ++d) fetch(d, pend[d]);
 #pragma unroll
-            for (int d = 0; d < kDepth; ++d) {
-                if (i + d < nbw) compute_block<D>(ring[d], qop, acc, st, vn[d], p.scale_log2, g);
-                load_block<D>(ring[d], k_head, v_head, block_stride, block_of(min(i + d + kDepth, nbw - 1), vn[d]),
-                              lane);
-            }
-        }
+    for (int d = 0; d < kDepth; ++d) {
+        load_slot(d, d + kDepth);
+        __builtin_amdgcn_sched_barrier(0);
     }
-
-    float l_tot = st.l + __shfl_xor(st.l, 16);
-    l_tot = l_tot + __shfl_xor(l_tot, 32);
-
-    // Epilogue.  Each wave parks its unnormalised accumulator tiles (lane:
-    // head col, dims 16c+4g..) and its (m, l) per head in LDS; the
-    // workgroup then merges the waves with the log-sum-exp weights
-    // 2^(m_w - M) in wave order and writes the unit's nh rows of D values
-    // -- contiguous in either destination (out[s][h0..][:], or the partial
-    // block of (s, part) laid out [part][head][dim]) -- as 16-byte pieces.
-    __shared__ float tile[kWaves][kMfmaHeadsPerUnit][D + 4];
-    __shared__ float m_w[kWaves][kMfmaHeadsPerUnit];
-    __shared__ float l_w[kWaves][kMfmaHeadsPerUnit];
+    for (int i = 0; i < K; i += kDepth) {
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c)
-        *reinterpret_cast<float4*>(&tile[wave][col][16 * c + 4 * g]) = make_float4(acc[c][0], acc[c][1], acc[c][2], acc[c][3]);
-    if (g == 0) {
-        m_w[wave][col] = st.m;
-        l_w[wave][col] = l_tot;
-    }
-    __syncthreads();
-    constexpr int kQuads = D / 4;  // 16-byte pieces per fp32 row
-    const int n4 = nh * kQuads;
-    const bool single = n_parts == 1;
-    for (int f = threadIdx.x; f < n4; f += 64 * kWaves) {
-        const int row = f / kQuads;
-        const int c4 = f % kQuads;
-        float M = m_w[0][row];
-#pragma unroll
-        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, m_w[w][row]);
-        const float M_use = (M == -INFINITY) ? 0.f : M;
-        float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
-        float den = 0.f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            const float a = kWaves == 1 ? 1.f : exp2_fast(m_w[w][row] - M_use);
-            const float4 v = *reinterpret_cast<const float4*>(&tile[w][row][4 * c4]);
-            num.x = fmaf(a, v.x, num.x);
-            num.y = fmaf(a, v.y, num.y);
-            num.z = fmaf(a, v.z, num.z);
-            num.w = fmaf(a, v.w, num.w);
-            den = fmaf(a, l_w[w][row], den);
-        }
-        if (single) {
-            const float inv = den > 0.f ? 1.f / den : 0.f;
-            const int64_t o = ((int64_t)s * Hq + h0) * D + 4 * f;
-            if (p.out_bf16) {
-                const uint2 w2 = make_uint2(f32_to_bf16_bits(num.x * inv) | (f32_to_bf16_bits(num.y * inv) << 16),
-                                            f32_to_bf16_bits(num.z * inv) | (f32_to_bf16_bits(num.w * inv) << 16));
-                *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + o) = w2;
-            } else {
-                *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + o) =
-                    make_float4(num.x * inv, num.y * inv, num.z * inv, num.w * inv);
+        for (int d = 0; d < kDepth; ++d) {
+            if (i + d < K) {
+                compute_block<D>(ring[d], acc, st, info[d].meta & 31, p.scale_log2, g);
+                if (info[d].meta & kSegLast) finish_segment(info[d].seq, info[d].slot);
             }
-        } else {
-            const int64_t row0 = ((int64_t)s * p.num_parts + part) * Hq + h0;
-            *reinterpret_cast<float4*>(p.o_part + row0 * D + 4 * f) = num;
-            if (c4 == 0) {
-                p.m_part[row0 + row] = M;
-                p.l_part[row0 + row] = den;
-            }
+            __builtin_amdgcn_sched_barrier(0);
+            load_slot(d, i + d + 2 * kDepth);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 }
 
 }  // namespace
 
-hipError_t launch_decode_bf16_mfma(const DecodeParams& p, hipStream_t stream) {
-    const int64_t units = decode_units(p);
-    if (units == 0) return hipSuccess;
-    const dim3 grid((unsigned)units), block(64 * kWavesPerUnit);
+size_t balanced_lds_bytes(int32_t num_seqs) { return (size_t)(2 * num_seqs + 1) * sizeof(int32_t); }
+
+const void* balanced_kernel(int32_t head_dim) {
+    return head_dim == 128 ? reinterpret_cast<const void*>(&decode_bf16_balanced_kernel<128, kPrefetchBlocks>)
+                           : reinterpret_cast<const void*>(&decode_bf16_balanced_kernel<64, kPrefetchBlocks>);
+}
+
+hipError_t launch_decode_bf16_balanced(const DecodeParams& p, hipStream_t stream) {
+    if (p.num_seqs == 0) return hipSuccess;
+    const dim3 grid((unsigned)((int64_t)p.walkers * p.head_unit_groups)), block(64 * p.waves_per_group);
+    const size_t lds = balanced_lds_bytes(p.num_seqs);
     if (p.head_dim == 128)
-        hipLaunchKernelGGL((decode_bf16_mfma_kernel<128, kPrefetchBlocks, kWavesPerUnit>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((decode_bf16_balanced_kernel<128, kPrefetchBlocks>), grid, block, lds, stream, p);
     else
-        hipLaunchKernelGGL((decode_bf16_mfma_kernel<64, kPrefetchBlocks, kWavesPerUnit>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((decode_bf16_balanced_kernel<64, kPrefetchBlocks>), grid, block, lds, stream, p);
     return hipGetLastError();
 }
 

@@ -8,10 +8,12 @@
 
 namespace pkv {
 
-constexpr int kBlockSize = 16;       // tokens per KV block
-constexpr int kMaxPartBlocks = 64;   // blocks per split-K partition (1024 tokens)
-constexpr int kMfmaHeadsPerUnit = 16;  // query heads one MFMA decode wave serves (tile width)
-constexpr int kValuHeadsPerUnit = 8;   // query heads one VALU decode wave serves (register budget)
+constexpr int kBlockSize = 16;           // tokens per KV block
+constexpr int kMfmaHeadsPerUnit = 16;    // query heads one MFMA decode wave serves (tile width)
+constexpr int kValuHeadsPerUnit = 8;     // query heads one VALU decode wave serves (register budget)
+constexpr int kMaxWavesPerGroup = 8;     // KV-head waves in one balanced-decode workgroup
+constexpr int kMaxSeqsPerLaunch = 4096;  // sequences one balanced-decode launch takes (LDS tables)
+constexpr int kMinRangeBlocks = 4;       // shortest range of blocks one workgroup walks
 
 // Everything one decode launch needs.  Passed by value as the kernel argument.
 struct DecodeParams {
@@ -21,33 +23,65 @@ struct DecodeParams {
     const int32_t* block_tables; // [B][max_blocks_per_seq]
     const int32_t* context_lens; // [B]
     void* out;                   // [B][Hq][D]
-    float* o_part;               // [B][P][Hq][D]   (split only)
-    float* m_part;               // [B][P][Hq]      reference max, log2 units
-    float* l_part;               // [B][P][Hq]      sum of 2^(s - m)
+    float* o_part;               // partial outputs (layout depends on the path, see below)
+    float* m_part;               // partial reference max, log2 units
+    float* l_part;               // partial sum of 2^(s - m)
+    int32_t* seq_off;            // balanced path: [B + 1] first flattened block of each sequence
     float scale_log2;            // scale * log2(e)
     int32_t num_seqs;
     int32_t num_q_heads;
     int32_t num_kv_heads;
     int32_t group;               // Hq / Hkv
-    int32_t heads_per_unit;      // query heads per decode wave
-    int32_t n_head_groups;       // ceil(group / heads_per_unit)
+    int32_t n_head_groups;       // ceil(group / heads per wave)
     int32_t head_dim;
     int64_t num_blocks;          // pool size; table entries outside it are skipped
     int32_t max_blocks_per_seq;
     int32_t ctx_cap;             // context lengths are clamped to [0, ctx_cap]
-    int32_t part_blocks;         // blocks per partition
-    int32_t num_parts;           // P = partitions covering ctx_cap
     int32_t out_bf16;            // 1: bf16 output, 0: f32 output
+    // partitioned path (fp32 KV): fixed partitions of part_blocks blocks,
+    // partials laid out [B][P][Hq](×D)
+    int32_t part_blocks;
+    int32_t num_parts;
+    // balanced path (bf16 KV): `walkers` workgroup columns split the
+    // flattened block list of all sequences into ranges; partials laid out
+    // [2 * ranges][Hq](×D)
+    int32_t walkers;             // workgroups per head-unit group
+    int32_t range_cap;           // longest range in blocks (0 = no cap)
+    int32_t waves_per_group;     // KV-head waves per workgroup
+    int32_t head_units;          // Hkv * n_head_groups
+    int32_t head_unit_groups;    // ceil(head_units / waves_per_group)
 };
 
-// Number of decode work units (one wave each) the partition kernels launch.
+// Split of T flattened blocks into ranges for `walkers` workgroups: each
+// range holds `cs` blocks (the last one possibly fewer), `nr` ranges in all.
+// Shared by the decode and the reduce so that both see the same ranges.
+__host__ __device__ inline void range_geometry(int32_t T, int32_t walkers, int32_t cap, int32_t& cs, int32_t& nr) {
+    int32_t c = T > 0 ? (T + walkers - 1) / walkers : 1;
+    if (c < kMinRangeBlocks) c = kMinRangeBlocks;
+    if (cap > 0 && c > cap) c = cap;
+    cs = c;
+    nr = T > 0 ? (T + c - 1) / c : 0;
+}
+
+// Partial-result row of range r for a sequence whose blocks start at flattened
+// offset `first`: slot 0 if the sequence began before the range (the range's
+// first piece), slot 1 otherwise (its last piece).
+__host__ __device__ inline int32_t range_slot(int32_t r, int32_t cs, int32_t first) {
+    return 2 * r + (first < r * cs ? 0 : 1);
+}
+
+// Number of decode work units (one wave each) the partitioned kernel launches.
 inline int64_t decode_units(const DecodeParams& p) {
     return (int64_t)p.num_parts * p.num_seqs * p.n_head_groups * p.num_kv_heads;
 }
 
-hipError_t launch_decode_bf16_mfma(const DecodeParams& p, hipStream_t stream);
+// Balanced bf16 decode: dynamic LDS bytes and launch shape.
+size_t balanced_lds_bytes(int32_t num_seqs);
+const void* balanced_kernel(int32_t head_dim);
+
+hipError_t launch_decode_bf16_balanced(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeParams& p, bool bf16, hipStream_t stream);
-hipError_t launch_splitk_reduce(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_splitk_reduce(const DecodeParams& p, bool balanced, hipStream_t stream);
 hipError_t launch_cache_write(const void* k_new, const void* v_new, const int64_t* slot_mapping,
                               void* k_cache, void* v_cache, int64_t num_tokens, int32_t num_kv_heads,
                               int32_t head_dim, int64_t num_blocks, bool bf16, hipStream_t stream);

@@ -1,5 +1,5 @@
-// C-ABI layer of libpagedkv.so: argument checks, workspace carving, launch
-// selection.  Declarations and the contract of every entry point are in
+// C-ABI layer of libpagedkv.so: argument checks, launch planning, workspace
+// carving.  Declarations and the contract of every entry point are in
 // include/pagedkv.h.  Nothing here allocates, frees or synchronises.
 #include <math.h>
 #include <stdarg.h>
@@ -28,35 +28,55 @@ pkv_status from_hip(hipError_t e, const char* what) {
 
 bool dtype_ok(pkv_dtype d) { return d == PKV_F32 || d == PKV_BF16; }
 
-int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Effective context cap: lengths are clamped to what the tables can address.
-int32_t context_cap(int32_t max_context_len, int32_t max_blocks_per_seq, int32_t block_size) {
-    const int64_t by_table = (int64_t)max_blocks_per_seq * block_size;
-    return (int32_t)(max_context_len < by_table ? max_context_len : by_table);
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+constexpr int32_t kMaxPartitionTokens = 1 << 24;
+constexpr int32_t kValuAutoPartition = 1024;  // fp32 path: automatic partition length (tokens)
+
+// Workgroups of the balanced decode that fit on the current device at once.
+int64_t resident_groups(int32_t head_dim, int32_t waves_per_group, int32_t seqs_per_launch) {
+    int dev = 0, cus = 0, per_cu = 0;
+    const size_t lds = pkv::balanced_lds_bytes(seqs_per_launch);
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0 ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, pkv::balanced_kernel(head_dim), 64 * waves_per_group,
+                                                     lds) != hipSuccess ||
+        per_cu <= 0) {
+        (void)hipGetLastError();  // no usable device: plan for a 256-CU part, two waves per SIMD
+        cus = 256;
+        per_cu = waves_per_group >= pkv::kMaxWavesPerGroup ? 1 : pkv::kMaxWavesPerGroup / waves_per_group;
+    }
+    return (int64_t)cus * per_cu;
 }
 
-int32_t auto_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len) {
-    (void)num_seqs;
-    (void)num_kv_heads;
-    const int32_t bs = pkv::kBlockSize;
-    const int32_t cap = pkv::kMaxPartBlocks * bs;
-    if (max_context_len <= 0) return bs;
-    if (max_context_len <= cap) return ceil_div(max_context_len, bs) * bs;  // one partition, no reduce
-    // the waves of a decode workgroup split a partition's blocks among
-    // themselves, so long partitions keep every wave busy with few partials
-    return cap;
-}
-
-struct Resolved {
+// How one decode call is carried out.
+struct Plan {
+    bool balanced;       // bf16 KV: balanced ranges; fp32 KV: fixed partitions
+    int32_t ctx_cap;     // context lengths are clamped to this
+    int32_t group;
+    int32_t n_head_groups;
+    // partitioned path
     int32_t part_tokens;
     int32_t num_parts;
-    int32_t ctx_cap;
-    size_t workspace;
+    // balanced path
+    int32_t chunk_seqs;  // sequences per launch
+    int32_t num_chunks;
+    int32_t walkers;
+    int32_t waves_per_group;
+    int32_t head_units;
+    int32_t head_unit_groups;
+    int32_t range_cap;   // blocks
+    int64_t max_ranges;  // per launch
+    size_t off_bytes;    // per-launch offset table
+    size_t chunk_bytes;  // per-launch workspace
+    size_t workspace;    // whole call
 };
 
-pkv_status resolve(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                   int32_t max_blocks_per_seq, int32_t max_context_len, int32_t partition_size, Resolved* r) {
+pkv_status make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                     int32_t block_size, int32_t max_blocks_per_seq, int32_t max_context_len, int32_t partition_size,
+                     pkv_dtype kv_dtype, Plan* pl) {
     if (num_seqs < 0) return fail(PKV_ERR_INVALID_ARG, "num_seqs must be >= 0 (got %d)", num_seqs);
     if (num_q_heads <= 0 || num_kv_heads <= 0)
         return fail(PKV_ERR_INVALID_ARG, "head counts must be positive (q %d, kv %d)", num_q_heads, num_kv_heads);
@@ -65,85 +85,178 @@ pkv_status resolve(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, 
                     num_kv_heads);
     if (head_dim != 64 && head_dim != 128) return fail(PKV_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", head_dim);
     if (block_size != pkv::kBlockSize) return fail(PKV_ERR_UNSUPPORTED, "block_size %d (supported: 16)", block_size);
+    if (!dtype_ok(kv_dtype)) return fail(PKV_ERR_UNSUPPORTED, "unknown KV dtype");
     if (max_blocks_per_seq < 0 || max_context_len < 0)
         return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq and max_context_len must be >= 0");
     if (partition_size != 0 &&
-        (partition_size < block_size || partition_size > pkv::kMaxPartBlocks * block_size || partition_size % block_size))
+        (partition_size < block_size || partition_size > kMaxPartitionTokens || partition_size % block_size))
         return fail(PKV_ERR_UNSUPPORTED, "partition_size %d: 0 or a multiple of %d in [%d, %d]", partition_size,
-                    block_size, block_size, pkv::kMaxPartBlocks * block_size);
-    // partition count and workspace depend on max_context_len only, so the
-    // workspace query agrees with every decode call of the same sizes
-    const int32_t pt = partition_size ? partition_size : auto_partition(num_seqs, num_kv_heads, max_context_len);
-    r->part_tokens = pt;
-    r->ctx_cap = context_cap(max_context_len, max_blocks_per_seq, block_size);
-    r->num_parts = max_context_len > 0 ? ceil_div(max_context_len, pt) : 1;
-    r->workspace = r->num_parts > 1 ? (size_t)num_seqs * num_q_heads * r->num_parts * (head_dim + 2) * sizeof(float) : 0;
+                    block_size, block_size, kMaxPartitionTokens);
+    memset(pl, 0, sizeof(*pl));
+    const int64_t by_table = (int64_t)max_blocks_per_seq * block_size;
+    pl->ctx_cap = (int32_t)(max_context_len < by_table ? max_context_len : by_table);
+    pl->group = num_q_heads / num_kv_heads;
+    pl->balanced = kv_dtype == PKV_BF16;
+    const int32_t heads_per_wave = pl->balanced ? pkv::kMfmaHeadsPerUnit : pkv::kValuHeadsPerUnit;
+    pl->n_head_groups = (int32_t)ceil_div(pl->group, heads_per_wave);
+    if (!pl->balanced) {
+        // partition count and workspace depend on max_context_len only, so the
+        // workspace query agrees with every decode call of the same sizes
+        int32_t pt = partition_size;
+        if (!pt) pt = max_context_len <= kValuAutoPartition ? (int32_t)(ceil_div(max_context_len, block_size) * block_size)
+                                                            : kValuAutoPartition;
+        if (pt <= 0) pt = block_size;
+        pl->part_tokens = pt;
+        pl->num_parts = max_context_len > 0 ? (int32_t)ceil_div(max_context_len, pt) : 1;
+        pl->workspace =
+            pl->num_parts > 1 ? (size_t)num_seqs * num_q_heads * pl->num_parts * (head_dim + 2) * sizeof(float) : 0;
+        return PKV_OK;
+    }
+    pl->chunk_seqs = num_seqs < pkv::kMaxSeqsPerLaunch ? num_seqs : pkv::kMaxSeqsPerLaunch;
+    pl->num_chunks = num_seqs > 0 ? (int32_t)ceil_div(num_seqs, pl->chunk_seqs) : 0;
+    pl->head_units = num_kv_heads * pl->n_head_groups;
+    pl->waves_per_group = pl->head_units < pkv::kMaxWavesPerGroup ? pl->head_units : pkv::kMaxWavesPerGroup;
+    pl->head_unit_groups = (int32_t)ceil_div(pl->head_units, pl->waves_per_group);
+    const int64_t slots = resident_groups(head_dim, pl->waves_per_group, pl->chunk_seqs > 0 ? pl->chunk_seqs : 1);
+    const int64_t w = slots / pl->head_unit_groups;
+    pl->walkers = (int32_t)(w < 1 ? 1 : (w > (1 << 20) ? (1 << 20) : w));
+    pl->range_cap = partition_size / block_size;
+    const int64_t t_max = (int64_t)pl->chunk_seqs * ceil_div(pl->ctx_cap, block_size);
+    if (t_max >= (int64_t)1 << 30)
+        return fail(PKV_ERR_UNSUPPORTED, "%d sequences of up to %d tokens: too many blocks for one launch",
+                    pl->chunk_seqs, pl->ctx_cap);
+    int64_t nr = pl->walkers;
+    if (pl->range_cap > 0 && ceil_div(t_max, pl->range_cap) > nr) nr = ceil_div(t_max, pl->range_cap);
+    pl->max_ranges = nr;
+    pl->off_bytes = align_up((size_t)(pl->chunk_seqs + 1) * sizeof(int32_t), 256);
+    pl->chunk_bytes =
+        align_up(pl->off_bytes + (size_t)(2 * nr) * num_q_heads * (head_dim + 2) * sizeof(float), 256);
+    pl->workspace = num_seqs > 0 ? pl->chunk_bytes * pl->num_chunks : 0;
     return PKV_OK;
 }
 
-pkv_status build_params(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
-                        const int32_t* context_lens, float scale, void* out, int32_t num_seqs, int32_t num_q_heads,
-                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
-                        int32_t max_blocks_per_seq, int32_t max_context_len, int32_t partition_size, void* workspace,
-                        size_t workspace_bytes, pkv_dtype kv_dtype, pkv_dtype out_dtype, pkv::DecodeParams* p,
-                        Resolved* r) {
-    pkv_status st = resolve(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
-                            max_context_len, partition_size, r);
+// The arguments of one decode call, checked.
+struct Call {
+    Plan plan;
+    pkv::DecodeParams base;
+    pkv_dtype kv_dtype;
+    size_t q_row_bytes;    // bytes of q per sequence
+    size_t out_row_bytes;  // bytes of out per sequence
+    char* workspace;
+};
+
+pkv_status prepare(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                   const int32_t* context_lens, float scale, void* out, int32_t num_seqs, int32_t num_q_heads,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                   int32_t max_blocks_per_seq, int32_t max_context_len, int32_t partition_size, void* workspace,
+                   size_t workspace_bytes, pkv_dtype kv_dtype, pkv_dtype out_dtype, Call* c) {
+    pkv_status st = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                              max_context_len, partition_size, kv_dtype, &c->plan);
     if (st != PKV_OK) return st;
-    if (!dtype_ok(kv_dtype) || !dtype_ok(out_dtype)) return fail(PKV_ERR_UNSUPPORTED, "unknown dtype");
+    const Plan& pl = c->plan;
+    if (!dtype_ok(out_dtype)) return fail(PKV_ERR_UNSUPPORTED, "unknown output dtype");
     if (num_seqs > 0 && (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out))
         return fail(PKV_ERR_INVALID_ARG, "null tensor pointer");
     if (num_blocks <= 0 && num_seqs > 0) return fail(PKV_ERR_INVALID_ARG, "num_blocks must be positive");
     if (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)out) % 16)
         return fail(PKV_ERR_INVALID_ARG, "q, k_cache, v_cache and out must be 16-byte aligned");
     if (!isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "scale must be finite");
-    if (r->workspace > 0) {
-        if (!workspace) return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", r->workspace);
-        if (workspace_bytes < r->workspace)
-            return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", r->workspace, workspace_bytes);
+    if (pl.workspace > 0) {
+        if (!workspace) return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", pl.workspace);
+        if (workspace_bytes < pl.workspace)
+            return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", pl.workspace, workspace_bytes);
         if (((uintptr_t)workspace) % 256) return fail(PKV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
     }
-    const int32_t group = num_q_heads / num_kv_heads;
-    p->q = q;
-    p->k_cache = k_cache;
-    p->v_cache = v_cache;
-    p->block_tables = block_tables;
-    p->context_lens = context_lens;
-    p->out = out;
-    const size_t rows = (size_t)num_seqs * num_q_heads * r->num_parts;
+    pkv::DecodeParams& p = c->base;
+    memset(&p, 0, sizeof(p));
+    p.q = q;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.block_tables = block_tables;
+    p.context_lens = context_lens;
+    p.out = out;
+    p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+    p.num_seqs = num_seqs;
+    p.num_q_heads = num_q_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.group = pl.group;
+    p.n_head_groups = pl.n_head_groups;
+    p.head_dim = head_dim;
+    p.num_blocks = num_blocks;
+    p.max_blocks_per_seq = max_blocks_per_seq;
+    p.ctx_cap = pl.ctx_cap;
+    p.out_bf16 = out_dtype == PKV_BF16;
     float* ws = static_cast<float*>(workspace);
-    p->o_part = r->workspace ? ws : nullptr;
-    p->m_part = r->workspace ? ws + rows * head_dim : nullptr;
-    p->l_part = r->workspace ? ws + rows * (head_dim + 1) : nullptr;
-    p->scale_log2 = (float)((double)scale * 1.4426950408889634);
-    p->num_seqs = num_seqs;
-    p->num_q_heads = num_q_heads;
-    p->num_kv_heads = num_kv_heads;
-    p->group = group;
-    p->heads_per_unit = kv_dtype == PKV_BF16 ? pkv::kMfmaHeadsPerUnit : pkv::kValuHeadsPerUnit;
-    p->n_head_groups = (group + p->heads_per_unit - 1) / p->heads_per_unit;
-    p->head_dim = head_dim;
-    p->num_blocks = num_blocks;
-    p->max_blocks_per_seq = max_blocks_per_seq;
-    p->ctx_cap = r->ctx_cap;
-    p->part_blocks = r->part_tokens / block_size;
-    p->num_parts = r->num_parts;
-    p->out_bf16 = out_dtype == PKV_BF16;
+    if (pl.balanced) {
+        p.walkers = pl.walkers;
+        p.range_cap = pl.range_cap;
+        p.waves_per_group = pl.waves_per_group;
+        p.head_units = pl.head_units;
+        p.head_unit_groups = pl.head_unit_groups;
+    } else {
+        p.part_blocks = pl.part_tokens / block_size;
+        p.num_parts = pl.num_parts;
+        const size_t rows = (size_t)num_seqs * num_q_heads * pl.num_parts;
+        p.o_part = pl.workspace ? ws : nullptr;
+        p.m_part = pl.workspace ? ws + rows * head_dim : nullptr;
+        p.l_part = pl.workspace ? ws + rows * (head_dim + 1) : nullptr;
+    }
+    c->kv_dtype = kv_dtype;
+    c->q_row_bytes = (size_t)num_q_heads * head_dim * (kv_dtype == PKV_BF16 ? 2 : 4);
+    c->out_row_bytes = (size_t)num_q_heads * head_dim * (out_dtype == PKV_BF16 ? 2 : 4);
+    c->workspace = static_cast<char*>(workspace);
     return PKV_OK;
 }
 
-pkv_status run_partitions(const pkv::DecodeParams& p, pkv_dtype kv_dtype, hipStream_t stream) {
-    if (p.num_seqs == 0) return PKV_OK;
-    hipError_t e = kv_dtype == PKV_BF16 ? pkv::launch_decode_bf16_mfma(p, stream)
-                                        : pkv::launch_decode_valu(p, false, stream);
-    return from_hip(e, "decode partition kernel launch");
+// Parameters of launch chunk i of a balanced call (a slice of the batch with
+// its own region of the workspace).
+pkv::DecodeParams chunk_params(const Call& c, int32_t i) {
+    const Plan& pl = c.plan;
+    pkv::DecodeParams p = c.base;
+    const int32_t s0 = i * pl.chunk_seqs;
+    const int32_t n = c.base.num_seqs - s0 < pl.chunk_seqs ? c.base.num_seqs - s0 : pl.chunk_seqs;
+    p.num_seqs = n;
+    p.q = static_cast<const char*>(c.base.q) + (size_t)s0 * c.q_row_bytes;
+    p.out = static_cast<char*>(c.base.out) + (size_t)s0 * c.out_row_bytes;
+    p.block_tables = c.base.block_tables + (int64_t)s0 * c.base.max_blocks_per_seq;
+    p.context_lens = c.base.context_lens + s0;
+    char* w = c.workspace + (size_t)i * pl.chunk_bytes;
+    p.seq_off = reinterpret_cast<int32_t*>(w);
+    const size_t rows = (size_t)(2 * pl.max_ranges) * c.base.num_q_heads;
+    float* f = reinterpret_cast<float*>(w + pl.off_bytes);
+    p.o_part = f;
+    p.m_part = f + rows * c.base.head_dim;
+    p.l_part = f + rows * (c.base.head_dim + 1);
+    return p;
+}
+
+pkv_status run_decode_kernels(const Call& c, hipStream_t stream) {
+    if (c.base.num_seqs == 0) return PKV_OK;
+    if (!c.plan.balanced)
+        return from_hip(pkv::launch_decode_valu(c.base, false, stream), "decode partition kernel launch");
+    for (int32_t i = 0; i < c.plan.num_chunks; ++i) {
+        pkv_status st = from_hip(pkv::launch_decode_bf16_balanced(chunk_params(c, i), stream), "decode kernel launch");
+        if (st != PKV_OK) return st;
+    }
+    return PKV_OK;
+}
+
+pkv_status run_reduce_kernels(const Call& c, hipStream_t stream) {
+    if (c.base.num_seqs == 0) return PKV_OK;
+    if (!c.plan.balanced)
+        return from_hip(pkv::launch_splitk_reduce(c.base, false, stream), "split-K reduce launch");
+    for (int32_t i = 0; i < c.plan.num_chunks; ++i) {
+        pkv_status st = from_hip(pkv::launch_splitk_reduce(chunk_params(c, i), true, stream), "split-K reduce launch");
+        if (st != PKV_OK) return st;
+    }
+    return PKV_OK;
 }
 
 }  // namespace
 
 extern "C" {
 
-int32_t pkv_abi_version(void) { return 1; }
+int32_t pkv_abi_version(void) { return 2; }
 
 const char* pkv_status_string(pkv_status status) {
     switch (status) {
@@ -177,21 +290,15 @@ pkv_status pkv_reshape_and_cache(const void* k_new, const void* v_new, const int
                     "reshape_and_cache launch");
 }
 
-int32_t pkv_decode_auto_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                       int32_t max_context_len) {
-    (void)num_q_heads;
-    (void)head_dim;
-    return auto_partition(num_seqs, num_kv_heads > 0 ? num_kv_heads : 1, max_context_len);
-}
-
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                  int32_t max_context_len, int32_t partition_size) {
-    Resolved r;
-    const int32_t blocks = ceil_div(max_context_len > 0 ? max_context_len : 0, pkv::kBlockSize);
-    if (resolve(num_seqs, num_q_heads, num_kv_heads, head_dim, pkv::kBlockSize, blocks, max_context_len,
-                partition_size, &r) != PKV_OK)
-        return 0;
-    return r.workspace;
+                                  int32_t max_context_len, int32_t partition_size, pkv_dtype kv_dtype) {
+    Plan pl;
+    const int32_t blocks = (int32_t)ceil_div(max_context_len > 0 ? max_context_len : 0, pkv::kBlockSize);
+    const char saved = g_last_error[0];
+    pkv_status st = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, pkv::kBlockSize, blocks,
+                              max_context_len, partition_size, kv_dtype, &pl);
+    g_last_error[0] = saved;
+    return st == PKV_OK ? pl.workspace : 0;
 }
 
 pkv_status pkv_paged_attention_decode_partitions(const void* q, const void* k_cache, const void* v_cache,
@@ -202,32 +309,29 @@ pkv_status pkv_paged_attention_decode_partitions(const void* q, const void* k_ca
                                                  int32_t partition_size, void* workspace, size_t workspace_bytes,
                                                  pkv_dtype kv_dtype, pkv_dtype out_dtype, void* stream) {
     g_last_error[0] = 0;
-    pkv::DecodeParams p;
-    Resolved r;
-    pkv_status st = build_params(q, k_cache, v_cache, block_tables, context_lens, scale, out, num_seqs, num_q_heads,
-                                 num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len,
-                                 partition_size, workspace, workspace_bytes, kv_dtype, out_dtype, &p, &r);
+    Call c;
+    pkv_status st = prepare(q, k_cache, v_cache, block_tables, context_lens, scale, out, num_seqs, num_q_heads,
+                            num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len,
+                            partition_size, workspace, workspace_bytes, kv_dtype, out_dtype, &c);
     if (st != PKV_OK) return st;
-    return run_partitions(p, kv_dtype, static_cast<hipStream_t>(stream));
+    return run_decode_kernels(c, static_cast<hipStream_t>(stream));
 }
 
 pkv_status pkv_paged_attention_decode_reduce(const int32_t* context_lens, void* out, int32_t num_seqs,
                                              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                              int32_t block_size, int32_t max_blocks_per_seq, int32_t max_context_len,
                                              int32_t partition_size, void* workspace, size_t workspace_bytes,
-                                             pkv_dtype out_dtype, void* stream) {
+                                             pkv_dtype kv_dtype, pkv_dtype out_dtype, void* stream) {
     g_last_error[0] = 0;
-    pkv::DecodeParams p;
-    Resolved r;
+    Call c;
     // the reduce reads only lengths, partials and out; the K/V/q/table
     // pointers are not used, so stand-ins keep the shared checks happy
     const void* unused = context_lens;
-    pkv_status st = build_params(unused, unused, unused, context_lens, context_lens, 1.0f, out, num_seqs, num_q_heads,
-                                 num_kv_heads, head_dim, block_size, 1, max_blocks_per_seq, max_context_len,
-                                 partition_size, workspace, workspace_bytes, PKV_BF16, out_dtype, &p, &r);
+    pkv_status st = prepare(unused, unused, unused, context_lens, context_lens, 1.0f, out, num_seqs, num_q_heads,
+                            num_kv_heads, head_dim, block_size, 1, max_blocks_per_seq, max_context_len,
+                            partition_size, workspace, workspace_bytes, kv_dtype, out_dtype, &c);
     if (st != PKV_OK) return st;
-    if (num_seqs == 0) return PKV_OK;
-    return from_hip(pkv::launch_splitk_reduce(p, static_cast<hipStream_t>(stream)), "split-K reduce launch");
+    return run_reduce_kernels(c, static_cast<hipStream_t>(stream));
 }
 
 pkv_status pkv_paged_attention_decode(const void* q, const void* k_cache, const void* v_cache,
@@ -237,16 +341,15 @@ pkv_status pkv_paged_attention_decode(const void* q, const void* k_cache, const 
                                       int32_t max_context_len, int32_t partition_size, void* workspace,
                                       size_t workspace_bytes, pkv_dtype kv_dtype, pkv_dtype out_dtype, void* stream) {
     g_last_error[0] = 0;
-    pkv::DecodeParams p;
-    Resolved r;
-    pkv_status st = build_params(q, k_cache, v_cache, block_tables, context_lens, scale, out, num_seqs, num_q_heads,
-                                 num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len,
-                                 partition_size, workspace, workspace_bytes, kv_dtype, out_dtype, &p, &r);
+    Call c;
+    pkv_status st = prepare(q, k_cache, v_cache, block_tables, context_lens, scale, out, num_seqs, num_q_heads,
+                            num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len,
+                            partition_size, workspace, workspace_bytes, kv_dtype, out_dtype, &c);
     if (st != PKV_OK) return st;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    st = run_partitions(p, kv_dtype, s);
-    if (st != PKV_OK || p.num_parts <= 1 || num_seqs == 0) return st;
-    return from_hip(pkv::launch_splitk_reduce(p, s), "split-K reduce launch");
+    st = run_decode_kernels(c, s);
+    if (st != PKV_OK) return st;
+    return run_reduce_kernels(c, s);
 }
 
 }  // extern "C"

@@ -32,14 +32,13 @@ _vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ct
 _SIGNATURES = {
     "pkv_abi_version": (_i32, []),
     "pkv_reshape_and_cache": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _i32, _vp]),
-    "pkv_decode_auto_partition_size": (_i32, [_i32, _i32, _i32, _i32, _i32]),
-    "pkv_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "pkv_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pkv_paged_attention_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _f32, _vp, _i32, _i32, _i32, _i32, _i32, _i64,
                                           _i32, _i32, _i32, _vp, _sz, _i32, _i32, _vp]),
     "pkv_paged_attention_decode_partitions": (_i32, [_vp, _vp, _vp, _vp, _vp, _f32, _vp, _i32, _i32, _i32, _i32, _i32,
                                                      _i64, _i32, _i32, _i32, _vp, _sz, _i32, _i32, _vp]),
     "pkv_paged_attention_decode_reduce": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _sz,
-                                                 _i32, _vp]),
+                                                 _i32, _i32, _vp]),
     "pkv_status_string": (ctypes.c_char_p, [_i32]),
     "pkv_last_error": (ctypes.c_char_p, []),
 }
@@ -133,15 +132,11 @@ def reshape_and_cache(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: to
 
 
 def decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
-                           max_context_len: int, partition_size: int = 0) -> int:
+                           max_context_len: int, partition_size: int = 0, kv_dtype: torch.dtype = torch.bfloat16) -> int:
+    """Workspace bytes a decode of these sizes needs on the current device."""
+    code = PKV_BF16 if kv_dtype == torch.bfloat16 else PKV_F32
     return int(load_library().pkv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                                         max_context_len, partition_size))
-
-
-def auto_partition_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
-                        max_context_len: int) -> int:
-    return int(load_library().pkv_decode_auto_partition_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                                              max_context_len))
+                                                         max_context_len, partition_size, code))
 
 
 class _DecodeArgs:
@@ -166,7 +161,7 @@ class _DecodeArgs:
         self.max_context_len = int(max_context_len)
         self.B, self.hq, self.hkv, self.D, self.nb = B, hq, hkv, D, nb
         self.partition_size = int(partition_size)
-        need = decode_workspace_bytes(B, hq, hkv, D, self.max_context_len, self.partition_size)
+        need = decode_workspace_bytes(B, hq, hkv, D, self.max_context_len, self.partition_size, k_cache.dtype)
         if need and workspace is None:
             workspace = torch.empty(need, dtype=torch.uint8, device=dev)
         if workspace is not None:
@@ -179,8 +174,8 @@ class _DecodeArgs:
                      self.partition_size, self.ws_ptr, self.ws_bytes, _dtype_code(k_cache), _dtype_code(out),
                      _stream(dev))
         self.reduce_args = (_ptr(context_lens), _ptr(out), B, hq, hkv, D, BLOCK_SIZE, block_tables.shape[1],
-                            self.max_context_len, self.partition_size, self.ws_ptr, self.ws_bytes, _dtype_code(out),
-                            _stream(dev))
+                            self.max_context_len, self.partition_size, self.ws_ptr, self.ws_bytes,
+                            _dtype_code(k_cache), _dtype_code(out), _stream(dev))
 
 
 def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

@@ -51,7 +51,7 @@ def test_single_hip_runtime_in_process(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pkv_abi_version() == 1
+    assert lib.pkv_abi_version() == 2
     for code in range(5):
         assert lib.pkv_status_string(code)
     assert lib.pkv_status_string(99) == b"unknown status"
@@ -93,7 +93,7 @@ def test_decode_validation(lib):
     assert dec(lib, D=96) == UNSUPPORTED
     assert dec(lib, bs=32) == UNSUPPORTED
     assert dec(lib, ps=24) == UNSUPPORTED
-    assert dec(lib, ps=2048) == UNSUPPORTED
+    assert dec(lib, ps=(1 << 24) + 16) == UNSUPPORTED
     assert dec(lib, kvd=5) == UNSUPPORTED
     assert dec(lib, B=-1) == INVALID
     assert dec(lib, maxctx=-5) == INVALID
@@ -102,7 +102,7 @@ def test_decode_validation(lib):
     assert dec(lib, scale=math.inf) == INVALID
     assert dec(lib, scale=math.nan) == INVALID
     # split needed (2000 tokens > one partition): workspace missing / short / misaligned
-    need = lib.pkv_decode_workspace_bytes(4, 32, 8, 128, 2000, 0)
+    need = lib.pkv_decode_workspace_bytes(4, 32, 8, 128, 2000, 0, BF16)
     assert need > 0
     assert dec(lib, ws=None, wsb=need) == WORKSPACE
     assert dec(lib, wsb=need - 1) == WORKSPACE
@@ -110,23 +110,50 @@ def test_decode_validation(lib):
     assert dec(lib, ws=FAKE + 16, wsb=need) == WORKSPACE
     # nothing to do: no launch
     assert dec(lib, B=0, q=None, kc=None, vc=None, bt=None, lens=None, out=None, ws=None) == OK
-    red = lib.pkv_paged_attention_decode_reduce(FAKE, FAKE, 4, 32, 8, 128, 16, 128, 2000, 0, None, 0, BF16, None)
+    red = lib.pkv_paged_attention_decode_reduce(FAKE, FAKE, 4, 32, 8, 128, 16, 128, 2000, 0, None, 0, BF16, BF16, None)
     assert red == WORKSPACE
 
 
-def test_workspace_size_and_auto_partition(lib):
-    # fits one partition: no workspace
-    assert lib.pkv_decode_workspace_bytes(4, 4, 4, 64, 37, 0) == 0
-    assert lib.pkv_decode_auto_partition_size(4, 4, 4, 64, 37) == 48
-    assert lib.pkv_decode_auto_partition_size(4, 4, 4, 64, 512) == 512
-    for (B, hq, hkv, D, ctx, ps) in [(64, 32, 8, 128, 4096, 256), (8, 64, 8, 128, 131072, 512), (3, 4, 2, 64, 100, 16)]:
-        P = -(-ctx // ps)
-        assert lib.pkv_decode_workspace_bytes(B, hq, hkv, D, ctx, ps) == B * hq * P * (D + 2) * 4
-    ps = lib.pkv_decode_auto_partition_size(64, 32, 8, 128, 4096)
-    assert ps == 1024
-    assert lib.pkv_decode_workspace_bytes(64, 32, 8, 128, 4096, 0) == 64 * 32 * (-(-4096 // ps)) * 130 * 4
-    assert lib.pkv_decode_workspace_bytes(64, 30, 8, 128, 4096, 0) == 0   # invalid sizes
-    assert lib.pkv_decode_workspace_bytes(64, 32, 8, 128, 4096, 40) == 0
+def _align(x, a=256):
+    return -(-x // a) * a
+
+
+def balanced_workspace(B, hq, hkv, D, ctx, ps, walkers_per_head_group):
+    """Workspace of the bf16 (balanced) plan when no GPU is visible: a 256-CU part."""
+    chunk = min(B, 4096)
+    chunks = -(-B // chunk)
+    nr = walkers_per_head_group
+    if ps:
+        nr = max(nr, -(-(chunk * -(-ctx // 16)) // (ps // 16)))
+    per = _align(_align((chunk + 1) * 4) + 2 * nr * hq * (D + 2) * 4)
+    return per * chunks
+
+
+def test_workspace_sizes(lib):
+    # fp32 KV: fixed partitions; none needed when the context fits one partition
+    assert lib.pkv_decode_workspace_bytes(4, 4, 4, 64, 37, 0, F32) == 0
+    assert lib.pkv_decode_workspace_bytes(4, 4, 4, 64, 1024, 0, F32) == 0
+    for (B, hq, hkv, D, ctx, ps) in [(64, 32, 8, 128, 4096, 256), (8, 64, 8, 128, 131072, 512), (3, 4, 2, 64, 100, 16),
+                                     (64, 32, 8, 128, 4096, 0)]:
+        P = -(-ctx // (ps or 1024))
+        assert lib.pkv_decode_workspace_bytes(B, hq, hkv, D, ctx, ps, F32) == B * hq * P * (D + 2) * 4
+    # bf16 KV: always a workspace (flattened offsets + range partials); with
+    # no GPU the plan assumes 256 CUs holding one 8-wave workgroup each
+    assert not torch.cuda.is_available()
+    for (B, hq, hkv, D, ctx, ps) in [(64, 32, 8, 128, 4096, 0), (8, 64, 8, 128, 131072, 512), (256, 32, 8, 128, 8192, 0),
+                                     (5000, 32, 8, 128, 100, 0), (4, 8, 4, 64, 37, 16)]:
+        head_units = hkv * -(-(hq // hkv) // 16)
+        waves = min(head_units, 8)
+        groups = -(-head_units // waves)
+        per_cu = 1 if waves >= 8 else 8 // waves
+        walkers = max(1, 256 * per_cu // groups)
+        assert lib.pkv_decode_workspace_bytes(B, hq, hkv, D, ctx, ps, BF16) == \
+            balanced_workspace(B, hq, hkv, D, ctx, ps, walkers), (B, hq, hkv, D, ctx, ps)
+    assert lib.pkv_decode_workspace_bytes(0, 32, 8, 128, 4096, 0, BF16) == 0
+    # invalid sizes
+    assert lib.pkv_decode_workspace_bytes(64, 30, 8, 128, 4096, 0, BF16) == 0
+    assert lib.pkv_decode_workspace_bytes(64, 32, 8, 128, 4096, 40, BF16) == 0
+    assert lib.pkv_decode_workspace_bytes(64, 32, 8, 128, 4096, 0, 9) == 0
 
 
 def test_binding_shapes():
