@@ -12,9 +12,10 @@ across steps, several copies of the pool are used in rotation, so a step never
 reads data a recent step read.
 
 Printed: one JSON line with the KV-read bandwidth (algorithmic KV bytes per
-step / wall time per step), decode tokens/s, the dominant kernel's roofline
-(HIP events around its launches), and the CPU oracle's rate on a bounded
-sample of the same workload.
+step / wall time per step, over K steps with nothing else on the stream),
+decode tokens/s, the dominant kernel's roofline (HIP events around its
+launches in a second pass of K steps), and the CPU oracle's rate on a
+bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -62,15 +63,30 @@ def measured_traffic(workload: str, partition_size: int):
 
 
 def build_workload(name: str, ps: int):
+    """(batch, steps): a static DecodeBatch and None, or, for the
+    continuous-batching run, a DecodeBatch describing its first step (pools
+    before any write) and the list of its ten steps."""
     import workloads as W
-    if name == "llama3_8b_decode":
-        return W.llama3_8b_decode(partition_size=ps)
     if name == "long_context":
-        return W.long_context(partition_size=ps or 512)
+        return W.long_context(partition_size=ps if ps >= 0 else 512), None
+    ps = max(ps, 0)
+    if name == "continuous_batching":
+        sim = W.ContinuousBatching(partition_size=ps)
+        k_pool, v_pool = sim.initial_pools()
+        steps = [sim.step(i) for i in range(sim.steps)]
+        st = steps[0]
+        b = W.DecodeBatch(name=sim.name, seed=sim.seed, dtype=sim.dtype, num_q_heads=sim.Hq, num_kv_heads=sim.Hkv,
+                          head_dim=sim.D, block_size=sim.bs, num_blocks=sim.num_blocks, q=st.q, k_new=st.k_write,
+                          v_new=st.v_write, slot_mapping=st.slot_mapping, k_pool=k_pool, v_pool=v_pool,
+                          block_tables=st.block_tables, context_lens=st.context_lens, scale=sim.scale,
+                          partition_size=ps)
+        return b, steps
+    if name == "llama3_8b_decode":
+        return W.llama3_8b_decode(partition_size=ps), None
     if name == "shared_prefix":
-        return W.shared_prefix(partition_size=ps)
+        return W.shared_prefix(partition_size=ps), None
     if name == "tiny_fp32":
-        return W.tiny_fp32()
+        return W.tiny_fp32(), None
     raise SystemExit(f"unknown --config {name}")
 
 
@@ -228,7 +244,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="llama3_8b_decode")
-    ap.add_argument("--partition-size", type=int, default=0, help="0 = the library's automatic choice")
+    ap.add_argument("--partition-size", type=int, default=-1,
+                    help="0 = the library's balanced split; default: the workload's own (512 for long_context)")
     ap.add_argument("--replicas", type=int, default=0, help="pool copies in rotation (0 = enough for >= 2 GiB of KV)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
@@ -240,7 +257,7 @@ def main():
     args = ap.parse_args()
 
     if args.summarize_profile:
-        ps = args.partition_size or "balanced"
+        ps = args.partition_size if args.partition_size > 0 else "balanced"
         summarize_profile(args.summarize_profile, args.config, ps, args.profile_copy_mib,
                           os.path.join(ROOT, "profiles", f"decode_{args.config}.md"), TRAFFIC_FILE,
                           open(args.profile_commands).read() if args.profile_commands else "")
@@ -263,7 +280,7 @@ def main():
         return
 
     t_gen = time.perf_counter()
-    b = build_workload(args.config, args.partition_size)
+    b, batching_steps = build_workload(args.config, args.partition_size)
     gen_s = time.perf_counter() - t_gen
     dtype = torch.bfloat16 if b.dtype == "bf16" else torch.float32
 
@@ -272,57 +289,79 @@ def main():
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
         return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
-    kv_bytes = b.kv_bytes()
+    def ints(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    # The inputs of every distinct step, resident on the GPU: one for a
+    # static batch, ten for the continuous-batching run (cycled in order).
+    if batching_steps is None:
+        host_steps = [(b.k_new, b.v_new, b.slot_mapping, b.q, b.block_tables, b.context_lens)]
+    else:
+        host_steps = [(st.k_write, st.v_write, st.slot_mapping, st.q, st.block_tables, st.context_lens)
+                      for st in batching_steps]
+    es = 2 if b.dtype == "bf16" else 4
+    step_kv = [int(np.asarray(h[5], dtype=np.int64).sum()) * 2 * b.num_kv_heads * b.head_dim * es for h in host_steps]
+    kv_bytes = sum(step_kv) / len(step_kv)  # per step, averaged over the distinct steps
     pool_bytes = b.k_pool.nbytes + b.v_pool.nbytes
-    R = args.replicas or max(2, math.ceil(2 * 2**30 / max(1, kv_bytes)))
+    # pool copies in rotation, so that no step reads what a recent step left
+    # in the 256 MB Infinity Cache (a continuous-batching step reads > 1 GB)
+    R = args.replicas or (1 if batching_steps is not None else max(2, math.ceil(2 * 2**30 / max(1, kv_bytes))))
     k0, v0 = dev(b.k_pool), dev(b.v_pool)
     kcs = [k0] + [k0.clone() for _ in range(R - 1)]
     vcs = [v0] + [v0.clone() for _ in range(R - 1)]
-    q, k_new, v_new = dev(b.q), dev(b.k_new), dev(b.v_new)
-    slots = torch.from_numpy(b.slot_mapping).cuda()
-    bt = torch.from_numpy(b.block_tables).cuda()
-    lens = torch.from_numpy(b.context_lens).cuda()
-    out = torch.empty(q.shape, dtype=dtype, device="cuda")
-    ps = args.partition_size or (b.partition_size or 0)
-    plans = [ops.prepare_decode(q, kcs[r], vcs[r], bt, lens, b.scale, out, partition_size=ps,
-                                max_context_len=b.max_context_len) for r in range(R)]
-    ws = plans[0].workspace
-    plans = [ops.prepare_decode(q, kcs[r], vcs[r], bt, lens, b.scale, out, partition_size=ps,
-                                max_context_len=b.max_context_len, workspace=ws) for r in range(R)]
+    ps = b.partition_size if args.partition_size < 0 else args.partition_size
+    gpu_steps = []
+    for (kw, vw, sm, qh, bth, lh) in host_steps:
+        q = dev(qh)
+        gpu_steps.append(dict(k_new=dev(kw), v_new=dev(vw), slots=ints(sm), q=q, bt=ints(bth), lens=ints(lh),
+                              max_ctx=int(np.max(lh)), out=torch.empty(q.shape, dtype=dtype, device="cuda")))
+    ws_bytes = max(ops.decode_workspace_bytes(b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim, g["max_ctx"], ps,
+                                              dtype) for g in gpu_steps)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    n_in = len(gpu_steps)
+    plans = {}
+    for j, g in enumerate(gpu_steps):
+        for r in range(R):
+            plans[j, r] = ops.prepare_decode(g["q"], kcs[r], vcs[r], g["bt"], g["lens"], b.scale, g["out"],
+                                             partition_size=ps, max_context_len=g["max_ctx"], workspace=ws)
     resolved_ps = ps if ps else ("balanced" if b.dtype == "bf16" else "auto")
 
     def step(i, ev=None):
-        r = i % R
+        j, r = i % n_in, i % R
+        g = gpu_steps[j]
+        ops.reshape_and_cache(g["k_new"], g["v_new"], g["slots"], kcs[r], vcs[r])
         if ev is not None:
             ev[0].record()
-        ops.reshape_and_cache(k_new, v_new, slots, kcs[r], vcs[r])
+        ops.run_partitions(plans[j, r])
         if ev is not None:
             ev[1].record()
-        ops.run_partitions(plans[r])
-        if ev is not None:
-            ev[2].record()
-        ops.run_reduce(plans[r])
-        if ev is not None:
-            ev[3].record()
+        ops.run_reduce(plans[j, r])
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
+    # timed region 1: K whole steps, nothing but the kernels on the stream
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, events[i])
+        step(args.warmup + i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    timed_kv = sum(step_kv[(args.warmup + i) % n_in] for i in range(args.steps))
 
-    cw = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
-    dec = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
-    red = sum(e[2].elapsed_time(e[3]) for e in events) / args.steps
+    # timed region 2: the same K steps with HIP events around each decode
+    # launch (on the launch stream), for the decode kernel's own duration
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(args.warmup + args.steps + i, events[i])
+    torch.cuda.synchronize()
+    dec_times = [e[0].elapsed_time(e[1]) for e in events]
+    dec = sum(dec_times) / args.steps
+    dec_kv = sum(step_kv[(args.warmup + args.steps + i) % n_in] for i in range(args.steps))
     ms_per_step = wall / args.steps * 1e3
-    value = kv_bytes / (ms_per_step / 1e3) / 1e9
-    achieved = kv_bytes / (dec / 1e3) / 1e9
+    value = timed_kv / wall / 1e9
+    achieved = dec_kv / (sum(dec_times) / 1e3) / 1e9
     traffic = measured_traffic(b.name, resolved_ps)
 
     rec = {
@@ -342,15 +381,15 @@ def main():
                    "num_kv_heads": b.num_kv_heads, "head_dim": b.head_dim, "block_size": b.block_size,
                    "context_len_mean": round(float(b.context_lens.mean()), 1),
                    "context_len_max": b.max_context_len, "partition_size": resolved_ps,
-                   "kv_bytes_per_step": kv_bytes, "pool_bytes": pool_bytes, "pool_replicas": R},
+                   "kv_bytes_per_step": int(round(kv_bytes)), "distinct_steps": n_in, "pool_bytes": pool_bytes,
+                   "pool_replicas": R},
         "frac_of_peak": round(value / PEAK_HBM_GBS, 4),
         "tokens_per_s": round(b.num_seqs / (ms_per_step / 1e3), 1),
-        "kernels_ms": {"reshape_and_cache": round(cw, 5), "decode_partitions": round(dec, 5),
-                       "splitk_reduce": round(red, 5)},
+        "decode_kernel_ms": round(dec, 5),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "kernel": "decode_bf16_balanced_kernel" if b.dtype == "bf16" else "decode_valu_kernel",
-                     "bytes_per_launch": kv_bytes},
+                     "bytes_per_launch": int(round(kv_bytes))},
         "input_generation_s": round(gen_s, 2),
     }
     try:

@@ -95,8 +95,8 @@ pkv_status pkv_reshape_and_cache(const void* k_new, const void* v_new, const int
  * on the current HIP device (the bf16 plan depends on its compute-unit
  * count; with no usable device a 256-CU part is assumed).  Returns 0 for
  * invalid sizes, and 0 when none is needed (fp32 KV whose contexts fit in one
- * partition).  bf16 KV always needs some: the flattened block offsets of the
- * batch and the partial results of sequences split across ranges.
+ * partition).  bf16 KV always needs some: the flattened block offsets of
+ * the batch and the partial results of sequences split across ranges.
  */
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                   int32_t head_dim, int32_t max_context_len, int32_t partition_size,
@@ -129,7 +129,9 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  *                  longest piece of a context reduced before the split-K
  *                  merge (see below); 0 = let the library choose
  *   workspace      [device] >= pkv_decode_workspace_bytes(...) bytes,
- *                  256-byte aligned; may be NULL when that is 0
+ *                  256-byte aligned; may be NULL when that is 0.  Its
+ *                  contents need no initialisation; one workspace serves one
+ *                  call at a time.
  * Work split.  bf16 KV: the blocks of all sequences, taken in order, form
  * one flattened list that is cut into equal ranges, one per workgroup the
  * device holds at once (or shorter, at most partition_size tokens each), so

@@ -16,7 +16,9 @@
 // inside one range is finished in place (out = o / l); the pieces of a
 // sequence that straddles ranges leave their (max, sum, unnormalised
 // output) and a second kernel (splitk_reduce.hip) merges them with
-// log-sum-exp weights.
+// log-sum-exp weights.  (Merging in this kernel, by whichever wave brings
+// the last piece of a sequence, was measured slower: the merge becomes a
+// chain of dependent loads at the very end of the walk.)
 //
 // A workgroup holds one wave per KV head (up to 8); all its waves walk the
 // same blocks, so at any moment they read the neighbouring 4 KiB tiles of
@@ -55,6 +57,8 @@ namespace {
 constexpr int kPrefetchBlocks = PKV_PREFETCH_BLOCKS;  // KV blocks each wave keeps in flight
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
@@ -75,6 +79,8 @@ struct SlotInfo {
 };
 
 constexpr int kSegLast = 1 << 5;  // this block ends a segment (sequence or range)
+constexpr int kCoherent = 16;     // buffer cache policy: sc1 (device scope, write-through)
+constexpr int kBufferWord3 = 0x00020000;  // buffer descriptor word 3: 32-bit raw data
 
 // Reductions over the four lane groups of a head column (lanes l, l^16,
 // l^32, l^48) with the gfx950 lane-swap instructions: plain VALU work, no
@@ -222,6 +228,37 @@ __global__ __launch_bounds__(64 * kMaxWavesPerGroup) void decode_bf16_balanced_k
     if (walker == 0 && hug == 0)
         for (int i = tid; i <= B; i += nthr) p.seq_off[i] = s_off[i];
 
+    const int hu = hug * p.waves_per_group + wave;
+    if (hu >= p.head_units) return;  // no barrier follows
+    const int kvh = hu % p.num_kv_heads;
+    const int hg = hu / p.num_kv_heads;
+    const int col = lane & 15;  // head column of the MFMA tiles
+    const int g = lane >> 4;    // lane group
+    const int Hq = p.num_q_heads;
+    const int h0 = kvh * p.group + hg * kMfmaHeadsPerUnit;
+    const int nh = min(kMfmaHeadsPerUnit, p.group - hg * kMfmaHeadsPerUnit);
+
+    // Store one output row group: lane (col, g) holds dims 16c + 4g .. +3 of
+    // head h0 + col; only the group's nh heads are written.
+    auto store_out = [&](int seq, const float4_t* v, float scale) {
+        if (col >= nh) return;
+        const int64_t o = ((int64_t)seq * Hq + h0 + col) * D + 4 * g;
+        if (p.out_bf16) {
+            uint16_t* ob = reinterpret_cast<uint16_t*>(p.out) + o;
+#pragma unroll
+            for (int c = 0; c < D / 16; ++c)
+                *reinterpret_cast<uint2*>(ob + 16 * c) =
+                    make_uint2(f32_to_bf16_bits(v[c][0] * scale) | (f32_to_bf16_bits(v[c][1] * scale) << 16),
+                               f32_to_bf16_bits(v[c][2] * scale) | (f32_to_bf16_bits(v[c][3] * scale) << 16));
+        } else {
+            float* of = reinterpret_cast<float*>(p.out) + o;
+#pragma unroll
+            for (int c = 0; c < D / 16; ++c)
+                *reinterpret_cast<float4*>(of + 16 * c) =
+                    make_float4(v[c][0] * scale, v[c][1] * scale, v[c][2] * scale, v[c][3] * scale);
+        }
+    };
+
     const int T = s_off[B];
     const int NG = p.walkers;
     int CS, NR;
@@ -231,15 +268,16 @@ __global__ __launch_bounds__(64 * kMaxWavesPerGroup) void decode_bf16_balanced_k
     const int r_final = walker + NG * (n_ranges - 1);
     const int K = (n_ranges - 1) * CS + min(CS, T - r_final * CS);  // blocks this workgroup walks
 
-    const int hu = hug * p.waves_per_group + wave;
-    if (hu >= p.head_units) return;
-    const int kvh = hu % p.num_kv_heads;
-    const int hg = hu / p.num_kv_heads;
-    const int col = lane & 15;  // head column of the MFMA tiles
-    const int g = lane >> 4;    // lane group
-    const int Hq = p.num_q_heads;
-    const int h0 = kvh * p.group + hg * kMfmaHeadsPerUnit;
-    const int nh = min(kMfmaHeadsPerUnit, p.group - hg * kMfmaHeadsPerUnit);
+    // last sequence starting at or before flattened block f (it holds block f)
+    auto seq_of_block = [&](int f) {
+        int lo = 0, hi = B - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_off[mid] <= f) lo = mid;
+            else hi = mid - 1;
+        }
+        return lo;
+    };
     // columns past the group repeat the group's last head: finite values,
     // never stored, and the softmax never mixes head columns
     const int qcol = min(col, nh - 1);
@@ -262,12 +300,7 @@ __global__ __launch_bounds__(64 * kMaxWavesPerGroup) void decode_bf16_balanced_k
             const int rs = r * CS;
             const int re = min(rs + CS, T);
             const int f = rs + (k - ri * CS);
-            int lo = 0, hi = B - 1;  // last sequence starting at or before f (it holds block f)
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (s_off[mid] <= f) lo = mid;
-                else hi = mid - 1;
-            }
+            const int lo = seq_of_block(f);
             const int o0 = s_off[lo];
             const int o1 = s_off[lo + 1];
             const int j = f - o0;
@@ -316,16 +349,20 @@ __global__ __launch_bounds__(64 * kMaxWavesPerGroup) void decode_bf16_balanced_k
         const int pb = ok ? raw : 0;
         info[d] = pend[d].info;
         if (!ok) info[d].meta &= kSegLast;
-        const uint4* kt = reinterpret_cast<const uint4*>(k_head + (int64_t)pb * block_stride);
-        const uint2* vt = reinterpret_cast<const uint2*>(v_head + (int64_t)pb * block_stride);
+        const u32x4_t* kt = reinterpret_cast<const u32x4_t*>(k_head + (int64_t)pb * block_stride);
+        const u32x2_t* vt = reinterpret_cast<const u32x2_t*>(v_head + (int64_t)pb * block_stride);
         const uint4* qr = reinterpret_cast<const uint4*>(q_base + (int64_t)info[d].seq * Hq * D);
+        // KV tiles are read once: non-temporal loads keep them from
+        // displacing reusable lines (q, tables, shared-prefix blocks) and
+        // measurably raise the streaming rate.
 #pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk) ring[d].k[kk] = kt[kk * 64 + lane];
+        for (int kk = 0; kk < D / 32; ++kk)
+            ring[d].k[kk] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(kt + kk * 64 + lane));
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk) ring[d].q[kk] = __builtin_bit_cast(bf16x8_t, qr[4 * kk + g]);
         const int vo = (lane & 15) * 4 + (lane >> 4);
 #pragma unroll
-        for (int c = 0; c < D / 16; ++c) ring[d].v[c] = vt[c * 64 + vo];
+        for (int c = 0; c < D / 16; ++c) ring[d].v[c] = __builtin_bit_cast(uint2, __builtin_nontemporal_load(vt + c * 64 + vo));
         fetch(k_next, pend[d]);
     };
 
@@ -334,37 +371,30 @@ __global__ __launch_bounds__(64 * kMaxWavesPerGroup) void decode_bf16_balanced_k
     for (int c = 0; c < D / 16; ++c) acc[c] = {0.f, 0.f, 0.f, 0.f};
     SoftmaxState st{-INFINITY, 0.f};
 
+    // the partial rows, addressed as one buffer
+    const __amdgpu_buffer_rsrc_t part_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(p.o_part, (short)0, (int)p.part_bytes, kBufferWord3);
+
     // End of a segment: finish the sequence (out = o / l) or leave the
     // piece's statistics for the merge, then start afresh.
     auto finish_segment = [&](int seq, int slot) {
         const float l_tot = sum_over_groups(st.l);
         if (col < nh) {
             if (slot < 0) {
-                const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-                const int64_t o = ((int64_t)seq * Hq + h0 + col) * D + 4 * g;
-                if (p.out_bf16) {
-                    uint16_t* ob = reinterpret_cast<uint16_t*>(p.out) + o;
-#pragma unroll
-                    for (int c = 0; c < D / 16; ++c)
-                        *reinterpret_cast<uint2*>(ob + 16 * c) =
-                            make_uint2(f32_to_bf16_bits(acc[c][0] * inv) | (f32_to_bf16_bits(acc[c][1] * inv) << 16),
-                                       f32_to_bf16_bits(acc[c][2] * inv) | (f32_to_bf16_bits(acc[c][3] * inv) << 16));
-                } else {
-                    float* of = reinterpret_cast<float*>(p.out) + o;
-#pragma unroll
-                    for (int c = 0; c < D / 16; ++c)
-                        *reinterpret_cast<float4*>(of + 16 * c) =
-                            make_float4(acc[c][0] * inv, acc[c][1] * inv, acc[c][2] * inv, acc[c][3] * inv);
-                }
+                store_out(seq, acc, l_tot > 0.f ? 1.f / l_tot : 0.f);
             } else {
+                // write-through stores (sc1): the rows are read once, by the
+                // reduce kernel, so they need not sit dirty in this XCD's L2
+                // (measured faster than plain stores when pieces are many)
                 const int64_t row = (int64_t)slot * Hq + h0 + col;
-                float* of = p.o_part + row * D + 4 * g;
+                const int ob = (int)((row * D + 4 * g) * sizeof(float));
 #pragma unroll
                 for (int c = 0; c < D / 16; ++c)
-                    *reinterpret_cast<float4*>(of + 16 * c) = make_float4(acc[c][0], acc[c][1], acc[c][2], acc[c][3]);
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, acc[c]), part_rsrc,
+                                                           ob + 64 * c, 0, kCoherent);
                 if (g == 0) {
-                    p.m_part[row] = st.m;
-                    p.l_part[row] = l_tot;
+                    __hip_atomic_store(p.m_part + row, st.m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(p.l_part + row, l_tot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
             }
         }
@@ -397,6 +427,7 @@ __global__ __launch_bounds__(64 * kMaxWavesPerGroup) void decode_bf16_balanced_k
             __builtin_amdgcn_sched_barrier(0);
         }
     }
+
 }
 
 }  // namespace

@@ -15,6 +15,7 @@ constexpr int kMaxWavesPerGroup = 8;     // KV-head waves in one balanced-decode
 constexpr int kMaxSeqsPerLaunch = 4096;  // sequences one balanced-decode launch takes (LDS tables)
 constexpr int kMinRangeBlocks = 4;       // shortest range of blocks one workgroup walks
 
+
 // Everything one decode launch needs.  Passed by value as the kernel argument.
 struct DecodeParams {
     const void* q;               // [B][Hq][D]
@@ -39,17 +40,18 @@ struct DecodeParams {
     int32_t ctx_cap;             // context lengths are clamped to [0, ctx_cap]
     int32_t out_bf16;            // 1: bf16 output, 0: f32 output
     // partitioned path (fp32 KV): fixed partitions of part_blocks blocks,
-    // partials laid out [B][P][Hq](×D)
+    // partials laid out [B][P][Hq](×D), merged by the reduce kernel
     int32_t part_blocks;
     int32_t num_parts;
     // balanced path (bf16 KV): `walkers` workgroup columns split the
     // flattened block list of all sequences into ranges; partials laid out
-    // [2 * ranges][Hq](×D)
+    // [2 * ranges][Hq](×D), merged by the reduce kernel
     int32_t walkers;             // workgroups per head-unit group
     int32_t range_cap;           // longest range in blocks (0 = no cap)
     int32_t waves_per_group;     // KV-head waves per workgroup
     int32_t head_units;          // Hkv * n_head_groups
     int32_t head_unit_groups;    // ceil(head_units / waves_per_group)
+    int64_t part_bytes;          // bytes of the o_part region (buffer-resource extent)
 };
 
 // Split of T flattened blocks into ranges for `walkers` workgroups: each

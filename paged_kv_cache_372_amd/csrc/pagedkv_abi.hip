@@ -115,6 +115,7 @@ pkv_status make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads
     pl->chunk_seqs = num_seqs < pkv::kMaxSeqsPerLaunch ? num_seqs : pkv::kMaxSeqsPerLaunch;
     pl->num_chunks = num_seqs > 0 ? (int32_t)ceil_div(num_seqs, pl->chunk_seqs) : 0;
     pl->head_units = num_kv_heads * pl->n_head_groups;
+
     pl->waves_per_group = pl->head_units < pkv::kMaxWavesPerGroup ? pl->head_units : pkv::kMaxWavesPerGroup;
     pl->head_unit_groups = (int32_t)ceil_div(pl->head_units, pl->waves_per_group);
     const int64_t slots = resident_groups(head_dim, pl->waves_per_group, pl->chunk_seqs > 0 ? pl->chunk_seqs : 1);
@@ -128,6 +129,9 @@ pkv_status make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads
     int64_t nr = pl->walkers;
     if (pl->range_cap > 0 && ceil_div(t_max, pl->range_cap) > nr) nr = ceil_div(t_max, pl->range_cap);
     pl->max_ranges = nr;
+    if ((int64_t)(2 * nr) * num_q_heads * head_dim * (int64_t)sizeof(float) >= ((int64_t)1 << 31))
+        return fail(PKV_ERR_UNSUPPORTED, "partial results of %lld ranges x %d heads exceed 2 GiB", (long long)nr,
+                    num_q_heads);
     pl->off_bytes = align_up((size_t)(pl->chunk_seqs + 1) * sizeof(int32_t), 256);
     pl->chunk_bytes =
         align_up(pl->off_bytes + (size_t)(2 * nr) * num_q_heads * (head_dim + 2) * sizeof(float), 256);
@@ -193,6 +197,7 @@ pkv_status prepare(const void* q, const void* k_cache, const void* v_cache, cons
         p.waves_per_group = pl.waves_per_group;
         p.head_units = pl.head_units;
         p.head_unit_groups = pl.head_unit_groups;
+        p.part_bytes = (int64_t)(2 * pl.max_ranges) * num_q_heads * head_dim * (int64_t)sizeof(float);
     } else {
         p.part_blocks = pl.part_tokens / block_size;
         p.num_parts = pl.num_parts;
@@ -243,8 +248,7 @@ pkv_status run_decode_kernels(const Call& c, hipStream_t stream) {
 
 pkv_status run_reduce_kernels(const Call& c, hipStream_t stream) {
     if (c.base.num_seqs == 0) return PKV_OK;
-    if (!c.plan.balanced)
-        return from_hip(pkv::launch_splitk_reduce(c.base, false, stream), "split-K reduce launch");
+    if (!c.plan.balanced) return from_hip(pkv::launch_splitk_reduce(c.base, false, stream), "split-K reduce launch");
     for (int32_t i = 0; i < c.plan.num_chunks; ++i) {
         pkv_status st = from_hip(pkv::launch_splitk_reduce(chunk_params(c, i), true, stream), "split-K reduce launch");
         if (st != PKV_OK) return st;

@@ -185,8 +185,8 @@ def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
     """Decode attention of ``q [B, Hq, D]`` over the paged cache into ``out``.
 
     ``max_context_len`` (host-known bound of ``context_lens``) avoids a
-    device-to-host sync; ``workspace`` (uint8, >= ``decode_workspace_bytes``)
-    avoids an allocation when the context is split.
+    device-to-host sync; ``workspace`` (uint8, >= ``decode_workspace_bytes``,
+    reusable) avoids an allocation.
     """
     a = _DecodeArgs(q, k_cache, v_cache, block_tables, context_lens, scale, out, partition_size, max_context_len,
                     workspace)

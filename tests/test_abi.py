@@ -126,7 +126,7 @@ def balanced_workspace(B, hq, hkv, D, ctx, ps, walkers_per_head_group):
     if ps:
         nr = max(nr, -(-(chunk * -(-ctx // 16)) // (ps // 16)))
     per = _align(_align((chunk + 1) * 4) + 2 * nr * hq * (D + 2) * 4)
-    return per * chunks
+    return per * chunks   # one region per launch
 
 
 def test_workspace_sizes(lib):

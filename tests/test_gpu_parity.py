@@ -298,3 +298,38 @@ def test_workspace_too_small_raises():
     with pytest.raises(RuntimeError, match="workspace"):
         ops.paged_attention_decode(db.q, db.k_cache, db.v_cache, db.bt, db.lens, b.scale, db.out, partition_size=256,
                                    max_context_len=b.max_context_len, workspace=ws)
+
+
+def test_workspace_reused_across_call_sizes():
+    """One workspace, never cleared, serves calls of different sizes in a row."""
+    a = W.llama3_8b_decode(num_seqs=6)                       # many ranges per sequence with the cap below
+    b = W.long_context(num_seqs=2, context_len=3000, partition_size=0)
+    need = max(ops.decode_workspace_bytes(x.num_seqs, x.num_q_heads, x.num_kv_heads, x.head_dim, x.max_context_len, ps)
+               for x, ps in ((a, 48), (b, 0)))
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")   # garbage: NaN patterns
+    first = None
+    for x, ps in ((a, 48), (b, 0), (a, 48)):
+        say(f"[{x.name} B={x.num_seqs} ps={ps}] shared workspace")
+        db = DeviceBatch(x)
+        db.write()
+        ops.paged_attention_decode(db.q, db.k_cache, db.v_cache, db.bt, db.lens, x.scale, db.out, partition_size=ps,
+                                   max_context_len=x.max_context_len, workspace=ws)
+        torch.cuda.synchronize()
+        kp, vp = oracle_pools(x)
+        ref = oracle.ref_paged_attention_decode(x.q, kp, vp, x.block_tables, x.context_lens, x.scale, x.dtype)
+        compare(out_f64(db.out), ref, x.dtype, f"{x.name} shared workspace")
+        if x is a:
+            if first is None:
+                first = db.out.clone()
+            else:
+                assert torch.equal(first.view(torch.int16), db.out.view(torch.int16))
+
+
+def test_more_than_4096_sequences():
+    """A batch above one launch's 4096 sequences runs as consecutive launches."""
+    rng = np.random.default_rng(4501)
+    lengths = rng.integers(1, 41, size=4500)
+    b = W.build_static("many", 45, "bf16", 8, 2, 64, lengths, W.pool_blocks_for(lengths, 16))
+    seqs = sorted(set([0, 1, 4095, 4096, 4097, 4499] + rng.choice(4500, 40, replace=False).tolist()))
+    run_and_check(b, seqs=seqs, what="4500 sequences, sampled")
+    run_and_check(b, partition_size=16, seqs=seqs, what="4500 sequences, one-block ranges")
