@@ -3,50 +3,94 @@
 // Caching the key/value of every processed token is what lets decode skip
 // recomputing them (runbyai sections 1-2); with paging, the slot names a
 // physical block and an offset inside it (runbyai section 3).  The copy is
-// bit for bit: the kernel moves 16-byte words (K) and raw elements (V) and
-// never converts a value.
+// bit for bit: the kernel moves 16-byte words (K) and raw 16-bit or 32-bit
+// elements (V) and never converts a value.
 //
-// One wave64 per (token, KV head); four waves per workgroup.
-//   K: the D values of the token are D/x 16-byte chunks; chunk c goes to
-//      tile + (c * 16 + offset) * x  (one lane per chunk).
-//   V: dim d goes to tile + d * 16 + offset (one element per lane and pass).
+// One workgroup (256 threads) per (group of 16 consecutive tokens, KV head).
+// Tokens are independent -- any slot mapping works -- but the lanes are laid
+// out so that when consecutive tokens fill consecutive slots of a block (a
+// prompt being written) the stores of a wave land in contiguous runs:
+//   K: tile [D/x][16][x]; thread (c, t) copies 16-byte chunk c of token t to
+//      tile(t) + (c * 16 + offset(t)) * 16 B -- 16 consecutive offsets form
+//      one contiguous run of 16 * 16 B.
+//   V: tile [D][16]; the 16 rows go through LDS and thread (t, d) writes
+//      element d of token t to tile(t) + d * 16 + offset(t), lanes running
+//      over t first -- consecutive offsets of one dim are contiguous.
+// A single appended token per sequence (the decode step) gets scattered
+// writes whatever the layout; there the launch, not the stores, dominates.
 #include "kernels.h"
 
 namespace pkv {
 namespace {
 
-template <typename E, int D>
-__global__ __launch_bounds__(256) void cache_write_kernel(const E* __restrict__ k_new, const E* __restrict__ v_new,
-                                                          const int64_t* __restrict__ slot_mapping,
-                                                          E* __restrict__ k_cache, E* __restrict__ v_cache,
-                                                          int64_t num_tokens, int num_kv_heads, int64_t num_slots) {
-    constexpr int X = 16 / (int)sizeof(E);
-    constexpr int NCH = D / X;
-    const int lane = threadIdx.x & 63;
-    const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (w >= num_tokens * num_kv_heads) return;
-    const int64_t t = w / num_kv_heads;
-    const int h = (int)(w % num_kv_heads);
-    const int64_t slot = slot_mapping[t];
-    if (slot < 0 || slot >= num_slots) return;
-    const int64_t blk = slot / kBlockSize;
-    const int off = (int)(slot % kBlockSize);
-    const int64_t tile = (blk * num_kv_heads + h) * (int64_t)(D * kBlockSize);
-    const int64_t row = (t * num_kv_heads + h) * (int64_t)D;
+constexpr int kTokens = 16;   // tokens per workgroup
+constexpr int kThreads = 256;
 
-    if (lane < NCH) {
-        const uint4 c = reinterpret_cast<const uint4*>(k_new + row)[lane];
-        reinterpret_cast<uint4*>(k_cache + tile)[lane * kBlockSize + off] = c;
+template <typename E, int D>
+__global__ __launch_bounds__(kThreads) void cache_write_kernel(const E* __restrict__ k_new, const E* __restrict__ v_new,
+                                                               const int64_t* __restrict__ slot_mapping,
+                                                               E* __restrict__ k_cache, E* __restrict__ v_cache,
+                                                               int64_t num_tokens, int num_kv_heads, int64_t num_slots) {
+    constexpr int X = 16 / (int)sizeof(E);  // elements per 16-byte chunk
+    constexpr int NCH = D / X;              // chunks per row
+    constexpr int kRowPad = 16 / (int)sizeof(E);
+    __shared__ __align__(16) E vrow[kTokens][D + kRowPad];
+    __shared__ int64_t tile_of[kTokens];    // element offset of the token's (block, head) tile, -1 = skip
+    __shared__ int off_of[kTokens];
+
+    const int h = blockIdx.x % num_kv_heads;
+    const int64_t t0 = (int64_t)(blockIdx.x / num_kv_heads) * kTokens;
+    const int tid = threadIdx.x;
+
+    if (tid < kTokens) {
+        const int64_t t = t0 + tid;
+        int64_t tile = -1;
+        int off = 0;
+        if (t < num_tokens) {
+            const int64_t slot = slot_mapping[t];
+            if (slot >= 0 && slot < num_slots) {
+                tile = (slot / kBlockSize * num_kv_heads + h) * (int64_t)(D * kBlockSize);
+                off = (int)(slot % kBlockSize);
+            }
+        }
+        tile_of[tid] = tile;
+        off_of[tid] = off;
     }
-#pragma unroll
-    for (int d = lane; d < D; d += 64) v_cache[tile + (int64_t)d * kBlockSize + off] = v_new[row + d];
+    // V rows into LDS: thread (t, c) reads 16-byte chunk c of token t
+    for (int i = tid; i < kTokens * NCH; i += kThreads) {
+        const int t = i / NCH;
+        const int c = i % NCH;
+        if (t0 + t < num_tokens) {
+            const uint4 w = reinterpret_cast<const uint4*>(v_new + ((t0 + t) * num_kv_heads + h) * (int64_t)D)[c];
+            *reinterpret_cast<uint4*>(&vrow[t][c * X]) = w;
+        }
+    }
+    __syncthreads();
+
+    // K: thread (c, t), t fastest
+    for (int i = tid; i < kTokens * NCH; i += kThreads) {
+        const int t = i % kTokens;
+        const int c = i / kTokens;
+        const int64_t tile = tile_of[t];
+        if (tile < 0) continue;
+        const uint4 w = reinterpret_cast<const uint4*>(k_new + ((t0 + t) * num_kv_heads + h) * (int64_t)D)[c];
+        reinterpret_cast<uint4*>(k_cache + tile)[c * kBlockSize + off_of[t]] = w;
+    }
+    // V: thread (d, t), t fastest
+    for (int i = tid; i < kTokens * D; i += kThreads) {
+        const int t = i % kTokens;
+        const int d = i / kTokens;
+        const int64_t tile = tile_of[t];
+        if (tile < 0) continue;
+        v_cache[tile + (int64_t)d * kBlockSize + off_of[t]] = vrow[t][d];
+    }
 }
 
 template <typename E>
 hipError_t launch_typed(const void* k_new, const void* v_new, const int64_t* slots, void* k_cache, void* v_cache,
                         int64_t num_tokens, int num_kv_heads, int head_dim, int64_t num_blocks, hipStream_t stream) {
-    const int64_t waves = num_tokens * num_kv_heads;
-    const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+    const int64_t groups = (num_tokens + kTokens - 1) / kTokens * num_kv_heads;
+    const dim3 grid((unsigned)groups), block(kThreads);
     const int64_t num_slots = num_blocks * kBlockSize;
     const E* kn = static_cast<const E*>(k_new);
     const E* vn = static_cast<const E*>(v_new);
