@@ -46,6 +46,8 @@
 // Results depend only on logical token positions and the range split (a
 // function of the context lengths and the launch width), never on where
 // blocks sit in the pool.
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace pkv {
@@ -339,16 +341,22 @@ __global__ __launch_bounds__(64 * kMaxWavesPerGroup) void decode_bf16_balanced_k
     SlotInfo info[kDepth];
     Pending pend[kDepth];
 
-    // Fill ring slot d from its pending entry, then fetch the entry of walk
-    // position k_next, the one this slot takes after that.  Every refill
-    // issues the same vector loads, so the wait before a block covers only
-    // that block's loads.
-    auto load_slot = [&](int d, int k_next) {
-        const int raw = pend[d].raw;
-        const bool ok = raw >= 0 && (int64_t)raw < p.num_blocks;
-        const int pb = ok ? raw : 0;
-        info[d] = pend[d].info;
-        if (!ok) info[d].meta &= kSegLast;
+    // A fetched table entry, checked: the physical block to load (an id
+    // outside the pool loads block 0 with no valid token).  The empty asm
+    // pins the check here, so the wait for the scalar load happens now and
+    // not where the block is loaded.
+    auto accept = [&](const Pending& e, int& pb, SlotInfo& inf) {
+        const bool ok = e.raw >= 0 && (int64_t)e.raw < p.num_blocks;
+        pb = ok ? e.raw : 0;
+        inf = e.info;
+        if (!ok) inf.meta &= kSegLast;
+        asm volatile("" : "+s"(pb));
+    };
+
+    // Fill ring slot d with physical block pb.  Every refill issues the same
+    // vector loads, so the wait before a block covers only that block's loads.
+    auto load_slot = [&](int d, int pb, const SlotInfo& inf) {
+        info[d] = inf;
         const u32x4_t* kt = reinterpret_cast<const u32x4_t*>(k_head + (int64_t)pb * block_stride);
         const u32x2_t* vt = reinterpret_cast<const u32x2_t*>(v_head + (int64_t)pb * block_stride);
         const uint4* qr = reinterpret_cast<const uint4*>(q_base + (int64_t)info[d].seq * Hq * D);
@@ -363,7 +371,6 @@ __global__ __launch_bounds__(64 * kMaxWavesPerGroup) void decode_bf16_balanced_k
         const int vo = (lane & 15) * 4 + (lane >> 4);
 #pragma unroll
         for (int c = 0; c < D / 16; ++c) ring[d].v[c] = __builtin_bit_cast(uint2, __builtin_nontemporal_load(vt + c * 64 + vo));
-        fetch(k_next, pend[d]);
     };
 
     float4_t acc[D / 16];
@@ -404,29 +411,54 @@ __global__ __launch_bounds__(64 * kMaxWavesPerGroup) void decode_bf16_balanced_k
         st.l = 0.f;
     };
 
-    // The scheduling barriers keep each refill's loads together and in slot
-    // order, in the prologue as in the loop, so the count of loads issued
-    // after a slot's loads is the same on every path into the loop and the
-    // compiler waits for exactly that slot.
+    // Table entries travel through the scalar cache, whose loads complete
+    // out of order: any wait for one waits for all in flight.  So the
+    // entries are fetched in one burst at the top of an iteration and used
+    // at the top of the next, with no scalar load issued in between --
+    // the wait then finds them long arrived.  The scheduling barriers keep
+    // each refill's vector loads together and in slot order, in the prologue
+    // as in the loop, so the count of loads issued after a slot's loads is
+    // the same on every path into the loop and the compiler waits for
+    // exactly that slot.
+    int next_pb[kDepth];
+    SlotInfo next_info[kDepth];
 #pragma unroll
     for (int d = 0; d < kDepth; ++d) fetch(d, pend[d]);
 #pragma unroll
+    for (int d = 0; d < kDepth; ++d) accept(pend[d], next_pb[d], next_info[d]);
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) fetch(kDepth + d, pend[d]);
+#pragma unroll
     for (int d = 0; d < kDepth; ++d) {
-        load_slot(d, d + kDepth);
+        load_slot(d, next_pb[d], next_info[d]);
         __builtin_amdgcn_sched_barrier(0);
     }
-    for (int i = 0; i < K; i += kDepth) {
+    // One round: compute the kDepth blocks in the ring, refilling each slot
+    // with the block kDepth positions further on.  In the last rounds the
+    // refills past the walk's end are skipped (kFinal); before that every
+    // refill is issued, which keeps the loop's waits exact.
+    auto round = [&](int i, auto final_tag) {
+        constexpr bool kFinal = decltype(final_tag)::value;
+        // entries of positions i + kDepth + d, fetched one round ago
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d) accept(pend[d], next_pb[d], next_info[d]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d) fetch(i + 2 * kDepth + d, pend[d]);
 #pragma unroll
         for (int d = 0; d < kDepth; ++d) {
-            if (i + d < K) {
+            if (!kFinal || i + d < K) {
                 compute_block<D>(ring[d], acc, st, info[d].meta & 31, p.scale_log2, g);
                 if (info[d].meta & kSegLast) finish_segment(info[d].seq, info[d].slot);
             }
             __builtin_amdgcn_sched_barrier(0);
-            load_slot(d, i + d + 2 * kDepth);
+            if (!kFinal || i + d + kDepth < K) load_slot(d, next_pb[d], next_info[d]);
             __builtin_amdgcn_sched_barrier(0);
         }
-    }
+    };
+    int i = 0;
+    for (; i + 2 * kDepth <= K; i += kDepth) round(i, std::false_type{});
+    for (; i < K; i += kDepth) round(i, std::true_type{});
 
 }
 
