@@ -230,6 +230,12 @@ def summarize_profile(prefix: str, workload: str, partition_size, copy_mib: int,
         name = _short_kernel_name(k)
         lines.append(f"| `{name}` | {fetch[k]:.0f} | {write.get(k, 0):.0f} | {fetch[k] * 1024 * f_factor / 1e6:.1f} | "
                      f"{write.get(k, 0) * 1024 * w_factor / 1e6:.2f} |")
+    bench_log = prefix + "_bench.log"
+    if os.path.exists(bench_log):
+        last = [ln for ln in open(bench_log).read().splitlines() if ln.startswith("{")]
+        if last:
+            lines += ["", f"## Bench line of the same build (`python bench.py --config {workload}`)", "", "```",
+                      last[-1], "```"]
     rec = {"source_sha256": kernel_source_hash(), "workload": workload, "partition_size": partition_size,
            "kernel": dec, "fetch_kib_per_dispatch": fetch[dec], "write_kib_per_dispatch": write.get(dec, 0.0),
            "fetch_copy_factor": f_factor, "write_copy_factor": w_factor}
@@ -271,6 +277,7 @@ def main():
     import numpy as np
     import torch
     from paged_kv_cache_372_amd import ops
+    from paged_kv_cache_372_amd.blocks import tables_share_blocks
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -315,7 +322,8 @@ def main():
     for (kw, vw, sm, qh, bth, lh) in host_steps:
         q = dev(qh)
         gpu_steps.append(dict(k_new=dev(kw), v_new=dev(vw), slots=ints(sm), q=q, bt=ints(bth), lens=ints(lh),
-                              max_ctx=int(np.max(lh)), out=torch.empty(q.shape, dtype=dtype, device="cuda")))
+                              max_ctx=int(np.max(lh)), out=torch.empty(q.shape, dtype=dtype, device="cuda"),
+                              shared=tables_share_blocks(bth, lh, b.block_size)))
     ws_bytes = max(ops.decode_workspace_bytes(b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim, g["max_ctx"], ps,
                                               dtype) for g in gpu_steps)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
@@ -324,7 +332,8 @@ def main():
     for j, g in enumerate(gpu_steps):
         for r in range(R):
             plans[j, r] = ops.prepare_decode(g["q"], kcs[r], vcs[r], g["bt"], g["lens"], b.scale, g["out"],
-                                             partition_size=ps, max_context_len=g["max_ctx"], workspace=ws)
+                                             partition_size=ps, max_context_len=g["max_ctx"], workspace=ws,
+                                             shared_blocks=g["shared"])
     resolved_ps = ps if ps else ("balanced" if b.dtype == "bf16" else "auto")
 
     def step(i, ev=None):
@@ -383,7 +392,7 @@ def main():
                    "context_len_mean": round(float(b.context_lens.mean()), 1),
                    "context_len_max": b.max_context_len, "partition_size": resolved_ps,
                    "kv_bytes_per_step": int(round(kv_bytes)), "distinct_steps": n_in, "pool_bytes": pool_bytes,
-                   "pool_replicas": R},
+                   "pool_replicas": R, "shared_blocks": any(g["shared"] for g in gpu_steps)},
         "frac_of_peak": round(value / PEAK_HBM_GBS, 4),
         "tokens_per_s": round(b.num_seqs / (ms_per_step / 1e3), 1),
         "decode_kernel_ms": round(dec, 5),

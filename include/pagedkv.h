@@ -67,6 +67,17 @@ typedef enum pkv_dtype {
     PKV_BF16 = 1
 } pkv_dtype;
 
+/* Decode flags (a performance choice only: results are bit-identical with
+ * and without).
+ * PKV_DECODE_SHARED_BLOCKS: several sequences of the batch point at the same
+ *   physical blocks (a common prompt prefix, forked samples: runbyai
+ *   section 3 "Shared prefix"; ai-hpc 2.2 "Flexible Sharing").  With bf16 KV
+ *   the decode then reads K and V with ordinary loads, which keep a shared
+ *   block in the caches for its next reader.  Without it, K and V are read
+ *   with streaming (non-temporal) loads, the faster choice when every block
+ *   is read once.  fp32 KV ignores the flag. */
+#define PKV_DECODE_SHARED_BLOCKS 1u
+
 /* Version of this ABI (bumped on any incompatible change). */
 int32_t pkv_abi_version(void);
 
@@ -132,6 +143,8 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  *                  256-byte aligned; may be NULL when that is 0.  Its
  *                  contents need no initialisation; one workspace serves one
  *                  call at a time.
+ *   flags          0 or PKV_DECODE_SHARED_BLOCKS; other bits are rejected
+ *                  (PKV_ERR_INVALID_ARG)
  * Work split.  bf16 KV: the blocks of all sequences, taken in order, form
  * one flattened list that is cut into equal ranges, one per workgroup the
  * device holds at once (or shorter, at most partition_size tokens each), so
@@ -152,11 +165,12 @@ pkv_status pkv_paged_attention_decode(const void* q, const void* k_cache, const 
                                       int32_t head_dim, int32_t block_size, int64_t num_blocks,
                                       int32_t max_blocks_per_seq, int32_t max_context_len,
                                       int32_t partition_size, void* workspace, size_t workspace_bytes,
-                                      pkv_dtype kv_dtype, pkv_dtype out_dtype, void* stream);
+                                      pkv_dtype kv_dtype, pkv_dtype out_dtype, uint32_t flags, void* stream);
 
 /*
  * The two launches of pkv_paged_attention_decode, callable one at a time
- * (same arguments and meaning; the reduce takes the subset it reads).
+ * (same arguments and meaning; the reduce takes the subset it reads and
+ * no flags).
  * _partitions runs the block-table walk and writes `out` for the sequences
  * it finishes and fp32 partials for the others; _reduce merges those
  * partials into `out` (and, with bf16 KV, writes the zeros of empty
@@ -171,7 +185,7 @@ pkv_status pkv_paged_attention_decode_partitions(const void* q, const void* k_ca
                                                  int64_t num_blocks, int32_t max_blocks_per_seq,
                                                  int32_t max_context_len, int32_t partition_size, void* workspace,
                                                  size_t workspace_bytes, pkv_dtype kv_dtype, pkv_dtype out_dtype,
-                                                 void* stream);
+                                                 uint32_t flags, void* stream);
 
 pkv_status pkv_paged_attention_decode_reduce(const int32_t* context_lens, void* out, int32_t num_seqs,
                                              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,

@@ -18,6 +18,9 @@ This module owns that bookkeeping:
                        next token starts a new one (on-demand allocation).
 * ``pack_block_tables`` / ``pack_context_lens`` -- pack the per-sequence
                        state into the int32 arrays the C-ABI consumes.
+* ``tables_share_blocks`` -- whether a packed batch points several sequences
+                       at one block, which selects the decode's cached-read
+                       variant (the ``shared_blocks`` option).
 
 A flat slot index is ``physical_block * block_size + offset_in_block``.
 """
@@ -149,6 +152,15 @@ def pack_block_tables(seqs: Seq[Sequence], width: int, pad_block: int) -> np.nda
             raise ValueError(f"sequence {s.seq_id} needs {len(s.blocks)} blocks > table width {width}")
         bt[i, :len(s.blocks)] = s.blocks
     return bt
+
+
+def tables_share_blocks(block_tables: np.ndarray, context_lens: np.ndarray, block_size: int) -> bool:
+    """True when some physical block appears in the used part of two tables
+    (or twice in one), i.e. the decode will read it more than once."""
+    bt = np.asarray(block_tables)
+    used = [bt[i, :blocks_needed(max(int(L), 0), block_size)] for i, L in enumerate(np.asarray(context_lens))]
+    ids = np.concatenate(used) if used else np.zeros(0, dtype=np.int32)
+    return bool(np.unique(ids).size != ids.size)
 
 
 def pack_context_lens(seqs: Seq[Sequence]) -> np.ndarray:

@@ -185,7 +185,7 @@ struct Pending {
 
 typedef const int32_t __attribute__((address_space(4)))* scalar_i32_ptr;
 
-template <int D, int kDepth>
+template <int D, int kDepth, bool kCached>
 __global__ __launch_bounds__(64 * kMaxWavesPerGroup) void decode_bf16_balanced_kernel(DecodeParams p) {
     extern __shared__ int32_t tables[];
     __shared__ int32_t wave_total[kMaxWavesPerGroup];
@@ -360,17 +360,21 @@ __global__ __launch_bounds__(64 * kMaxWavesPerGroup) void decode_bf16_balanced_k
         const u32x4_t* kt = reinterpret_cast<const u32x4_t*>(k_head + (int64_t)pb * block_stride);
         const u32x2_t* vt = reinterpret_cast<const u32x2_t*>(v_head + (int64_t)pb * block_stride);
         const uint4* qr = reinterpret_cast<const uint4*>(q_base + (int64_t)info[d].seq * Hq * D);
-        // KV tiles are read once: non-temporal loads keep them from
-        // displacing reusable lines (q, tables, shared-prefix blocks) and
-        // measurably raise the streaming rate.
+        // Streaming (the default): each KV tile is read once, so non-temporal
+        // loads keep it from displacing reusable lines (q, tables) and
+        // measurably raise the rate.  kCached: sequences share blocks, so
+        // ordinary loads leave them in the caches for the next reader.
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk)
-            ring[d].k[kk] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(kt + kk * 64 + lane));
+            ring[d].k[kk] = __builtin_bit_cast(uint4, kCached ? kt[kk * 64 + lane]
+                                                              : __builtin_nontemporal_load(kt + kk * 64 + lane));
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk) ring[d].q[kk] = __builtin_bit_cast(bf16x8_t, qr[4 * kk + g]);
         const int vo = (lane & 15) * 4 + (lane >> 4);
 #pragma unroll
-        for (int c = 0; c < D / 16; ++c) ring[d].v[c] = __builtin_bit_cast(uint2, __builtin_nontemporal_load(vt + c * 64 + vo));
+        for (int c = 0; c < D / 16; ++c)
+            ring[d].v[c] = __builtin_bit_cast(uint2, kCached ? vt[c * 64 + vo]
+                                                             : __builtin_nontemporal_load(vt + c * 64 + vo));
     };
 
     float4_t acc[D / 16];
@@ -467,18 +471,26 @@ __global__ __launch_bounds__(64 * kMaxWavesPerGroup) void decode_bf16_balanced_k
 size_t balanced_lds_bytes(int32_t num_seqs) { return (size_t)(2 * num_seqs + 1) * sizeof(int32_t); }
 
 const void* balanced_kernel(int32_t head_dim) {
-    return head_dim == 128 ? reinterpret_cast<const void*>(&decode_bf16_balanced_kernel<128, kPrefetchBlocks>)
-                           : reinterpret_cast<const void*>(&decode_bf16_balanced_kernel<64, kPrefetchBlocks>);
+    // the plan sizes the grid from the streaming variant's occupancy; the
+    // cached variant needs no more registers or LDS
+    return head_dim == 128 ? reinterpret_cast<const void*>(&decode_bf16_balanced_kernel<128, kPrefetchBlocks, false>)
+                           : reinterpret_cast<const void*>(&decode_bf16_balanced_kernel<64, kPrefetchBlocks, false>);
+}
+
+template <int D>
+void launch_balanced(const DecodeParams& p, dim3 grid, dim3 block, size_t lds, hipStream_t stream) {
+    if (p.cached_kv)
+        hipLaunchKernelGGL((decode_bf16_balanced_kernel<D, kPrefetchBlocks, true>), grid, block, lds, stream, p);
+    else
+        hipLaunchKernelGGL((decode_bf16_balanced_kernel<D, kPrefetchBlocks, false>), grid, block, lds, stream, p);
 }
 
 hipError_t launch_decode_bf16_balanced(const DecodeParams& p, hipStream_t stream) {
     if (p.num_seqs == 0) return hipSuccess;
     const dim3 grid((unsigned)((int64_t)p.walkers * p.head_unit_groups)), block(64 * p.waves_per_group);
     const size_t lds = balanced_lds_bytes(p.num_seqs);
-    if (p.head_dim == 128)
-        hipLaunchKernelGGL((decode_bf16_balanced_kernel<128, kPrefetchBlocks>), grid, block, lds, stream, p);
-    else
-        hipLaunchKernelGGL((decode_bf16_balanced_kernel<64, kPrefetchBlocks>), grid, block, lds, stream, p);
+    if (p.head_dim == 128) launch_balanced<128>(p, grid, block, lds, stream);
+    else launch_balanced<64>(p, grid, block, lds, stream);
     return hipGetLastError();
 }
 

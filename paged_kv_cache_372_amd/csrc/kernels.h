@@ -39,6 +39,7 @@ struct DecodeParams {
     int32_t max_blocks_per_seq;
     int32_t ctx_cap;             // context lengths are clamped to [0, ctx_cap]
     int32_t out_bf16;            // 1: bf16 output, 0: f32 output
+    int32_t cached_kv;           // 1: read K/V with cache-resident loads (blocks shared between sequences)
     // partitioned path (fp32 KV): fixed partitions of part_blocks blocks,
     // partials laid out [B][P][Hq](×D), merged by the reduce kernel
     int32_t part_blocks;

@@ -153,12 +153,13 @@ pkv_status prepare(const void* q, const void* k_cache, const void* v_cache, cons
                    const int32_t* context_lens, float scale, void* out, int32_t num_seqs, int32_t num_q_heads,
                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
                    int32_t max_blocks_per_seq, int32_t max_context_len, int32_t partition_size, void* workspace,
-                   size_t workspace_bytes, pkv_dtype kv_dtype, pkv_dtype out_dtype, Call* c) {
+                   size_t workspace_bytes, pkv_dtype kv_dtype, pkv_dtype out_dtype, uint32_t flags, Call* c) {
     pkv_status st = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                               max_context_len, partition_size, kv_dtype, &c->plan);
     if (st != PKV_OK) return st;
     const Plan& pl = c->plan;
     if (!dtype_ok(out_dtype)) return fail(PKV_ERR_UNSUPPORTED, "unknown output dtype");
+    if (flags & ~(uint32_t)PKV_DECODE_SHARED_BLOCKS) return fail(PKV_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
     if (num_seqs > 0 && (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out))
         return fail(PKV_ERR_INVALID_ARG, "null tensor pointer");
     if (num_blocks <= 0 && num_seqs > 0) return fail(PKV_ERR_INVALID_ARG, "num_blocks must be positive");
@@ -190,6 +191,7 @@ pkv_status prepare(const void* q, const void* k_cache, const void* v_cache, cons
     p.max_blocks_per_seq = max_blocks_per_seq;
     p.ctx_cap = pl.ctx_cap;
     p.out_bf16 = out_dtype == PKV_BF16;
+    p.cached_kv = (flags & PKV_DECODE_SHARED_BLOCKS) ? 1 : 0;
     float* ws = static_cast<float*>(workspace);
     if (pl.balanced) {
         p.walkers = pl.walkers;
@@ -260,7 +262,7 @@ pkv_status run_reduce_kernels(const Call& c, hipStream_t stream) {
 
 extern "C" {
 
-int32_t pkv_abi_version(void) { return 2; }
+int32_t pkv_abi_version(void) { return 3; }
 
 const char* pkv_status_string(pkv_status status) {
     switch (status) {
@@ -311,12 +313,13 @@ pkv_status pkv_paged_attention_decode_partitions(const void* q, const void* k_ca
                                                  int32_t head_dim, int32_t block_size, int64_t num_blocks,
                                                  int32_t max_blocks_per_seq, int32_t max_context_len,
                                                  int32_t partition_size, void* workspace, size_t workspace_bytes,
-                                                 pkv_dtype kv_dtype, pkv_dtype out_dtype, void* stream) {
+                                                 pkv_dtype kv_dtype, pkv_dtype out_dtype, uint32_t flags,
+                                                 void* stream) {
     g_last_error[0] = 0;
     Call c;
     pkv_status st = prepare(q, k_cache, v_cache, block_tables, context_lens, scale, out, num_seqs, num_q_heads,
                             num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len,
-                            partition_size, workspace, workspace_bytes, kv_dtype, out_dtype, &c);
+                            partition_size, workspace, workspace_bytes, kv_dtype, out_dtype, flags, &c);
     if (st != PKV_OK) return st;
     return run_decode_kernels(c, static_cast<hipStream_t>(stream));
 }
@@ -333,7 +336,7 @@ pkv_status pkv_paged_attention_decode_reduce(const int32_t* context_lens, void* 
     const void* unused = context_lens;
     pkv_status st = prepare(unused, unused, unused, context_lens, context_lens, 1.0f, out, num_seqs, num_q_heads,
                             num_kv_heads, head_dim, block_size, 1, max_blocks_per_seq, max_context_len,
-                            partition_size, workspace, workspace_bytes, kv_dtype, out_dtype, &c);
+                            partition_size, workspace, workspace_bytes, kv_dtype, out_dtype, 0, &c);
     if (st != PKV_OK) return st;
     return run_reduce_kernels(c, static_cast<hipStream_t>(stream));
 }
@@ -343,12 +346,13 @@ pkv_status pkv_paged_attention_decode(const void* q, const void* k_cache, const 
                                       int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                       int32_t block_size, int64_t num_blocks, int32_t max_blocks_per_seq,
                                       int32_t max_context_len, int32_t partition_size, void* workspace,
-                                      size_t workspace_bytes, pkv_dtype kv_dtype, pkv_dtype out_dtype, void* stream) {
+                                      size_t workspace_bytes, pkv_dtype kv_dtype, pkv_dtype out_dtype, uint32_t flags,
+                                      void* stream) {
     g_last_error[0] = 0;
     Call c;
     pkv_status st = prepare(q, k_cache, v_cache, block_tables, context_lens, scale, out, num_seqs, num_q_heads,
                             num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len,
-                            partition_size, workspace, workspace_bytes, kv_dtype, out_dtype, &c);
+                            partition_size, workspace, workspace_bytes, kv_dtype, out_dtype, flags, &c);
     if (st != PKV_OK) return st;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     st = run_decode_kernels(c, s);

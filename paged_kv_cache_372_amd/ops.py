@@ -28,15 +28,18 @@ _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace", 4: 
 _lib = None
 
 _vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+_u32 = ctypes.c_uint32
+
+DECODE_SHARED_BLOCKS = 1   # decode flag: sequences share blocks, read K/V through the caches
 
 _SIGNATURES = {
     "pkv_abi_version": (_i32, []),
     "pkv_reshape_and_cache": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _i32, _vp]),
     "pkv_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pkv_paged_attention_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _f32, _vp, _i32, _i32, _i32, _i32, _i32, _i64,
-                                          _i32, _i32, _i32, _vp, _sz, _i32, _i32, _vp]),
+                                          _i32, _i32, _i32, _vp, _sz, _i32, _i32, _u32, _vp]),
     "pkv_paged_attention_decode_partitions": (_i32, [_vp, _vp, _vp, _vp, _vp, _f32, _vp, _i32, _i32, _i32, _i32, _i32,
-                                                     _i64, _i32, _i32, _i32, _vp, _sz, _i32, _i32, _vp]),
+                                                     _i64, _i32, _i32, _i32, _vp, _sz, _i32, _i32, _u32, _vp]),
     "pkv_paged_attention_decode_reduce": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _sz,
                                                  _i32, _i32, _vp]),
     "pkv_status_string": (ctypes.c_char_p, [_i32]),
@@ -143,7 +146,7 @@ class _DecodeArgs:
     """Validated decode arguments, reused by the one-call and two-phase entry points."""
 
     def __init__(self, q, k_cache, v_cache, block_tables, context_lens, scale, out, partition_size,
-                 max_context_len, workspace):
+                 max_context_len, workspace, shared_blocks=False):
         dev = q.device
         for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (block_tables, "block_tables"),
                      (context_lens, "context_lens"), (out, "out")):
@@ -172,7 +175,7 @@ class _DecodeArgs:
         self.args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), float(scale),
                      _ptr(out), B, hq, hkv, D, BLOCK_SIZE, nb, block_tables.shape[1], self.max_context_len,
                      self.partition_size, self.ws_ptr, self.ws_bytes, _dtype_code(k_cache), _dtype_code(out),
-                     _stream(dev))
+                     DECODE_SHARED_BLOCKS if shared_blocks else 0, _stream(dev))
         self.reduce_args = (_ptr(context_lens), _ptr(out), B, hq, hkv, D, BLOCK_SIZE, block_tables.shape[1],
                             self.max_context_len, self.partition_size, self.ws_ptr, self.ws_bytes,
                             _dtype_code(k_cache), _dtype_code(out), _stream(dev))
@@ -181,23 +184,25 @@ class _DecodeArgs:
 def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                            block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
                            out: torch.Tensor, *, partition_size: int = 0, max_context_len: Optional[int] = None,
-                           workspace: Optional[torch.Tensor] = None) -> None:
+                           workspace: Optional[torch.Tensor] = None, shared_blocks: bool = False) -> None:
     """Decode attention of ``q [B, Hq, D]`` over the paged cache into ``out``.
 
     ``max_context_len`` (host-known bound of ``context_lens``) avoids a
     device-to-host sync; ``workspace`` (uint8, >= ``decode_workspace_bytes``,
-    reusable) avoids an allocation.
+    reusable) avoids an allocation.  ``shared_blocks``: several sequences
+    point at the same physical blocks (a common prefix); K/V are then read
+    through the caches instead of streamed.  It never changes the result.
     """
     a = _DecodeArgs(q, k_cache, v_cache, block_tables, context_lens, scale, out, partition_size, max_context_len,
-                    workspace)
+                    workspace, shared_blocks)
     _check(load_library().pkv_paged_attention_decode(*a.args), "paged_attention_decode")
 
 
 def prepare_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out, *, partition_size=0,
-                   max_context_len=None, workspace=None) -> _DecodeArgs:
+                   max_context_len=None, workspace=None, shared_blocks=False) -> _DecodeArgs:
     """Validate once; the returned object drives ``run_partitions`` / ``run_reduce`` repeatedly."""
     return _DecodeArgs(q, k_cache, v_cache, block_tables, context_lens, scale, out, partition_size, max_context_len,
-                       workspace)
+                       workspace, shared_blocks)
 
 
 def run_decode(a: _DecodeArgs) -> None:

@@ -51,7 +51,7 @@ def test_single_hip_runtime_in_process(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pkv_abi_version() == 2
+    assert lib.pkv_abi_version() == 3
     for code in range(5):
         assert lib.pkv_status_string(code)
     assert lib.pkv_status_string(99) == b"unknown status"
@@ -80,11 +80,11 @@ def test_reshape_and_cache_validation(lib):
 
 def dec(lib, **kw):
     a = dict(q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, lens=FAKE, scale=0.1, out=FAKE, B=4, hq=32, hkv=8, D=128, bs=16,
-             nb=100, maxblk=128, maxctx=2000, ps=0, ws=FAKE, wsb=0, kvd=BF16, outd=BF16)
+             nb=100, maxblk=128, maxctx=2000, ps=0, ws=FAKE, wsb=0, kvd=BF16, outd=BF16, flags=0)
     a.update(kw)
     return lib.pkv_paged_attention_decode(a["q"], a["kc"], a["vc"], a["bt"], a["lens"], a["scale"], a["out"], a["B"],
                                           a["hq"], a["hkv"], a["D"], a["bs"], a["nb"], a["maxblk"], a["maxctx"],
-                                          a["ps"], a["ws"], a["wsb"], a["kvd"], a["outd"], None)
+                                          a["ps"], a["ws"], a["wsb"], a["kvd"], a["outd"], a["flags"], None)
 
 
 def test_decode_validation(lib):
@@ -101,6 +101,8 @@ def test_decode_validation(lib):
     assert dec(lib, nb=0) == INVALID
     assert dec(lib, scale=math.inf) == INVALID
     assert dec(lib, scale=math.nan) == INVALID
+    assert dec(lib, flags=2) == INVALID
+    assert b"flag" in lib.pkv_last_error()
     # split needed (2000 tokens > one partition): workspace missing / short / misaligned
     need = lib.pkv_decode_workspace_bytes(4, 32, 8, 128, 2000, 0, BF16)
     assert need > 0

@@ -21,6 +21,7 @@ import workloads as W
 from gpu_util import (DeviceBatch, compare, int_dev, oracle_pools, out_f64, sampled_seqs, say, to_dev,
                       to_host_bits)
 from paged_kv_cache_372_amd import ops
+from paged_kv_cache_372_amd.blocks import tables_share_blocks
 
 pytestmark = pytest.mark.gpu
 
@@ -135,6 +136,25 @@ def test_shared_prefix_full_size_and_private_copies():
     assert torch.equal(db.out.view(torch.int16), db2.out.view(torch.int16)), "shared vs private prefix differ"
 
 
+@pytest.mark.parametrize("make", [lambda: W.shared_prefix(num_seqs=16), lambda: W.llama3_8b_decode(num_seqs=6)],
+                         ids=["shared_prefix", "llama3"])
+def test_shared_blocks_flag_changes_nothing(make):
+    """Cached and streaming reads of K/V give bit-identical outputs, equal to the oracle."""
+    b = make()
+    outs = []
+    for shared in (True, False):
+        say(f"[{b.name} B={b.num_seqs} shared_blocks={shared}]")
+        db = DeviceBatch(b)
+        db.write()
+        db.decode(shared=shared)
+        torch.cuda.synchronize()
+        outs.append(db.out.clone())
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    kp, vp = oracle_pools(b)
+    ref = oracle.ref_paged_attention_decode(b.q, kp, vp, b.block_tables, b.context_lens, b.scale, b.dtype)
+    compare(out_f64(outs[0]), ref, b.dtype, f"{b.name} with cached reads")
+
+
 def test_long_context_small():
     run_and_check(W.long_context(num_seqs=2, context_len=8192), what="8192 tokens, partition 512")
 
@@ -158,7 +178,8 @@ def _batching(sim, steps, sample=None):
         ops.reshape_and_cache(to_dev(st.k_write, sim.dtype), to_dev(st.v_write, sim.dtype),
                               int_dev(st.slot_mapping, np.int64), dk, dv)
         ops.paged_attention_decode(q, dk, dv, bt, lens, sim.scale, out, partition_size=sim.partition_size,
-                                   max_context_len=int(st.context_lens.max()))
+                                   max_context_len=int(st.context_lens.max()),
+                                   shared_blocks=tables_share_blocks(st.block_tables, st.context_lens, 16))
         torch.cuda.synchronize()
         k_pool, v_pool = oracle.ref_reshape_and_cache(st.k_write, st.v_write, st.slot_mapping, k_pool, v_pool)
         seqs = list(range(sim.B)) if sample is None else sampled_seqs(st.context_lens, sample, i)
