@@ -1,4 +1,5 @@
-"""CPU oracle for paged-KV decode (float64, NumPy).
+"""CPU oracle for paged-KV attention (float64, NumPy): decode, the cache
+write and multi-token-query (chunked prefill) attention.
 
 TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
 and the ``cpu_baseline`` leg of ``bench.py``.  The product package never
@@ -7,7 +8,8 @@ imports it, and it shares no code with the GPU kernels.
 from .paged_attention import (gather_contiguous, kv_head_of, merge_partitions, partition_stats,
                               read_k_row, read_v_row, ref_decode_sequence, ref_paged_attention_decode,
                               ref_reshape_and_cache, slot_of_position, softmax_attention, widen)
+from .prefill import query_positions, ref_paged_attention_prefill
 
 __all__ = ["gather_contiguous", "kv_head_of", "merge_partitions", "partition_stats", "read_k_row",
            "read_v_row", "ref_decode_sequence", "ref_paged_attention_decode", "ref_reshape_and_cache",
-           "slot_of_position", "softmax_attention", "widen"]
+           "slot_of_position", "softmax_attention", "widen", "query_positions", "ref_paged_attention_prefill"]
