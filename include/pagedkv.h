@@ -194,6 +194,46 @@ pkv_status pkv_paged_attention_decode_reduce(const int32_t* context_lens, void* 
                                              size_t workspace_bytes, pkv_dtype kv_dtype, pkv_dtype out_dtype,
                                              void* stream);
 
+/*
+ * Multi-token-query paged attention (chunked prefill).  Prefill processes a
+ * whole prompt at once and is compute-bound (runbyai section 1); long
+ * prompts are cut into chunks that share each step with decode requests,
+ * and a request may process any number of tokens in a step (architvora
+ * "Continuous Batching").
+ *
+ * Request s owns rows r0 = query_start_loc[s] .. r1 = query_start_loc[s+1]-1
+ * of q and out: n = r1 - r0 query tokens, the last n of its L =
+ * context_lens[s] cached tokens (the cache write of their keys and values
+ * comes first, as for decode).  Query i sits at position p = L - n + i and
+ * attends causally to positions 0..p of its own sequence, read through
+ * block_tables[s]:
+ *     out[r0+i][h][:] = sum_{j<=p} softmax_j(scale * <q[r0+i][h], K_j>) * V_j,
+ * with K_j / V_j the KV-head h / (num_q_heads / num_kv_heads) rows of token
+ * j.  n = 1 is decode.  A query with p < 0 (n > L) gets zeros.  Matrix
+ * products take bf16 operands with fp32 accumulation; the softmax weights
+ * enter the product with V rounded to bf16 once.
+ *
+ *   q              [device] bf16 [num_tokens][num_q_heads][head_dim]
+ *   k_cache, v_cache [device] pools (layout above), bf16 only
+ *   block_tables   [device] int32 [num_seqs][max_blocks_per_seq]
+ *   context_lens   [device] int32 [num_seqs]
+ *   query_start_loc [device] int32 [num_seqs + 1], non-decreasing, first 0,
+ *                  last num_tokens (rows outside [0, num_tokens) are
+ *                  clamped away, never read or written)
+ *   out            [device] [num_tokens][num_q_heads][head_dim], out_dtype
+ *   max_context_len  host-known bound of context_lens (larger are clamped)
+ * No workspace.  Requests are processed 4096 per launch.  Results do not
+ * depend on where blocks sit in the pool.  fp32 KV returns
+ * PKV_ERR_UNSUPPORTED.
+ */
+pkv_status pkv_paged_attention_prefill(const void* q, const void* k_cache, const void* v_cache,
+                                       const int32_t* block_tables, const int32_t* context_lens,
+                                       const int32_t* query_start_loc, float scale, void* out, int32_t num_seqs,
+                                       int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                       int32_t max_blocks_per_seq, int32_t max_context_len, pkv_dtype kv_dtype,
+                                       pkv_dtype out_dtype, void* stream);
+
 /* Static description of a status code.  Never NULL. */
 const char* pkv_status_string(pkv_status status);
 

@@ -28,6 +28,14 @@ HIPCC_FLAGS = [
 ]
 
 
+# Extra flags per source.  The prefill kernel keeps four column tiles of
+# accumulators live; by default the compiler puts MFMA results in AGPRs and
+# moves them back and forth every iteration, which this flag avoids.
+FILE_FLAGS = {
+    "prefill_mfma.hip": ["-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form"],
+}
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
@@ -45,7 +53,7 @@ def build(verbose: bool = False) -> str:
 
     def compile_one(src: str) -> str:
         obj = os.path.join(BUILD_DIR, os.path.basename(src)[:-4] + ".o")
-        cmd = [cc, *HIPCC_FLAGS, "-c", src, "-o", obj]
+        cmd = [cc, *HIPCC_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
         res = subprocess.run(cmd, capture_output=True, text=True)
         errs = "\n".join(l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l)
         if res.returncode != 0:

@@ -84,23 +84,6 @@ constexpr int kSegLast = 1 << 5;  // this block ends a segment (sequence or rang
 constexpr int kCoherent = 16;     // buffer cache policy: sc1 (device scope, write-through)
 constexpr int kBufferWord3 = 0x00020000;  // buffer descriptor word 3: 32-bit raw data
 
-// Reductions over the four lane groups of a head column (lanes l, l^16,
-// l^32, l^48) with the gfx950 lane-swap instructions: plain VALU work, no
-// LDS traffic, so nothing in the block loop waits on the LDS counter.
-__device__ __forceinline__ float max_over_groups(float x) {
-    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-
-__device__ __forceinline__ float sum_over_groups(float x) {
-    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
 struct SoftmaxState {
     float m;   // reference max (log2 units), same in all lanes of a head column
     float l;   // this lane's share of sum 2^(s - m)

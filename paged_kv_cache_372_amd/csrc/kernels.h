@@ -78,6 +78,37 @@ inline int64_t decode_units(const DecodeParams& p) {
     return (int64_t)p.num_parts * p.num_seqs * p.n_head_groups * p.num_kv_heads;
 }
 
+// Everything one multi-token-query (chunked prefill) launch needs.
+struct PrefillParams {
+    const void* q;                  // [T][Hq][D] bf16, requests' rows packed
+    const void* k_cache;            // [NB][Hkv][D/8][16][8]
+    const void* v_cache;            // [NB][Hkv][D][16]
+    const int32_t* block_tables;    // [B][max_blocks_per_seq] (this launch's requests)
+    const int32_t* context_lens;    // [B]
+    const int32_t* query_start_loc; // [B + 1] absolute rows of q / out
+    void* out;                      // [T][Hq][D]
+    float scale_log2;
+    int32_t num_seqs;               // B of this launch
+    int32_t num_tokens;             // T of the whole call: rows are clamped to it
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t group;                  // Hq / Hkv
+    int32_t head_dim;
+    int64_t num_blocks;
+    int32_t max_blocks_per_seq;
+    int32_t ctx_cap;
+    int32_t out_bf16;
+    int32_t tile_bound;             // workgroup tiles launched per KV head (>= the tiles needed)
+};
+
+// Rows (query token x head of a KV group) one prefill workgroup covers.
+constexpr int kPrefillRowsPerWave = 64;
+constexpr int kPrefillWaves = 4;
+constexpr int kPrefillRowsPerGroup = kPrefillRowsPerWave * kPrefillWaves;
+
+size_t prefill_lds_bytes(int32_t num_seqs);
+hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream);
+
 // Balanced bf16 decode: dynamic LDS bytes and launch shape.
 size_t balanced_lds_bytes(int32_t num_seqs);
 const void* balanced_kernel(int32_t head_dim);
@@ -105,6 +136,23 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 __device__ __forceinline__ float exp2_fast(float x) {
     // v_exp_f32: 2^x, exp2(-inf) = 0
     return __builtin_amdgcn_exp2f(x);
+}
+
+// Reductions over the four lane groups of an MFMA column (lanes l, l^16,
+// l^32, l^48) with the gfx950 lane-swap instructions: plain VALU work, no
+// LDS traffic, so nothing in the block loop waits on the LDS counter.
+__device__ __forceinline__ float max_over_groups(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float sum_over_groups(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 __device__ __forceinline__ int clamp_ctx(int L, int cap) {

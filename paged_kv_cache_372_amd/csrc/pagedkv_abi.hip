@@ -360,4 +360,68 @@ pkv_status pkv_paged_attention_decode(const void* q, const void* k_cache, const 
     return run_reduce_kernels(c, s);
 }
 
+pkv_status pkv_paged_attention_prefill(const void* q, const void* k_cache, const void* v_cache,
+                                       const int32_t* block_tables, const int32_t* context_lens,
+                                       const int32_t* query_start_loc, float scale, void* out, int32_t num_seqs,
+                                       int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                       int32_t max_blocks_per_seq, int32_t max_context_len, pkv_dtype kv_dtype,
+                                       pkv_dtype out_dtype, void* stream) {
+    g_last_error[0] = 0;
+    if (num_seqs < 0 || num_tokens < 0) return fail(PKV_ERR_INVALID_ARG, "num_seqs and num_tokens must be >= 0");
+    if (num_q_heads <= 0 || num_kv_heads <= 0)
+        return fail(PKV_ERR_INVALID_ARG, "head counts must be positive (q %d, kv %d)", num_q_heads, num_kv_heads);
+    if (num_q_heads % num_kv_heads)
+        return fail(PKV_ERR_INVALID_ARG, "num_q_heads (%d) must be a multiple of num_kv_heads (%d)", num_q_heads,
+                    num_kv_heads);
+    if (head_dim != 64 && head_dim != 128) return fail(PKV_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", head_dim);
+    if (block_size != pkv::kBlockSize) return fail(PKV_ERR_UNSUPPORTED, "block_size %d (supported: 16)", block_size);
+    if (kv_dtype != PKV_BF16) return fail(PKV_ERR_UNSUPPORTED, "prefill supports bf16 KV only");
+    if (!dtype_ok(out_dtype)) return fail(PKV_ERR_UNSUPPORTED, "unknown output dtype");
+    if (max_blocks_per_seq < 0 || max_context_len < 0)
+        return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq and max_context_len must be >= 0");
+    if (!isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "scale must be finite");
+    if (num_seqs == 0 || num_tokens == 0) return PKV_OK;
+    if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start_loc || !out)
+        return fail(PKV_ERR_INVALID_ARG, "null tensor pointer");
+    if (num_blocks <= 0) return fail(PKV_ERR_INVALID_ARG, "num_blocks must be positive");
+    if (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)out) % 16)
+        return fail(PKV_ERR_INVALID_ARG, "q, k_cache, v_cache and out must be 16-byte aligned");
+    const int32_t group = num_q_heads / num_kv_heads;
+    const int64_t rows = (int64_t)num_tokens * group;
+    const int64_t by_table = (int64_t)max_blocks_per_seq * block_size;
+    pkv::PrefillParams p;
+    memset(&p, 0, sizeof(p));
+    p.q = q;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.out = out;
+    p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+    p.num_tokens = num_tokens;
+    p.num_q_heads = num_q_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.group = group;
+    p.head_dim = head_dim;
+    p.num_blocks = num_blocks;
+    p.max_blocks_per_seq = max_blocks_per_seq;
+    p.ctx_cap = (int32_t)(max_context_len < by_table ? max_context_len : by_table);
+    p.out_bf16 = out_dtype == PKV_BF16;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    for (int32_t s0 = 0; s0 < num_seqs; s0 += pkv::kMaxSeqsPerLaunch) {
+        const int32_t n = num_seqs - s0 < pkv::kMaxSeqsPerLaunch ? num_seqs - s0 : pkv::kMaxSeqsPerLaunch;
+        p.num_seqs = n;
+        p.block_tables = block_tables + (int64_t)s0 * max_blocks_per_seq;
+        p.context_lens = context_lens + s0;
+        p.query_start_loc = query_start_loc + s0;
+        const int64_t bound = ceil_div(rows, pkv::kPrefillRowsPerGroup) + n;
+        if (bound * num_kv_heads >= ((int64_t)1 << 31))
+            return fail(PKV_ERR_UNSUPPORTED, "%d tokens x %d query heads: too many workgroups for one launch",
+                        num_tokens, num_q_heads);
+        p.tile_bound = (int32_t)bound;
+        pkv_status rc = from_hip(pkv::launch_prefill_bf16(p, st), "prefill kernel launch");
+        if (rc != PKV_OK) return rc;
+    }
+    return PKV_OK;
+}
+
 }  // extern "C"

@@ -1,0 +1,386 @@
+// Multi-token-query paged attention (chunked prefill), bf16 KV, on the gfx950
+// matrix cores.
+//
+// What is computed.  A request s brings n_s >= 1 new query tokens whose keys
+// and values are already in the paged cache, which then holds L_s tokens, the
+// new ones last.  Query i (position p = L_s - n_s + i) attends over positions
+// 0..p: causal attention aligned at the end of the context.  n_s = 1 is
+// decode.  Prefill is the parallel, compute-heavy stage (runbyai section 1);
+// long prompts are cut into chunks that share each step with decode requests
+// (architvora "Continuous Batching"), so a chunk attends over everything
+// cached before it plus itself.  The keys are reached through the request's
+// block table (architvora "Paged Attention").
+//
+// Work decomposition.  The rows of a request are its (query token, head of
+// the KV group) pairs, token-major: n_s * G rows per KV head.  A workgroup
+// takes 256 consecutive rows of one (request, KV head); each of its 4 waves
+// takes 64 rows and walks, on its own, the key blocks those rows can see.
+// The 4 waves read the same K/V blocks at about the same time, so the
+// workgroup's loads hit in L1/L2 after the first; the KV head is the
+// workgroup index modulo Hkv, which keeps each head on one XCD (with 8 KV
+// heads) and its blocks in that XCD's L2.  Heaviest tiles (the last rows of
+// a request see the most keys) are launched first.
+//
+// Per pair of 16-token blocks (A, B), per wave, for each of its four 16-row
+// column tiles j:
+//   S^T[32 keys x 16 rows] = K . Q_j^T        2 x D/32 x mfma_f32_16x16x32_bf16
+//   online softmax on S (exp2 domain, scale*log2e folded in, causal mask)
+//   O_j^T[D x 16 rows] += V^T . P_j^T         D/16 x mfma_f32_16x16x32_bf16
+// The K-dimension of the PV product runs over the 32 keys of the pair in the
+// order (A 4g..4g+3, B 4g..4g+3) for lane group g: that is exactly what the
+// QK result leaves in each lane, so P needs no data movement, and the V^T
+// operand is the two 8-byte V loads of A and B side by side.  P is rounded
+// to bf16 once (a flash-attention-style product; decode, which is bound by
+// memory, carries two bf16 terms instead).
+//
+// Memory: K/V operands are loaded straight from the pool into a register
+// ring two pairs deep (the pool layout makes each load a contiguous 1 KiB or
+// 512 B run per wave); table entries come through the scalar cache one round
+// ahead, as in the decode kernel.  There is no LDS staging: LDS-DMA loads
+// make the compiler wait for every load in flight before any LDS read.
+#include <type_traits>
+
+#include "kernels.h"
+
+namespace pkv {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef const int32_t __attribute__((address_space(4)))* scalar_i32_ptr;
+
+constexpr int kNQ = kPrefillRowsPerWave / 16;  // 16-row column tiles per wave
+constexpr int kPairDepth = 2;                    // block pairs in flight per wave
+constexpr float kSlack = 8.f;                    // lazy-rescale margin (log2 units)
+
+template <int D>
+struct PairRegs {
+    uint4 k[2][D / 32];  // block A, B: load kk holds chunk 4kk + l/16 of token l%16
+    u32x4_t v[D / 16];   // dim 16c + l%16: A's tokens 4(l/16)..+3 in .xy, B's in .zw
+};
+
+// Uniform facts about a pair: first logical block and valid tokens of A, B.
+struct PairInfo {
+    int blk;
+    int nv_a;
+    int nv_b;
+};
+
+struct PairPending {
+    int ea, eb;  // table entries as read (validated at use)
+    int k;       // pair index (clamped)
+};
+
+struct ColState {
+    float m;  // reference max, log2 units (same in the four lane groups of a column)
+    float l;  // this lane's share of the sum of weights
+};
+
+__device__ __forceinline__ uint32_t tail_mask(int nv, int first) {
+    // 16-bit lanes [first, first + 1] of a token run, kept when inside nv
+    return nv >= first + 2 ? 0xFFFFFFFFu : (nv == first + 1 ? 0x0000FFFFu : 0u);
+}
+
+template <int D>
+__global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(PrefillParams p) {
+    extern __shared__ int32_t t_off[];  // [B + 1] first workgroup tile of each request
+    __shared__ int32_t wave_total[kPrefillWaves];
+    const int B = p.num_seqs;
+    const int T = p.num_tokens;
+    const int G = p.group;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    // rows [r0, r1) of q/out belong to request i (clamped to the call's T)
+    auto rows_of = [&](int i, int& r0, int& r1) {
+        r0 = min(max(p.query_start_loc[i], 0), T);
+        r1 = min(max(p.query_start_loc[i + 1], r0), T);
+    };
+
+    // ---- workgroup tiles of every request (exclusive prefix sums)
+    {
+        const int nthr = 64 * kPrefillWaves;
+        const int per = (B + nthr - 1) / nthr;
+        const int i0 = min(B, tid * per);
+        const int i1 = min(B, i0 + per);
+        int sum = 0;
+        for (int i = i0; i < i1; ++i) {
+            int a, b;
+            rows_of(i, a, b);
+            sum += ((b - a) * G + kPrefillRowsPerGroup - 1) / kPrefillRowsPerGroup;
+        }
+        int x = sum;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int y = __shfl_up(x, d);
+            if (lane >= d) x += y;
+        }
+        if (lane == 63) wave_total[wave] = x;
+        __syncthreads();
+        int run = x - sum;
+        for (int w = 0; w < wave; ++w) run += wave_total[w];
+        for (int i = i0; i < i1; ++i) {
+            t_off[i] = run;
+            int a, b;
+            rows_of(i, a, b);
+            run += ((b - a) * G + kPrefillRowsPerGroup - 1) / kPrefillRowsPerGroup;
+        }
+        if (tid == nthr - 1) t_off[B] = run;
+        __syncthreads();
+    }
+    // values read from LDS or memory below are the same in every lane; say
+    // so, so that table entries are fetched through the scalar cache
+    const int total = __builtin_amdgcn_readfirstlane(t_off[B]);
+    const int idx = blockIdx.x / p.num_kv_heads;
+    const int kvh = blockIdx.x - idx * p.num_kv_heads;
+    if (idx >= total) return;
+    const int tile = total - 1 - idx;  // heaviest tiles first
+    int s = 0;
+    {
+        int lo = 0, hi = B - 1;  // last request whose first tile is <= tile
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (t_off[mid] <= tile) lo = mid;
+            else hi = mid - 1;
+        }
+        s = __builtin_amdgcn_readfirstlane(lo);
+    }
+    int r0, r1;
+    rows_of(s, r0, r1);
+    r0 = __builtin_amdgcn_readfirstlane(r0);
+    r1 = __builtin_amdgcn_readfirstlane(r1);
+    const int n = r1 - r0;
+    const int rows = n * G;
+    const int R0 = (tile - __builtin_amdgcn_readfirstlane(t_off[s])) * kPrefillRowsPerGroup + wave * kPrefillRowsPerWave;
+    if (R0 >= rows) return;  // no barrier follows
+    const int L = __builtin_amdgcn_readfirstlane(clamp_ctx(p.context_lens[s], p.ctx_cap));
+    const int Rl = min(R0 + kPrefillRowsPerWave - 1, rows - 1);
+    const int kend = min(L, L - n + Rl / G + 1);  // keys [0, kend) are visible to some row
+
+    const int col = lane & 15;
+    const int g = lane >> 4;
+    const int Hq = p.num_q_heads;
+
+    // per column tile: query position of this lane's row and its row offset
+    int qpos[kNQ];
+    int64_t orow[kNQ];
+#pragma unroll
+    for (int j = 0; j < kNQ; ++j) {
+        const int R = R0 + 16 * j + col;
+        if (R < rows) {
+            const int t = R / G;
+            qpos[j] = L - n + t;  // < 0: no key is visible
+            orow[j] = ((int64_t)(r0 + t) * Hq + kvh * G + (R - t * G)) * D;
+        } else {
+            qpos[j] = -1;
+            orow[j] = -1;
+        }
+    }
+
+    // Q^T operands: column tile j, k-group g holds dims 32kk + 8g .. +7
+    bf16x8_t qv[kNQ][D / 32];
+    const uint16_t* qb = reinterpret_cast<const uint16_t*>(p.q);
+#pragma unroll
+    for (int j = 0; j < kNQ; ++j)
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk) {
+            uint4 w = make_uint4(0, 0, 0, 0);
+            if (orow[j] >= 0) w = *reinterpret_cast<const uint4*>(qb + orow[j] + 32 * kk + 8 * g);
+            qv[j][kk] = __builtin_bit_cast(bf16x8_t, w);
+        }
+
+    float4_t acc[kNQ][D / 16];
+#pragma unroll
+    for (int j = 0; j < kNQ; ++j)
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) acc[j][c] = {0.f, 0.f, 0.f, 0.f};
+    ColState st[kNQ];
+#pragma unroll
+    for (int j = 0; j < kNQ; ++j) st[j] = {-INFINITY, 0.f};
+
+    const int nblk = kend > 0 ? (kend + kBlockSize - 1) / kBlockSize : 0;
+    const int NP = (nblk + 1) / 2;
+
+    if (NP > 0) {
+        const int64_t block_stride = (int64_t)p.num_kv_heads * D * kBlockSize;
+        const uint16_t* k_head = reinterpret_cast<const uint16_t*>(p.k_cache) + (int64_t)kvh * D * kBlockSize;
+        const uint16_t* v_head = reinterpret_cast<const uint16_t*>(p.v_cache) + (int64_t)kvh * D * kBlockSize;
+        const scalar_i32_ptr bt = (scalar_i32_ptr)(p.block_tables + (int64_t)s * p.max_blocks_per_seq);
+        const int vo = (lane & 15) * 4 + (lane >> 4);
+
+        PairRegs<D> ring[kPairDepth];
+        PairInfo info[kPairDepth];
+        PairPending pend[kPairDepth];
+
+        auto fetch = [&](int k, PairPending& e) __attribute__((always_inline)) {
+            const int kc = min(k, NP - 1);
+            e.k = kc;
+            e.ea = bt[2 * kc];
+            e.eb = bt[min(2 * kc + 1, nblk - 1)];
+        };
+        // checked entries -> physical blocks to load (an id outside the pool
+        // loads block 0 with no valid token); the empty asm pins the wait
+        // for the scalar loads here
+        auto accept = [&](const PairPending& e, int& pa, int& pb, PairInfo& inf) __attribute__((always_inline)) {
+            const bool oka = e.ea >= 0 && (int64_t)e.ea < p.num_blocks;
+            const bool okb = e.eb >= 0 && (int64_t)e.eb < p.num_blocks && 2 * e.k + 1 < nblk;
+            pa = oka ? e.ea : 0;
+            pb = okb ? e.eb : 0;
+            inf.blk = 2 * e.k;
+            inf.nv_a = oka ? min(kBlockSize, L - 2 * e.k * kBlockSize) : 0;
+            inf.nv_b = okb ? min(kBlockSize, L - (2 * e.k + 1) * kBlockSize) : 0;
+            asm volatile("" : "+s"(pa), "+s"(pb));
+        };
+        auto load_pair = [&](int d, int pa, int pb, const PairInfo& inf) __attribute__((always_inline)) {
+            info[d] = inf;
+            const u32x4_t* ka = reinterpret_cast<const u32x4_t*>(k_head + (int64_t)pa * block_stride);
+            const u32x4_t* kb = reinterpret_cast<const u32x4_t*>(k_head + (int64_t)pb * block_stride);
+            const u32x2_t* va = reinterpret_cast<const u32x2_t*>(v_head + (int64_t)pa * block_stride);
+            const u32x2_t* vb = reinterpret_cast<const u32x2_t*>(v_head + (int64_t)pb * block_stride);
+            // ordinary loads: the other waves and workgroups of this request
+            // read the same blocks
+#pragma unroll
+            for (int kk = 0; kk < D / 32; ++kk) ring[d].k[0][kk] = __builtin_bit_cast(uint4, ka[kk * 64 + lane]);
+#pragma unroll
+            for (int kk = 0; kk < D / 32; ++kk) ring[d].k[1][kk] = __builtin_bit_cast(uint4, kb[kk * 64 + lane]);
+#pragma unroll
+            for (int c = 0; c < D / 16; ++c) ring[d].v[c].xy = va[c * 64 + vo];
+#pragma unroll
+            for (int c = 0; c < D / 16; ++c) ring[d].v[c].zw = vb[c * 64 + vo];
+        };
+
+        auto compute_pair = [&](PairRegs<D>& r, const PairInfo& inf) __attribute__((always_inline)) {
+            // V^T operands: tokens past a block's valid count are zeroed in
+            // place (they may hold NaN, and 0 * NaN = NaN)
+            {
+                const uint32_t ma0 = tail_mask(inf.nv_a - 4 * g, 0), ma1 = tail_mask(inf.nv_a - 4 * g, 2);
+                const uint32_t mb0 = tail_mask(inf.nv_b - 4 * g, 0), mb1 = tail_mask(inf.nv_b - 4 * g, 2);
+#pragma unroll
+                for (int c = 0; c < D / 16; ++c) r.v[c] &= u32x4_t{ma0, ma1, mb0, mb1};
+            }
+            const int kpa = inf.blk * kBlockSize + 4 * g;  // key position of this lane's first A token
+            const int kpb = kpa + kBlockSize;
+#pragma unroll
+            for (int j = 0; j < kNQ; ++j) {
+                // S^T of both blocks for column tile j
+                float4_t sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < D / 32; ++kk) {
+                    sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.k[0][kk]), qv[j][kk],
+                                                                 sa, 0, 0, 0);
+                    sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.k[1][kk]), qv[j][kk],
+                                                                 sb, 0, 0, 0);
+                }
+                float sv[8];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const bool oa = (4 * g + i < inf.nv_a) && (kpa + i <= qpos[j]);
+                    const bool ob = (4 * g + i < inf.nv_b) && (kpb + i <= qpos[j]);
+                    sv[i] = oa ? sa[i] * p.scale_log2 : -INFINITY;
+                    sv[4 + i] = ob ? sb[i] * p.scale_log2 : -INFINITY;
+                }
+                float mx = sv[0];
+#pragma unroll
+                for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
+                mx = max_over_groups(mx);
+                const bool raise = mx > st[j].m + kSlack;
+                if (__any(raise)) {
+                    const float alpha = raise ? exp2_fast(st[j].m - mx) : 1.f;  // m = -inf -> 0
+                    st[j].l *= alpha;
+#pragma unroll
+                    for (int c = 0; c < D / 16; ++c) acc[j][c] *= alpha;
+                    st[j].m = raise ? mx : st[j].m;
+                }
+                const float m_use = st[j].m == -INFINITY ? 0.f : st[j].m;
+                float pr[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) pr[i] = exp2_fast(sv[i] - m_use);
+                st[j].l += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+                uint32_t w[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    w[i] = f32_to_bf16_bits(pr[2 * i]) | (f32_to_bf16_bits(pr[2 * i + 1]) << 16);
+                const bf16x8_t pj = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+#pragma unroll
+                for (int c = 0; c < D / 16; ++c)
+                    acc[j][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.v[c]), pj,
+                                                                        acc[j][c], 0, 0, 0);
+            }
+        };
+
+        // prologue: entries of the first kPairDepth pairs, then those of the
+        // next round, then the first loads
+        int next_pa[kPairDepth], next_pb[kPairDepth];
+        PairInfo next_info[kPairDepth];
+#pragma unroll
+        for (int d = 0; d < kPairDepth; ++d) fetch(d, pend[d]);
+#pragma unroll
+        for (int d = 0; d < kPairDepth; ++d) accept(pend[d], next_pa[d], next_pb[d], next_info[d]);
+#pragma unroll
+        for (int d = 0; d < kPairDepth; ++d) fetch(kPairDepth + d, pend[d]);
+#pragma unroll
+        for (int d = 0; d < kPairDepth; ++d) {
+            load_pair(d, next_pa[d], next_pb[d], next_info[d]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        auto round = [&](int i, auto final_tag) __attribute__((always_inline)) {
+            constexpr bool kFinal = decltype(final_tag)::value;
+#pragma unroll
+            for (int d = 0; d < kPairDepth; ++d) accept(pend[d], next_pa[d], next_pb[d], next_info[d]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int d = 0; d < kPairDepth; ++d) fetch(i + 2 * kPairDepth + d, pend[d]);
+#pragma unroll
+            for (int d = 0; d < kPairDepth; ++d) {
+                if (!kFinal || i + d < NP) compute_pair(ring[d], info[d]);
+                __builtin_amdgcn_sched_barrier(0);
+                if (!kFinal || i + d + kPairDepth < NP) load_pair(d, next_pa[d], next_pb[d], next_info[d]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        int i = 0;
+        for (; i + 2 * kPairDepth <= NP; i += kPairDepth) round(i, std::false_type{});
+        for (; i < NP; i += kPairDepth) round(i, std::true_type{});
+    }
+
+    // ---- epilogue: out = O / l (zeros for rows that see no key)
+    const bool obf = p.out_bf16 != 0;
+#pragma unroll
+    for (int j = 0; j < kNQ; ++j) {
+        const float lt = sum_over_groups(st[j].l);
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        if (orow[j] < 0) continue;
+        if (obf) {
+            uint16_t* ob = reinterpret_cast<uint16_t*>(p.out) + orow[j] + 4 * g;
+#pragma unroll
+            for (int c = 0; c < D / 16; ++c)
+                *reinterpret_cast<uint2*>(ob + 16 * c) =
+                    make_uint2(f32_to_bf16_bits(acc[j][c][0] * inv) | (f32_to_bf16_bits(acc[j][c][1] * inv) << 16),
+                               f32_to_bf16_bits(acc[j][c][2] * inv) | (f32_to_bf16_bits(acc[j][c][3] * inv) << 16));
+        } else {
+            float* of = reinterpret_cast<float*>(p.out) + orow[j] + 4 * g;
+#pragma unroll
+            for (int c = 0; c < D / 16; ++c)
+                *reinterpret_cast<float4*>(of + 16 * c) = make_float4(acc[j][c][0] * inv, acc[j][c][1] * inv,
+                                                                      acc[j][c][2] * inv, acc[j][c][3] * inv);
+        }
+    }
+}
+
+}  // namespace
+
+size_t prefill_lds_bytes(int32_t num_seqs) { return (size_t)(num_seqs + 1) * sizeof(int32_t); }
+
+hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream) {
+    if (p.num_seqs == 0 || p.tile_bound == 0) return hipSuccess;
+    const dim3 grid((unsigned)((int64_t)p.tile_bound * p.num_kv_heads)), block(64 * kPrefillWaves);
+    const size_t lds = prefill_lds_bytes(p.num_seqs);
+    if (p.head_dim == 128) hipLaunchKernelGGL((prefill_bf16_kernel<128>), grid, block, lds, stream, p);
+    else hipLaunchKernelGGL((prefill_bf16_kernel<64>), grid, block, lds, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace pkv

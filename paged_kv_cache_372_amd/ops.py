@@ -42,6 +42,8 @@ _SIGNATURES = {
                                                      _i64, _i32, _i32, _i32, _vp, _sz, _i32, _i32, _u32, _vp]),
     "pkv_paged_attention_decode_reduce": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _sz,
                                                  _i32, _i32, _vp]),
+    "pkv_paged_attention_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                           _i64, _i32, _i32, _i32, _i32, _vp]),
     "pkv_status_string": (ctypes.c_char_p, [_i32]),
     "pkv_last_error": (ctypes.c_char_p, []),
 }
@@ -215,3 +217,37 @@ def run_partitions(a: _DecodeArgs) -> None:
 
 def run_reduce(a: _DecodeArgs) -> None:
     _check(load_library().pkv_paged_attention_decode_reduce(*a.reduce_args), "paged_attention_decode_reduce")
+
+
+def paged_attention_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                            block_tables: torch.Tensor, context_lens: torch.Tensor, query_start_loc: torch.Tensor,
+                            scale: float, out: torch.Tensor, *, max_context_len: Optional[int] = None) -> None:
+    """Multi-token-query (chunked prefill) attention of ``q [T, Hq, D]`` into ``out``.
+
+    Request ``s`` owns rows ``query_start_loc[s] .. query_start_loc[s+1]-1``:
+    the last ``n_s`` of its ``context_lens[s]`` cached tokens, each attending
+    causally over its sequence.  bf16 KV only.
+    """
+    lib = load_library()
+    dev = q.device
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (block_tables, "block_tables"),
+                 (context_lens, "context_lens"), (query_start_loc, "query_start_loc"), (out, "out")):
+        _check_tensor(t, n, dev)
+    nb, hkv, D = _pool_dims(k_cache, v_cache)
+    _require(k_cache.dtype == torch.bfloat16, "prefill supports bf16 KV only")
+    _require(q.dim() == 3 and q.shape[2] == D and q.dtype == k_cache.dtype, f"q must be bf16 [T, Hq, {D}]")
+    T, hq = q.shape[0], q.shape[1]
+    B = context_lens.shape[0] if context_lens.dim() == 1 else -1
+    _require(context_lens.dtype == torch.int32 and B >= 0, "context_lens must be int32 [B]")
+    _require(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and block_tables.shape[0] == B,
+             "block_tables must be int32 [B, max_blocks_per_seq]")
+    _require(query_start_loc.dtype == torch.int32 and tuple(query_start_loc.shape) == (B + 1,),
+             "query_start_loc must be int32 [B + 1]")
+    _require(tuple(out.shape) == tuple(q.shape), "out must have q's shape")
+    if max_context_len is None:  # costs a device->host synchronisation
+        max_context_len = int(context_lens.max().item()) if B else 0
+    st = lib.pkv_paged_attention_prefill(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                         _ptr(context_lens), _ptr(query_start_loc), float(scale), _ptr(out), B, T,
+                                         hq, hkv, D, BLOCK_SIZE, nb, block_tables.shape[1], int(max_context_len),
+                                         _dtype_code(k_cache), _dtype_code(out), _stream(dev))
+    _check(st, "paged_attention_prefill")

@@ -116,6 +116,33 @@ def test_decode_validation(lib):
     assert red == WORKSPACE
 
 
+def pre(lib, **kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, lens=FAKE, qsl=FAKE, scale=0.1, out=FAKE, B=4, T=64, hq=32, hkv=8,
+             D=128, bs=16, nb=100, maxblk=128, maxctx=2000, kvd=BF16, outd=BF16)
+    a.update(kw)
+    return lib.pkv_paged_attention_prefill(a["q"], a["kc"], a["vc"], a["bt"], a["lens"], a["qsl"], a["scale"],
+                                           a["out"], a["B"], a["T"], a["hq"], a["hkv"], a["D"], a["bs"], a["nb"],
+                                           a["maxblk"], a["maxctx"], a["kvd"], a["outd"], None)
+
+
+def test_prefill_validation(lib):
+    assert pre(lib, kvd=F32) == UNSUPPORTED
+    assert b"bf16" in lib.pkv_last_error()
+    assert pre(lib, hq=30) == INVALID
+    assert pre(lib, D=96) == UNSUPPORTED
+    assert pre(lib, bs=8) == UNSUPPORTED
+    assert pre(lib, outd=9) == UNSUPPORTED
+    assert pre(lib, T=-1) == INVALID
+    assert pre(lib, scale=math.nan) == INVALID
+    assert pre(lib, qsl=None) == INVALID
+    assert pre(lib, nb=0) == INVALID
+    assert pre(lib, out=FAKE + 8) == INVALID
+    # nothing to do: no launch, no pointer needed
+    assert pre(lib, T=0, q=None, kc=None, vc=None, bt=None, lens=None, qsl=None, out=None) == OK
+    assert pre(lib, B=0, q=None) == OK
+    assert lib.pkv_last_error() == b""
+
+
 def _align(x, a=256):
     return -(-x // a) * a
 

@@ -401,6 +401,123 @@ class ContinuousBatching:
                             num_prompt_tokens=n_prompt)
 
 
+# --------------------------------------------------------------------------
+# multi-token-query (chunked prefill) batches
+# --------------------------------------------------------------------------
+
+PREFILL_SEED = 3726
+
+
+@dataclass
+class PrefillBatch:
+    """One step of chunked prefill: every request brings ``n_s`` new tokens.
+
+    Request ``s`` has ``cached[s]`` tokens in the pools already and writes
+    its ``n_s`` new ones (rows ``query_start_loc[s] .. query_start_loc[s+1]-1``
+    of ``q``/``k_new``/``v_new``) at positions ``cached[s] .. cached[s]+n_s-1``
+    through ``slot_mapping``; ``context_lens[s] = cached[s] + n_s``.  The
+    pools hold NaN everywhere else, the new tokens' slots included.
+    """
+
+    name: str
+    seed: int
+    dtype: str
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    q: np.ndarray
+    k_new: np.ndarray
+    v_new: np.ndarray
+    slot_mapping: np.ndarray
+    k_pool: np.ndarray
+    v_pool: np.ndarray
+    block_tables: np.ndarray
+    context_lens: np.ndarray
+    query_start_loc: np.ndarray
+    scale: float
+    info: Dict[str, object] = field(default_factory=dict)
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.context_lens.shape[0])
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def max_context_len(self) -> int:
+        return int(self.context_lens.max()) if self.context_lens.size else 0
+
+    def query_lens(self) -> np.ndarray:
+        return np.diff(self.query_start_loc).astype(np.int64)
+
+    def flops(self) -> int:
+        """Algorithmic flops: 4 * D per (query token, query head, visible key)."""
+        n = self.query_lens()
+        L = self.context_lens.astype(np.int64)
+        # query i of a request (0-based) sees L - n + i + 1 keys
+        visible = (n * (L - n) + n * (n + 1) // 2).sum()
+        return int(4 * self.head_dim * self.num_q_heads * visible)
+
+
+def build_prefill(name: str, seed: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                  cached: Seq[int], new: Seq[int], dtype: str = "bf16", block_size: int = 16,
+                  pool_factor: float = 1.5) -> PrefillBatch:
+    """Requests with ``cached[s]`` tokens already in the pools and ``new[s]`` to process."""
+    bs = block_size
+    cached = [int(c) for c in cached]
+    new = [int(n) for n in new]
+    if any(n < 1 for n in new) or any(c < 0 for c in cached):
+        raise ValueError("every request processes at least one token")
+    lengths = [c + n for c, n in zip(cached, new)]
+    nb = pool_blocks_for(lengths, bs, pool_factor, extra_blocks=1)
+    pool = BlockPool(nb, bs, order=np.random.default_rng([seed, 100]).permutation(nb))
+    seqs: List[Sequence] = []
+    slots = []
+    for i, (c, n) in enumerate(zip(cached, new)):
+        s = Sequence(i)
+        s.reserve(pool, c)
+        slots.append(s.reserve(pool, n))
+        seqs.append(s)
+    slot_mapping = np.concatenate(slots).astype(np.int64)
+    k_pool, v_pool = _fill_pools(nb, num_kv_heads, head_dim, bs, dtype, seed)
+    _poison_all_but(k_pool, v_pool, seqs, cached, bs, dtype)
+    free = pool.free_ids()
+    width = max(blocks_needed(L, bs) for L in lengths)
+    bt = pack_block_tables(seqs, width, free[0])
+    T = sum(new)
+    q = normal_values(T * num_q_heads * head_dim, dtype, seed, _STREAMS["q"]).reshape(T, num_q_heads, head_dim)
+    k_new = normal_values(T * num_kv_heads * head_dim, dtype, seed, _STREAMS["k_new"]).reshape(T, num_kv_heads, head_dim)
+    v_new = normal_values(T * num_kv_heads * head_dim, dtype, seed, _STREAMS["v_new"]).reshape(T, num_kv_heads, head_dim)
+    qsl = np.concatenate([[0], np.cumsum(new)]).astype(np.int32)
+    return PrefillBatch(name=name, seed=seed, dtype=dtype, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
+                        head_dim=head_dim, block_size=bs, num_blocks=nb, q=q, k_new=k_new, v_new=v_new,
+                        slot_mapping=slot_mapping, k_pool=k_pool, v_pool=v_pool, block_tables=bt,
+                        context_lens=pack_context_lens(seqs), query_start_loc=qsl,
+                        scale=1.0 / math.sqrt(head_dim), info={"cached": cached})
+
+
+def chunked_prefill(seed: int = PREFILL_SEED, num_seqs: int = 16, chunk: int = 512, cached_max: int = 3584,
+                    num_decode: int = 0, decode_cached_max: int = 4095) -> PrefillBatch:
+    """Llama-3-8B-shaped (32 q / 8 KV heads, D = 128, bf16) chunked-prefill step.
+
+    ``num_seqs`` requests each process a chunk of ``chunk`` tokens on top of
+    a cached prefix uniform on [0, cached_max] (whole chunks of a long prompt
+    under a token budget of num_seqs * chunk), followed by ``num_decode``
+    decode requests (one token each on top of U[1, decode_cached_max]).
+    """
+    rng = np.random.default_rng([seed, 0])
+    cached = list(rng.integers(0, cached_max, size=num_seqs, endpoint=True))
+    new = [chunk] * num_seqs
+    if num_decode:
+        cached += list(rng.integers(1, decode_cached_max, size=num_decode, endpoint=True))
+        new += [1] * num_decode
+    return build_prefill("chunked_prefill", seed, 32, 8, 128, cached, new)
+
+
 def build(name: str, seed: Optional[int] = None, **kw):
     """Static workloads by name (``continuous_batching`` returns the simulator)."""
     seed = DEFAULT_SEEDS[name] if seed is None else seed
