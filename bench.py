@@ -32,14 +32,27 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
 METRIC = "paged-attn decode: achieved KV-read HBM GB/s (% of peak) + decode tokens/s"
+PEAK_BF16_TFLOPS = 2500.0
+PREFILL_METRIC = "paged-attn chunked prefill: attention TFLOP/s (causal flops) + prefill tokens/s"
+PREFILL_CONFIGS = ("chunked_prefill",)
+
+
+def family(workload: str) -> str:
+    return "prefill" if workload in PREFILL_CONFIGS else "decode"
+
+
 def traffic_file(workload: str) -> str:
-    return os.path.join(ROOT, "profiles", f"decode_traffic_{workload}.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_372_amd", "csrc", f) for f in ("decode_mfma.hip", "kernels.h")]
+    return os.path.join(ROOT, "profiles", f"{family(workload)}_traffic_{workload}.json")
 
 
-def kernel_source_hash() -> str:
+def kernel_sources(workload: str):
+    main = "prefill_mfma.hip" if family(workload) == "prefill" else "decode_mfma.hip"
+    return [os.path.join(ROOT, "paged_kv_cache_372_amd", "csrc", f) for f in (main, "kernels.h")]
+
+
+def kernel_source_hash(workload: str = "llama3_8b_decode") -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in kernel_sources(workload):
         h.update(open(p, "rb").read())
     return h.hexdigest()
 
@@ -54,7 +67,7 @@ def measured_traffic(workload: str, partition_size: int):
         rec = json.load(open(traffic_file(workload)))
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256") != kernel_source_hash():
+    if rec.get("source_sha256") != kernel_source_hash(workload):
         return None
     if rec.get("workload") != workload or rec.get("partition_size") != partition_size:
         return None
@@ -172,6 +185,7 @@ def calibrate_copy(mib: int, reps: int):
 
 
 DECODE_KERNEL_PREFIX = "void pkv::(anonymous namespace)::decode_bf16_balanced_kernel"
+PREFILL_KERNEL_PREFIX = "void pkv::(anonymous namespace)::prefill_bf16_kernel"
 
 
 def _read_counter(dirpath: str, counter: str):
@@ -210,7 +224,8 @@ def summarize_profile(prefix: str, workload: str, partition_size, copy_mib: int,
     copy_name = "__amd_rocclr_copyBuffer"
     f_factor = copy_kib / cal_f[copy_name]
     w_factor = copy_kib / cal_w[copy_name]
-    dec = [k for k in fetch if k.startswith(DECODE_KERNEL_PREFIX)][0]
+    prefix_k = PREFILL_KERNEL_PREFIX if family(workload) == "prefill" else DECODE_KERNEL_PREFIX
+    dec = [k for k in fetch if k.startswith(prefix_k)][0]
     lines = [f"# rocprofv3: decode kernels on the {workload} workload", "",
              "Commands (run from the repository root; `cd /tmp && export TMPDIR=/tmp` first):", "", "```",
              commands.strip(), "```", "", "## Kernel trace (`--kernel-trace --stats`)", "",
@@ -236,13 +251,117 @@ def summarize_profile(prefix: str, workload: str, partition_size, copy_mib: int,
         if last:
             lines += ["", f"## Bench line of the same build (`python bench.py --config {workload}`)", "", "```",
                       last[-1], "```"]
-    rec = {"source_sha256": kernel_source_hash(), "workload": workload, "partition_size": partition_size,
+    rec = {"source_sha256": kernel_source_hash(workload), "workload": workload, "partition_size": partition_size,
            "kernel": dec, "fetch_kib_per_dispatch": fetch[dec], "write_kib_per_dispatch": write.get(dec, 0.0),
            "fetch_copy_factor": f_factor, "write_copy_factor": w_factor}
     os.makedirs(os.path.dirname(out_md), exist_ok=True)
     open(out_md, "w").write("\n".join(lines) + "\n")
     json.dump(rec, open(out_json, "w"), indent=1)
     print(f"wrote {out_md} and {out_json}")
+
+
+def cpu_baseline_prefill(b, budget_s: float = 12.0):
+    """The prefill oracle, as it stands, request after request of the same
+    workload, until about ``budget_s`` seconds of CPU work are done."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    kp, vp = oracle.ref_reshape_and_cache(b.k_new, b.v_new, b.slot_mapping, b.k_pool, b.v_pool)
+    n = b.query_lens()
+    L = b.context_lens.astype(np.int64)
+    t0 = time.perf_counter()
+    done, flops, tokens = 0, 0, 0
+    for s in range(b.num_seqs):
+        oracle.ref_paged_attention_prefill(b.q, kp, vp, b.block_tables, b.context_lens, b.query_start_loc, b.scale,
+                                           b.dtype, seqs=[s])
+        done += 1
+        tokens += int(n[s])
+        flops += 4 * b.head_dim * b.num_q_heads * int(n[s] * (L[s] - n[s]) + n[s] * (n[s] + 1) // 2)
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of the {b.num_seqs} requests of the {b.name} workload ({tokens} query tokens, "
+                      f"float64, all {b.num_q_heads} q heads, after the oracle's cache write), {dt:.1f} s",
+            "tokens_per_s": round(tokens / dt, 3), "cpu_model": _cpu_model(), "os_cpu_count": os.cpu_count()}
+
+
+def run_prefill(args):
+    """Chunked-prefill step: the cache write of every new token, then the
+    multi-token-query attention.  Value = algorithmic (causal) attention
+    flops per step / wall time per step."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_372_amd import ops
+    import workloads as W
+
+    t_gen = time.perf_counter()
+    b = W.chunked_prefill()
+    gen_s = time.perf_counter() - t_gen
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+    def ints(a, dt):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=dt)).cuda()
+
+    q, k_new, v_new = dev(b.q), dev(b.k_new), dev(b.v_new)
+    kc, vc = dev(b.k_pool), dev(b.v_pool)
+    slots = ints(b.slot_mapping, np.int64)
+    bt, lens, qsl = ints(b.block_tables, np.int32), ints(b.context_lens, np.int32), ints(b.query_start_loc, np.int32)
+    out = torch.empty_like(q)
+    flops = b.flops()
+
+    def step(ev=None):
+        ops.reshape_and_cache(k_new, v_new, slots, kc, vc)
+        if ev is not None:
+            ev[0].record()
+        ops.paged_attention_prefill(q, kc, vc, bt, lens, qsl, b.scale, out, max_context_len=b.max_context_len)
+        if ev is not None:
+            ev[1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    k_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    ms = wall / args.steps * 1e3
+    value = flops / (ms / 1e3) / 1e12
+    achieved = flops / (k_ms / 1e3) / 1e12
+    traffic = measured_traffic(b.name, "none")
+    rec = {
+        "metric": PREFILL_METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": b.name, "seed": b.seed, "num_seqs": b.num_seqs, "num_tokens": b.num_tokens,
+                   "num_q_heads": b.num_q_heads, "num_kv_heads": b.num_kv_heads, "head_dim": b.head_dim,
+                   "block_size": b.block_size, "chunk": int(b.query_lens().max()),
+                   "cached_mean": round(float(np.mean(b.info["cached"])), 1),
+                   "context_len_max": b.max_context_len, "flops_per_step": flops},
+        "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "tokens_per_s": round(b.num_tokens / (ms / 1e3), 1),
+        "prefill_kernel_ms": round(k_ms, 5),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "kernel": "prefill_bf16_kernel", "flops_per_launch": flops},
+        "input_generation_s": round(gen_s, 2),
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline_prefill(b, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
 
 
 def main():
@@ -265,8 +384,11 @@ def main():
 
     if args.summarize_profile:
         ps = args.partition_size if args.partition_size > 0 else "balanced"
+        if family(args.config) == "prefill":
+            ps = "none"
         summarize_profile(args.summarize_profile, args.config, ps, args.profile_copy_mib,
-                          os.path.join(ROOT, "profiles", f"decode_{args.config}.md"), traffic_file(args.config),
+                          os.path.join(ROOT, "profiles", f"{family(args.config)}_{args.config}.md"),
+                          traffic_file(args.config),
                           open(args.profile_commands).read() if args.profile_commands else "")
         return
 
@@ -285,6 +407,10 @@ def main():
     ops.load_library()
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy, max(1, args.steps))
+        return
+
+    if family(args.config) == "prefill":
+        run_prefill(args)
         return
 
     t_gen = time.perf_counter()

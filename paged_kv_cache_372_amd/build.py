@@ -30,9 +30,11 @@ HIPCC_FLAGS = [
 
 # Extra flags per source.  The prefill kernel keeps four column tiles of
 # accumulators live; by default the compiler puts MFMA results in AGPRs and
-# moves them back and forth every iteration, which this flag avoids.
+# moves them back and forth every iteration, which the first flag avoids.
+# Its scores are finite or -inf, never NaN: without NaN semantics the
+# compiler drops the quieting max(x, x) it puts before every fmaxf.
 FILE_FLAGS = {
-    "prefill_mfma.hip": ["-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form"],
+    "prefill_mfma.hip": ["-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form", "-Xarch_device", "-fno-honor-nans"],
 }
 
 

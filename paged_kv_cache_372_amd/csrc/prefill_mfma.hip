@@ -54,6 +54,7 @@ typedef const int32_t __attribute__((address_space(4)))* scalar_i32_ptr;
 constexpr int kNQ = kPrefillRowsPerWave / 16;  // 16-row column tiles per wave
 constexpr int kPairDepth = 2;                    // block pairs in flight per wave
 constexpr float kSlack = 8.f;                    // lazy-rescale margin (log2 units)
+constexpr int kExpValu = 28;                     // VALU instructions for one column tile's weights
 
 template <int D>
 struct PairRegs {
@@ -77,6 +78,14 @@ struct ColState {
     float m;  // reference max, log2 units (same in the four lane groups of a column)
     float l;  // this lane's share of the sum of weights
 };
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
+// two fp32 -> packed bf16 (round to nearest even), one instruction
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{a, b}, bf16x2_t));
+}
 
 __device__ __forceinline__ uint32_t tail_mask(int nv, int first) {
     // 16-bit lanes [first, first + 1] of a token run, kept when inside nv
@@ -180,7 +189,11 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(Prefil
         }
     }
 
-    // Q^T operands: column tile j, k-group g holds dims 32kk + 8g .. +7
+    // Q^T operands: column tile j, k-group g holds dims 32kk + 8g .. +7.
+    // A negative scale is carried by q (negating bf16 is exact), so the
+    // softmax below works with c = |scale * log2 e| >= 0.
+    const float c_scale = fabsf(p.scale_log2);
+    const uint32_t qsign = p.scale_log2 < 0.f ? 0x80008000u : 0u;
     bf16x8_t qv[kNQ][D / 32];
     const uint16_t* qb = reinterpret_cast<const uint16_t*>(p.q);
 #pragma unroll
@@ -189,8 +202,15 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(Prefil
         for (int kk = 0; kk < D / 32; ++kk) {
             uint4 w = make_uint4(0, 0, 0, 0);
             if (orow[j] >= 0) w = *reinterpret_cast<const uint4*>(qb + orow[j] + 32 * kk + 8 * g);
+            w.x ^= qsign;
+            w.y ^= qsign;
+            w.z ^= qsign;
+            w.w ^= qsign;
             qv[j][kk] = __builtin_bit_cast(bf16x8_t, w);
         }
+    // first query position of the wave: a pair ending at or before it is
+    // visible to every row
+    const int qmin = L - n + R0 / G;
 
     float4_t acc[kNQ][D / 16];
 #pragma unroll
@@ -252,10 +272,14 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(Prefil
             for (int c = 0; c < D / 16; ++c) ring[d].v[c].zw = vb[c * 64 + vo];
         };
 
-        auto compute_pair = [&](PairRegs<D>& r, const PairInfo& inf) __attribute__((always_inline)) {
-            // V^T operands: tokens past a block's valid count are zeroed in
-            // place (they may hold NaN, and 0 * NaN = NaN)
-            {
+        // One pair.  kMasked: the pair holds tokens past the context end or
+        // past some row's position (the causal diagonal); otherwise every
+        // score is live and the mask work is skipped.
+        auto compute_pair = [&](PairRegs<D>& r, const PairInfo& inf, auto masked_tag) __attribute__((always_inline)) {
+            constexpr bool kMasked = decltype(masked_tag)::value;
+            if constexpr (kMasked) {
+                // tokens past a block's valid count are zeroed in place (they
+                // may hold NaN, and 0 * NaN = NaN)
                 const uint32_t ma0 = tail_mask(inf.nv_a - 4 * g, 0), ma1 = tail_mask(inf.nv_a - 4 * g, 2);
                 const uint32_t mb0 = tail_mask(inf.nv_b - 4 * g, 0), mb1 = tail_mask(inf.nv_b - 4 * g, 2);
 #pragma unroll
@@ -263,9 +287,11 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(Prefil
             }
             const int kpa = inf.blk * kBlockSize + 4 * g;  // key position of this lane's first A token
             const int kpb = kpa + kBlockSize;
+            // S^T of both blocks for every column tile, then the new maxima
+            float sv[kNQ][8];
+            float mx[kNQ];
 #pragma unroll
             for (int j = 0; j < kNQ; ++j) {
-                // S^T of both blocks for column tile j
                 float4_t sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kk = 0; kk < D / 32; ++kk) {
@@ -274,40 +300,76 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(Prefil
                     sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.k[1][kk]), qv[j][kk],
                                                                  sb, 0, 0, 0);
                 }
-                float sv[8];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const bool oa = (4 * g + i < inf.nv_a) && (kpa + i <= qpos[j]);
-                    const bool ob = (4 * g + i < inf.nv_b) && (kpb + i <= qpos[j]);
-                    sv[i] = oa ? sa[i] * p.scale_log2 : -INFINITY;
-                    sv[4 + i] = ob ? sb[i] * p.scale_log2 : -INFINITY;
+                    sv[j][i] = sa[i];
+                    sv[j][4 + i] = sb[i];
                 }
-                float mx = sv[0];
+                if constexpr (kMasked) {
 #pragma unroll
-                for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
-                mx = max_over_groups(mx);
-                const bool raise = mx > st[j].m + kSlack;
-                if (__any(raise)) {
-                    const float alpha = raise ? exp2_fast(st[j].m - mx) : 1.f;  // m = -inf -> 0
+                    for (int i = 0; i < 4; ++i) {
+                        const bool oa = (4 * g + i < inf.nv_a) && (kpa + i <= qpos[j]);
+                        const bool ob = (4 * g + i < inf.nv_b) && (kpb + i <= qpos[j]);
+                        sv[j][i] = oa ? sv[j][i] * c_scale : -INFINITY;
+                        sv[j][4 + i] = ob ? sv[j][4 + i] * c_scale : -INFINITY;
+                    }
+                }
+                float m8 = fmaxf(fmaxf(fmaxf(sv[j][0], sv[j][1]), fmaxf(sv[j][2], sv[j][3])),
+                                 fmaxf(fmaxf(sv[j][4], sv[j][5]), fmaxf(sv[j][6], sv[j][7])));
+                // unmasked: all scores live and c >= 0, so scale the max only
+                mx[j] = kMasked ? max_over_groups(m8) : max_over_groups(m8) * c_scale;
+            }
+            // one rescale check for the pair (rarely taken: see kSlack)
+            bool raise[kNQ];
+            bool any = false;
+#pragma unroll
+            for (int j = 0; j < kNQ; ++j) {
+                raise[j] = mx[j] > st[j].m + kSlack;
+                any = any || raise[j];
+            }
+            if (__any(any)) {
+#pragma unroll
+                for (int j = 0; j < kNQ; ++j) {
+                    const float alpha = raise[j] ? exp2_fast(st[j].m - mx[j]) : 1.f;  // m = -inf -> 0
                     st[j].l *= alpha;
 #pragma unroll
                     for (int c = 0; c < D / 16; ++c) acc[j][c] *= alpha;
-                    st[j].m = raise ? mx : st[j].m;
+                    st[j].m = raise[j] ? mx[j] : st[j].m;
                 }
+            }
+            // weights and the PV products
+#pragma unroll
+            for (int j = 0; j < kNQ; ++j) {
                 const float m_use = st[j].m == -INFINITY ? 0.f : st[j].m;
                 float pr[8];
+                if constexpr (kMasked) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) pr[i] = exp2_fast(sv[i] - m_use);
+                    for (int i = 0; i < 8; ++i) pr[i] = exp2_fast(sv[j][i] - m_use);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) pr[i] = exp2_fast(fmaf(sv[j][i], c_scale, -m_use));
+                }
                 st[j].l += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
-                uint32_t w[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    w[i] = f32_to_bf16_bits(pr[2 * i]) | (f32_to_bf16_bits(pr[2 * i + 1]) << 16);
-                const bf16x8_t pj = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+                const bf16x8_t pj = __builtin_bit_cast(
+                    bf16x8_t, make_uint4(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
+                                         pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])));
 #pragma unroll
                 for (int c = 0; c < D / 16; ++c)
                     acc[j][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.v[c]), pj,
                                                                         acc[j][c], 0, 0, 0);
+            }
+            if constexpr (!kMasked) {
+                // Interleave: the weights of tile j + 1 (VALU) are computed
+                // while the matrix core runs the PV products of tile j, so
+                // neither unit waits for the other.  (Masks: 0x2 VALU,
+                // 0x8 MFMA.)
+                __builtin_amdgcn_sched_group_barrier(0x2, kExpValu, 0);
+#pragma unroll
+                for (int t = 0; t < (kNQ - 1) * (D / 16); ++t) {
+                    __builtin_amdgcn_sched_group_barrier(0x8, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x2, kExpValu / (D / 16), 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x8, D / 16, 0);
             }
         };
 
@@ -326,7 +388,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(Prefil
             load_pair(d, next_pa[d], next_pb[d], next_info[d]);
             __builtin_amdgcn_sched_barrier(0);
         }
-        auto round = [&](int i, auto final_tag) __attribute__((always_inline)) {
+        auto round = [&](int i, auto final_tag, auto masked_tag) __attribute__((always_inline)) {
             constexpr bool kFinal = decltype(final_tag)::value;
 #pragma unroll
             for (int d = 0; d < kPairDepth; ++d) accept(pend[d], next_pa[d], next_pb[d], next_info[d]);
@@ -335,15 +397,24 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(Prefil
             for (int d = 0; d < kPairDepth; ++d) fetch(i + 2 * kPairDepth + d, pend[d]);
 #pragma unroll
             for (int d = 0; d < kPairDepth; ++d) {
-                if (!kFinal || i + d < NP) compute_pair(ring[d], info[d]);
+                if (!kFinal || i + d < NP) compute_pair(ring[d], info[d], masked_tag);
                 __builtin_amdgcn_sched_barrier(0);
                 if (!kFinal || i + d + kPairDepth < NP) load_pair(d, next_pa[d], next_pb[d], next_info[d]);
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
+        // Pairs [0, NPf) are visible to every row of the wave and hold 32
+        // cached tokens: their rounds skip the mask.  (A table entry outside
+        // the pool there is read as block 0 -- never out of bounds, but the
+        // result is then unspecified; in masked rounds such a block is
+        // skipped.)  The rest, the causal diagonal and the context end
+        // included, take the masked form.
+        const int NPf = min(NP, (qmin + 1) / (2 * kBlockSize));
         int i = 0;
-        for (; i + 2 * kPairDepth <= NP; i += kPairDepth) round(i, std::false_type{});
-        for (; i < NP; i += kPairDepth) round(i, std::true_type{});
+        for (; i + 2 * kPairDepth <= NP && i + kPairDepth <= NPf; i += kPairDepth)
+            round(i, std::false_type{}, std::false_type{});
+        for (; i + 2 * kPairDepth <= NP; i += kPairDepth) round(i, std::false_type{}, std::true_type{});
+        for (; i < NP; i += kPairDepth) round(i, std::true_type{}, std::true_type{});
     }
 
     // ---- epilogue: out = O / l (zeros for rows that see no key)
