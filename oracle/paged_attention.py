@@ -202,15 +202,36 @@ def ref_decode_sequence(q_s: np.ndarray, kc: np.ndarray, vc: np.ndarray, scale: 
     return out
 
 
+def widen_kv(kc: np.ndarray, vc: np.ndarray, dtype: str, heads: Sequence[int], k_scale=None, v_scale=None):
+    """float64 K/V of gathered rows ``[L, len(heads), D]``.
+
+    ``dtype`` "fp8": E4M3 codes times the per-KV-head scales (see
+    ``oracle/fp8.py``); otherwise the stored values widened exactly.
+    """
+    if dtype != "fp8":
+        return widen(kc, dtype), widen(vc, dtype)
+    from .fp8 import e4m3_decode
+    ks = np.asarray(k_scale, dtype=np.float64)[list(heads)].reshape(1, -1, 1)
+    vs = np.asarray(v_scale, dtype=np.float64)[list(heads)].reshape(1, -1, 1)
+    return e4m3_decode(kc) * ks, e4m3_decode(vc) * vs
+
+
+def q_dtype_of(dtype: str) -> str:
+    """Queries are not cached: with an fp8 cache they stay bf16."""
+    return "bf16" if dtype == "fp8" else dtype
+
+
 def ref_paged_attention_decode(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, block_tables: np.ndarray,
                                context_lens: np.ndarray, scale: float, dtype: str,
                                seqs: Optional[Iterable[int]] = None,
-                               q_heads: Optional[Sequence[int]] = None) -> np.ndarray:
+                               q_heads: Optional[Sequence[int]] = None,
+                               k_scale=None, v_scale=None) -> np.ndarray:
     """Paged decode attention, float64 result ``[len(seqs), len(q_heads), D]``.
 
     For each sequence: walk its block table to get contiguous K/V (only the
-    KV heads the requested query heads need), widen to float64, then plain
-    softmax attention per query head.
+    KV heads the requested query heads need), widen to float64 (for an fp8
+    cache: decode and scale per KV head), then plain softmax attention per
+    query head.
     """
     B, Hq, D = q.shape
     Hkv = k_pool.shape[1]
@@ -221,7 +242,8 @@ def ref_paged_attention_decode(q: np.ndarray, k_pool: np.ndarray, v_pool: np.nda
     for i, s in enumerate(seqs):
         L = int(context_lens[s])
         kc, vc = gather_contiguous(k_pool, v_pool, block_tables[s], L, heads=kv_needed)
-        out[i] = ref_decode_sequence(widen(q[s], dtype), widen(kc, dtype), widen(vc, dtype), scale, Hkv,
+        kw, vw = widen_kv(kc, vc, dtype, kv_needed, k_scale, v_scale)
+        out[i] = ref_decode_sequence(widen(q[s], q_dtype_of(dtype)), kw, vw, scale, Hkv,
                                      q_heads=q_heads, kv_heads_present=kv_needed)
     return out
 

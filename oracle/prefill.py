@@ -38,7 +38,7 @@ from typing import Iterable, Optional, Sequence
 
 import numpy as np
 
-from .paged_attention import gather_contiguous, kv_head_of, softmax_attention, widen
+from .paged_attention import gather_contiguous, kv_head_of, q_dtype_of, softmax_attention, widen, widen_kv
 
 
 def query_positions(context_len: int, num_queries: int) -> np.ndarray:
@@ -71,10 +71,12 @@ def ref_prefill_sequence(q_rows: np.ndarray, kc: np.ndarray, vc: np.ndarray, sca
 def ref_paged_attention_prefill(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, block_tables: np.ndarray,
                                 context_lens: np.ndarray, query_start_loc: np.ndarray, scale: float, dtype: str,
                                 seqs: Optional[Iterable[int]] = None,
-                                q_heads: Optional[Sequence[int]] = None) -> np.ndarray:
+                                q_heads: Optional[Sequence[int]] = None,
+                                k_scale=None, v_scale=None) -> np.ndarray:
     """Multi-token-query paged attention, float64 ``[T, len(q_heads), D]``.
 
-    Rows of requests not listed in ``seqs`` are left as NaN.
+    Rows of requests not listed in ``seqs`` are left as NaN.  ``dtype``
+    "fp8": E4M3 pools with per-KV-head scales, bf16 queries.
     """
     T, Hq, D = q.shape
     Hkv = k_pool.shape[1]
@@ -87,7 +89,7 @@ def ref_paged_attention_prefill(q: np.ndarray, k_pool: np.ndarray, v_pool: np.nd
         r0, r1 = int(query_start_loc[s]), int(query_start_loc[s + 1])
         L = int(context_lens[s])
         kc, vc = gather_contiguous(k_pool, v_pool, block_tables[s], L, heads=kv_needed)
-        out[r0:r1] = ref_prefill_sequence(widen(q[r0:r1], dtype), widen(kc, dtype), widen(vc, dtype), scale, Hkv,
-                                          q_heads, kv_needed)
+        kw, vw = widen_kv(kc, vc, dtype, kv_needed, k_scale, v_scale)
+        out[r0:r1] = ref_prefill_sequence(widen(q[r0:r1], q_dtype_of(dtype)), kw, vw, scale, Hkv, q_heads, kv_needed)
     return out
 
