@@ -83,6 +83,8 @@ def build_workload(name: str, ps: int):
     import workloads as W
     if name == "long_context":
         return W.long_context(partition_size=ps if ps >= 0 else 512), None
+    if name == "long_context_fp8":
+        return W.fp8_variant(W.long_context(partition_size=ps if ps >= 0 else 512)), None
     ps = max(ps, 0)
     if name == "continuous_batching":
         sim = W.ContinuousBatching(partition_size=ps)
@@ -97,6 +99,8 @@ def build_workload(name: str, ps: int):
         return b, steps
     if name == "llama3_8b_decode":
         return W.llama3_8b_decode(partition_size=ps), None
+    if name == "llama3_8b_decode_fp8":
+        return W.fp8_variant(W.llama3_8b_decode(partition_size=ps)), None
     if name == "shared_prefix":
         return W.shared_prefix(partition_size=ps), None
     if name == "tiny_fp32":
@@ -113,13 +117,21 @@ def cpu_baseline(b, budget_s: float = 12.0):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         threads = 1
-    kp, vp = oracle.ref_reshape_and_cache(b.k_new, b.v_new, b.slot_mapping, b.k_pool, b.v_pool)
+    fp8 = b.dtype == "fp8"
+    if fp8:
+        ks, vs = b.info["k_scale"], b.info["v_scale"]
+        kp, vp = oracle.ref_reshape_and_cache_fp8(b.k_new, b.v_new, b.slot_mapping, b.k_pool, b.v_pool, ks, vs,
+                                                  "bf16")
+    else:
+        ks = vs = None
+        kp, vp = oracle.ref_reshape_and_cache(b.k_new, b.v_new, b.slot_mapping, b.k_pool, b.v_pool)
     t0 = time.perf_counter()
     done, kv_bytes, passes = 0, 0, 0
-    es = 2 if b.dtype == "bf16" else 4
+    es = {"bf16": 2, "f32": 4, "fp8": 1}[b.dtype]
     while time.perf_counter() - t0 < budget_s:
         for s in range(b.num_seqs):
-            oracle.ref_paged_attention_decode(b.q, kp, vp, b.block_tables, b.context_lens, b.scale, b.dtype, seqs=[s])
+            oracle.ref_paged_attention_decode(b.q, kp, vp, b.block_tables, b.context_lens, b.scale, b.dtype, seqs=[s],
+                                              k_scale=ks, v_scale=vs)
             done += 1
             kv_bytes += int(b.context_lens[s]) * 2 * b.num_kv_heads * b.head_dim * es
             if time.perf_counter() - t0 >= budget_s:
@@ -416,12 +428,15 @@ def main():
     t_gen = time.perf_counter()
     b, batching_steps = build_workload(args.config, args.partition_size)
     gen_s = time.perf_counter() - t_gen
-    dtype = torch.bfloat16 if b.dtype == "bf16" else torch.float32
+    fp8 = b.dtype == "fp8"
+    dtype = torch.float32 if b.dtype == "f32" else torch.bfloat16   # q / out (bf16 over an fp8 cache)
+    pool_dtype = torch.uint8 if fp8 else dtype
 
     def dev(a):
-        if b.dtype == "bf16":
-            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
-        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:      # bf16 bit patterns
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(a).cuda()
 
     def ints(a):
         return torch.from_numpy(np.ascontiguousarray(a)).cuda()
@@ -433,7 +448,7 @@ def main():
     else:
         host_steps = [(st.k_write, st.v_write, st.slot_mapping, st.q, st.block_tables, st.context_lens)
                       for st in batching_steps]
-    es = 2 if b.dtype == "bf16" else 4
+    es = {"bf16": 2, "f32": 4, "fp8": 1}[b.dtype]
     step_kv = [int(np.asarray(h[5], dtype=np.int64).sum()) * 2 * b.num_kv_heads * b.head_dim * es for h in host_steps]
     kv_bytes = sum(step_kv) / len(step_kv)  # per step, averaged over the distinct steps
     pool_bytes = b.k_pool.nbytes + b.v_pool.nbytes
@@ -451,7 +466,12 @@ def main():
                               max_ctx=int(np.max(lh)), out=torch.empty(q.shape, dtype=dtype, device="cuda"),
                               shared=tables_share_blocks(bth, lh, b.block_size)))
     ws_bytes = max(ops.decode_workspace_bytes(b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim, g["max_ctx"], ps,
-                                              dtype) for g in gpu_steps)
+                                              pool_dtype) for g in gpu_steps)
+    if fp8:
+        k_scale = torch.from_numpy(np.asarray(b.info["k_scale"], dtype=np.float32)).cuda()
+        v_scale = torch.from_numpy(np.asarray(b.info["v_scale"], dtype=np.float32)).cuda()
+    else:
+        k_scale = v_scale = None
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
     n_in = len(gpu_steps)
     plans = {}
@@ -459,13 +479,16 @@ def main():
         for r in range(R):
             plans[j, r] = ops.prepare_decode(g["q"], kcs[r], vcs[r], g["bt"], g["lens"], b.scale, g["out"],
                                              partition_size=ps, max_context_len=g["max_ctx"], workspace=ws,
-                                             shared_blocks=g["shared"])
-    resolved_ps = ps if ps else ("balanced" if b.dtype == "bf16" else "auto")
+                                             shared_blocks=g["shared"], k_scale=k_scale, v_scale=v_scale)
+    resolved_ps = ps if ps else ("auto" if b.dtype == "f32" else "balanced")
 
     def step(i, ev=None):
         j, r = i % n_in, i % R
         g = gpu_steps[j]
-        ops.reshape_and_cache(g["k_new"], g["v_new"], g["slots"], kcs[r], vcs[r])
+        if fp8:
+            ops.reshape_and_cache_fp8(g["k_new"], g["v_new"], g["slots"], kcs[r], vcs[r], k_scale, v_scale)
+        else:
+            ops.reshape_and_cache(g["k_new"], g["v_new"], g["slots"], kcs[r], vcs[r])
         if ev is not None:
             ev[0].record()
         ops.run_partitions(plans[j, r])
@@ -511,20 +534,21 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": b.dtype,
+        "dtype": "bf16" if fp8 else b.dtype,   # an fp8 cache is decoded to bf16 for the products
         "data": "synthetic",
         "config": {"workload": b.name, "seed": b.seed, "num_seqs": b.num_seqs, "num_q_heads": b.num_q_heads,
                    "num_kv_heads": b.num_kv_heads, "head_dim": b.head_dim, "block_size": b.block_size,
                    "context_len_mean": round(float(b.context_lens.mean()), 1),
                    "context_len_max": b.max_context_len, "partition_size": resolved_ps,
                    "kv_bytes_per_step": int(round(kv_bytes)), "distinct_steps": n_in, "pool_bytes": pool_bytes,
-                   "pool_replicas": R, "shared_blocks": any(g["shared"] for g in gpu_steps)},
+                   "pool_replicas": R, "shared_blocks": any(g["shared"] for g in gpu_steps),
+                   "kv_dtype": "fp8_e4m3" if fp8 else b.dtype},
         "frac_of_peak": round(value / PEAK_HBM_GBS, 4),
         "tokens_per_s": round(b.num_seqs / (ms_per_step / 1e3), 1),
         "decode_kernel_ms": round(dec, 5),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-                     "kernel": "decode_bf16_balanced_kernel" if b.dtype == "bf16" else "decode_valu_kernel",
+                     "kernel": "decode_valu_kernel" if b.dtype == "f32" else "decode_bf16_balanced_kernel",
                      "bytes_per_launch": int(round(kv_bytes))},
         "input_generation_s": round(gen_s, 2),
     }

@@ -32,12 +32,13 @@
  *     max_blocks_per_seq * block_size)].
  *   - Thread-safe: calls may come from several host threads at once.
  *
- * Element types: PKV_F32 (IEEE binary32) or PKV_BF16 (bfloat16, 16-bit).
+ * Element types: PKV_F32 (IEEE binary32) or PKV_BF16 (bfloat16, 16-bit); a KV
+ * pool may also hold PKV_FP8_E4M3 codes (one byte per element, see below).
  * Tensors are dense, row-major, with the shapes given below.
  *
  * KV pool layout (one K pool and one V pool, shape fixed at allocation):
  *   k_cache [num_blocks][num_kv_heads][head_dim/x][block_size][x],
- *           x = 16 / element_size (4 for f32, 8 for bf16): the head_dim
+ *           x = 16 / element_size (4 for f32, 8 for bf16, 16 for fp8): the head_dim
  *           values of a token are split into 16-byte chunks, and the chunks
  *           of the 16 tokens of a block are stored chunk-major;
  *   v_cache [num_blocks][num_kv_heads][head_dim][block_size]: for each dim,
@@ -64,7 +65,8 @@ typedef enum pkv_status {
 
 typedef enum pkv_dtype {
     PKV_F32 = 0,
-    PKV_BF16 = 1
+    PKV_BF16 = 1,
+    PKV_FP8_E4M3 = 2  /* KV pools only: OCP E4M3 codes, see the fp8 calls */
 } pkv_dtype;
 
 /* Decode flags (a performance choice only: results are bit-identical with
@@ -193,6 +195,56 @@ pkv_status pkv_paged_attention_decode_reduce(const int32_t* context_lens, void* 
                                              int32_t max_context_len, int32_t partition_size, void* workspace,
                                              size_t workspace_bytes, pkv_dtype kv_dtype, pkv_dtype out_dtype,
                                              void* stream);
+
+/*
+ * fp8 KV cache.  The pages name quantisation of the KV cache as the lever for
+ * long contexts (runbyai section 5); they fix no format.  Here a pool element
+ * is an OCP E4M3 code (1 sign bit, 4 exponent bits with bias 7, 3 mantissa
+ * bits, subnormals, largest finite 448, 0x7F / 0xFF NaN) and each KV head has
+ * one positive fp32 scale for K and one for V, chosen by the caller:
+ *   stored code = E4M3(fp32(x / scale[h]))  (a correctly rounded fp32
+ *                 division, then round to nearest even, saturating at +-448);
+ *   value read  = decode(code) * scale[h].
+ * Pools use the layout at the top with one-byte elements: a (block, head) tile
+ * is 2 KiB at head_dim 128, half the bytes of bf16.
+ *
+ * Quantising cache write: like pkv_reshape_and_cache, from f32 or bf16 rows
+ * (src_dtype) into fp8 pools.
+ *   k_scale, v_scale  [device] fp32 [num_kv_heads]
+ */
+pkv_status pkv_reshape_and_cache_fp8(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                                     void* k_cache, void* v_cache, const float* k_scale, const float* v_scale,
+                                     int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                     int64_t num_blocks, pkv_dtype src_dtype, void* stream);
+
+/*
+ * Decode over an fp8 cache: pkv_paged_attention_decode with K = decode(code) *
+ * k_scale[g] and V = decode(code) * v_scale[g] for KV head g.  q is bf16; out
+ * is out_dtype.  The codes are converted to bf16 exactly and the products
+ * run as for a bf16 cache (the scales enter the score scale and the output).
+ * Workspace: pkv_decode_workspace_bytes(..., PKV_FP8_E4M3).  The other decode
+ * entry points reject PKV_FP8_E4M3.
+ */
+pkv_status pkv_paged_attention_decode_fp8(const void* q, const void* k_cache, const void* v_cache,
+                                          const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                                          const int32_t* context_lens, float scale, void* out, int32_t num_seqs,
+                                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                          int32_t block_size, int64_t num_blocks, int32_t max_blocks_per_seq,
+                                          int32_t max_context_len, int32_t partition_size, void* workspace,
+                                          size_t workspace_bytes, pkv_dtype out_dtype, uint32_t flags, void* stream);
+
+/* The decode launch of pkv_paged_attention_decode_fp8 on its own; follow it
+ * with pkv_paged_attention_decode_reduce(..., kv_dtype = PKV_FP8_E4M3, ...)
+ * on the same stream with the same arguments and workspace. */
+pkv_status pkv_paged_attention_decode_partitions_fp8(const void* q, const void* k_cache, const void* v_cache,
+                                                     const float* k_scale, const float* v_scale,
+                                                     const int32_t* block_tables, const int32_t* context_lens,
+                                                     float scale, void* out, int32_t num_seqs, int32_t num_q_heads,
+                                                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                                     int64_t num_blocks, int32_t max_blocks_per_seq,
+                                                     int32_t max_context_len, int32_t partition_size,
+                                                     void* workspace, size_t workspace_bytes, pkv_dtype out_dtype,
+                                                     uint32_t flags, void* stream);
 
 /*
  * Multi-token-query paged attention (chunked prefill).  Prefill processes a

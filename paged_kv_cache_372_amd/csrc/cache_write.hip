@@ -86,6 +86,124 @@ __global__ __launch_bounds__(kThreads) void cache_write_kernel(const E* __restri
     }
 }
 
+// fp32 -> OCP E4M3 code: round to nearest (ties to even mantissa), saturate
+// at +-448; the sign of zero is kept.  Written out from the format (1 sign,
+// 4 exponent bits with bias 7, 3 mantissa bits, subnormals m * 2^-9) with
+// integer operations, so the result is fixed bit for bit.
+__device__ __forceinline__ uint32_t e4m3_rne_sat(float y) {
+    const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+    const float a = fminf(fabsf(y), 448.f);
+    if (a < 0.015625f)                                   // below 2^-6: multiples of 2^-9
+        return sign | (uint32_t)__builtin_rintf(a * 512.f);  // exact scaling, rint rounds to even
+    const uint32_t ab = __float_as_uint(a);
+    const uint32_t r = (ab >> 20) & 7u;                  // top 3 mantissa bits
+    const uint32_t rem = ab & 0xFFFFFu;                  // the 20 dropped bits
+    const uint32_t up = (rem > 0x80000u || (rem == 0x80000u && (r & 1u))) ? 1u : 0u;
+    const uint32_t code = ((((ab >> 23) - 120u) << 3) | r) + up;  // exponent bias 127 -> 7; a carry bumps it
+    return sign | (code < 0x7Eu ? code : 0x7Eu);
+}
+
+// Quantising cache write: fp8 pools, bf16 or fp32 inputs, one scale per KV
+// head for K and for V.  Same thread layout as the copy kernel above; a K
+// output chunk now holds 16 dims (16 one-byte codes).
+template <typename E, int D>
+__global__ __launch_bounds__(kThreads) void cache_write_fp8_kernel(const E* __restrict__ k_new,
+                                                                   const E* __restrict__ v_new,
+                                                                   const int64_t* __restrict__ slot_mapping,
+                                                                   uint8_t* __restrict__ k_cache,
+                                                                   uint8_t* __restrict__ v_cache,
+                                                                   const float* __restrict__ k_scale,
+                                                                   const float* __restrict__ v_scale,
+                                                                   int64_t num_tokens, int num_kv_heads,
+                                                                   int64_t num_slots) {
+    constexpr int NCH = D / 16;                       // 16-dim output chunks per row
+    constexpr int kRowPad = 16 / (int)sizeof(E);
+    __shared__ __align__(16) E vrow[kTokens][D + kRowPad];
+    __shared__ int64_t tile_of[kTokens];
+    __shared__ int off_of[kTokens];
+
+    const int h = blockIdx.x % num_kv_heads;
+    const int64_t t0 = (int64_t)(blockIdx.x / num_kv_heads) * kTokens;
+    const int tid = threadIdx.x;
+    const float ks = k_scale[h];
+    const float vs = v_scale[h];
+
+    if (tid < kTokens) {
+        const int64_t t = t0 + tid;
+        int64_t tile = -1;
+        int off = 0;
+        if (t < num_tokens) {
+            const int64_t slot = slot_mapping[t];
+            if (slot >= 0 && slot < num_slots) {
+                tile = (slot / kBlockSize * num_kv_heads + h) * (int64_t)(D * kBlockSize);
+                off = (int)(slot % kBlockSize);
+            }
+        }
+        tile_of[tid] = tile;
+        off_of[tid] = off;
+    }
+    constexpr int X = 16 / (int)sizeof(E);            // input elements per 16-byte load
+    for (int i = tid; i < kTokens * (D / X); i += kThreads) {
+        const int t = i / (D / X);
+        const int c = i % (D / X);
+        if (t0 + t < num_tokens) {
+            const uint4 w = reinterpret_cast<const uint4*>(v_new + ((t0 + t) * num_kv_heads + h) * (int64_t)D)[c];
+            *reinterpret_cast<uint4*>(&vrow[t][c * X]) = w;
+        }
+    }
+    __syncthreads();
+
+    auto to_f32 = [](E e) -> float {
+        if constexpr (sizeof(E) == 2) return __uint_as_float((uint32_t)e << 16);
+        else return __uint_as_float((uint32_t)e);
+    };
+    // K: thread (c, t), t fastest: 16 codes of chunk c of token t
+    for (int i = tid; i < kTokens * NCH; i += kThreads) {
+        const int t = i % kTokens;
+        const int c = i / kTokens;
+        const int64_t tile = tile_of[t];
+        if (tile < 0) continue;
+        const E* src = k_new + ((t0 + t) * num_kv_heads + h) * (int64_t)D + 16 * c;
+        uint32_t w[4];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            uint32_t b = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) b |= e4m3_rne_sat(to_f32(src[4 * q4 + e]) / ks) << (8 * e);
+            w[q4] = b;
+        }
+        reinterpret_cast<uint4*>(k_cache + tile)[c * kBlockSize + off_of[t]] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    // V: thread (d, t), t fastest: one code per (token, dim)
+    for (int i = tid; i < kTokens * D; i += kThreads) {
+        const int t = i % kTokens;
+        const int d = i / kTokens;
+        const int64_t tile = tile_of[t];
+        if (tile < 0) continue;
+        v_cache[tile + (int64_t)d * kBlockSize + off_of[t]] = (uint8_t)e4m3_rne_sat(to_f32(vrow[t][d]) / vs);
+    }
+}
+
+template <typename E>
+hipError_t launch_fp8(const void* k_new, const void* v_new, const int64_t* slots, void* k_cache, void* v_cache,
+                      const float* k_scale, const float* v_scale, int64_t num_tokens, int num_kv_heads,
+                      int head_dim, int64_t num_blocks, hipStream_t stream) {
+    const int64_t groups = (num_tokens + kTokens - 1) / kTokens * num_kv_heads;
+    const dim3 grid((unsigned)groups), block(kThreads);
+    const int64_t num_slots = num_blocks * kBlockSize;
+    const E* kn = static_cast<const E*>(k_new);
+    const E* vn = static_cast<const E*>(v_new);
+    uint8_t* kc = static_cast<uint8_t*>(k_cache);
+    uint8_t* vc = static_cast<uint8_t*>(v_cache);
+    if (head_dim == 128)
+        hipLaunchKernelGGL((cache_write_fp8_kernel<E, 128>), grid, block, 0, stream, kn, vn, slots, kc, vc, k_scale,
+                           v_scale, num_tokens, num_kv_heads, num_slots);
+    else
+        hipLaunchKernelGGL((cache_write_fp8_kernel<E, 64>), grid, block, 0, stream, kn, vn, slots, kc, vc, k_scale,
+                           v_scale, num_tokens, num_kv_heads, num_slots);
+    return hipGetLastError();
+}
+
 template <typename E>
 hipError_t launch_typed(const void* k_new, const void* v_new, const int64_t* slots, void* k_cache, void* v_cache,
                         int64_t num_tokens, int num_kv_heads, int head_dim, int64_t num_blocks, hipStream_t stream) {
@@ -106,6 +224,18 @@ hipError_t launch_typed(const void* k_new, const void* v_new, const int64_t* slo
 }
 
 }  // namespace
+
+hipError_t launch_cache_write_fp8(const void* k_new, const void* v_new, const int64_t* slot_mapping, void* k_cache,
+                                  void* v_cache, const float* k_scale, const float* v_scale, int64_t num_tokens,
+                                  int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks, bool src_bf16,
+                                  hipStream_t stream) {
+    if (num_tokens == 0) return hipSuccess;
+    if (src_bf16)
+        return launch_fp8<uint16_t>(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale, num_tokens,
+                                    num_kv_heads, head_dim, num_blocks, stream);
+    return launch_fp8<uint32_t>(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale, num_tokens,
+                                num_kv_heads, head_dim, num_blocks, stream);
+}
 
 hipError_t launch_cache_write(const void* k_new, const void* v_new, const int64_t* slot_mapping, void* k_cache,
                               void* v_cache, int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim,

@@ -57,6 +57,9 @@ namespace {
 #define PKV_PREFETCH_BLOCKS 3
 #endif
 constexpr int kPrefetchBlocks = PKV_PREFETCH_BLOCKS;  // KV blocks each wave keeps in flight
+// An fp8 ring slot takes 2/3 of the registers, but a deeper ring was
+// measured no faster, so fp8 keeps the same depth.
+constexpr int kPrefetchBlocksFp8 = kPrefetchBlocks;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
@@ -72,6 +75,48 @@ struct SlotRegs {
     uint2 v[D / 16];       // V^T: load c holds dim 16c + lane%16, tokens 4(lane/16)..+3
     bf16x8_t q[D / 32];    // Q^T as the B operand: column = head, k-group lane/16 holds chunk 4kk + lane/16
 };
+
+// The same for an fp8 (E4M3) cache: the raw codes, converted to bf16 operands
+// when the block is used (the conversion is exact).  K: load i holds the
+// 16-dim chunk 4i + lane/16 of token lane%16; the QK contraction takes dims in
+// the order that makes step kk read half (kk & 1) of load kk/2, and q is
+// loaded in that order.  V: load c holds dim 16c + lane%16, tokens
+// 4(lane/16)..+3, one code each.
+template <int D>
+struct SlotRegs8 {
+    uint4 k[D / 64];
+    uint32_t v[D / 16];
+    bf16x8_t q[D / 32];    // q step kk, k-group g: dims 64(kk/2) + 16g + 8(kk&1) .. +7
+};
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+template <bool kHigh>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+    // codes of bytes 2*kHigh, 2*kHigh + 1; scale 1.0: the exact value of each code
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHigh));
+}
+
+template <int D>
+__device__ __forceinline__ bf16x8_t k_operand(const SlotRegs<D>& r, int kk) {
+    return __builtin_bit_cast(bf16x8_t, r.k[kk]);
+}
+template <int D>
+__device__ __forceinline__ uint2 v_operand(const SlotRegs<D>& r, int c) {
+    return r.v[c];
+}
+template <int D>
+__device__ __forceinline__ bf16x8_t k_operand(const SlotRegs8<D>& r, int kk) {
+    const uint4 w = r.k[kk >> 1];
+    const uint32_t a = (kk & 1) ? w.z : w.x;
+    const uint32_t b = (kk & 1) ? w.w : w.y;
+    return __builtin_bit_cast(bf16x8_t, make_uint4(e4m3x2_to_bf16x2<false>(a), e4m3x2_to_bf16x2<true>(a),
+                                                   e4m3x2_to_bf16x2<false>(b), e4m3x2_to_bf16x2<true>(b)));
+}
+template <int D>
+__device__ __forceinline__ uint2 v_operand(const SlotRegs8<D>& r, int c) {
+    return make_uint2(e4m3x2_to_bf16x2<false>(r.v[c]), e4m3x2_to_bf16x2<true>(r.v[c]));
+}
 
 // Uniform facts about the block a ring slot holds.
 struct SlotInfo {
@@ -97,14 +142,14 @@ struct SoftmaxState {
 // moves less often.
 constexpr float kRescaleSlack = 8.f;
 
-template <int D>
-__device__ __forceinline__ void compute_block(const SlotRegs<D>& r, float4_t* acc, SoftmaxState& st, int valid_n,
+template <int D, typename Slot>
+__device__ __forceinline__ void compute_block(const Slot& r, float4_t* acc, SoftmaxState& st, int valid_n,
                                               float scale_log2, int g) {
     // S = K . Q^T: lane holds S[token 4g + i][head lane%16], i = 0..3
     float4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk)
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.k[kk]), r.q[kk], sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<D>(r, kk), r.q[kk], sacc, 0, 0, 0);
 
     float sv[4];
 #pragma unroll
@@ -143,7 +188,8 @@ __device__ __forceinline__ void compute_block(const SlotRegs<D>& r, float4_t* ac
     }
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
-        const short4_t a = __builtin_bit_cast(short4_t, make_uint2(r.v[c].x & vm0, r.v[c].y & vm1));
+        const uint2 vw = v_operand<D>(r, c);
+        const short4_t a = __builtin_bit_cast(short4_t, make_uint2(vw.x & vm0, vw.y & vm1));
         acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, p_hi, acc[c], 0, 0, 0);
         acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, p_lo, acc[c], 0, 0, 0);
     }
@@ -168,8 +214,10 @@ struct Pending {
 
 typedef const int32_t __attribute__((address_space(4)))* scalar_i32_ptr;
 
-template <int D, int kDepth, bool kCached>
+template <int D, int kDepth, bool kCached, bool kFp8>
 __global__ __launch_bounds__(64 * kMaxWavesPerGroup) void decode_bf16_balanced_kernel(DecodeParams p) {
+    using Elem = std::conditional_t<kFp8, uint8_t, uint16_t>;  // one K/V pool element
+    using Slot = std::conditional_t<kFp8, SlotRegs8<D>, SlotRegs<D>>;
     extern __shared__ int32_t tables[];
     __shared__ int32_t wave_total[kMaxWavesPerGroup];
     const int B = p.num_seqs;
@@ -268,8 +316,11 @@ __global__ __launch_bounds__(64 * kMaxWavesPerGroup) void decode_bf16_balanced_k
     const int qcol = min(col, nh - 1);
 
     const int64_t block_stride = (int64_t)p.num_kv_heads * D * kBlockSize;
-    const uint16_t* k_head = reinterpret_cast<const uint16_t*>(p.k_cache) + (int64_t)kvh * D * kBlockSize;
-    const uint16_t* v_head = reinterpret_cast<const uint16_t*>(p.v_cache) + (int64_t)kvh * D * kBlockSize;
+    const Elem* k_head = reinterpret_cast<const Elem*>(p.k_cache) + (int64_t)kvh * D * kBlockSize;
+    const Elem* v_head = reinterpret_cast<const Elem*>(p.v_cache) + (int64_t)kvh * D * kBlockSize;
+    // an fp8 cache: K's scale folds into the score scale, V's into the output
+    const float score_scale = kFp8 ? p.scale_log2 * p.k_scale[kvh] : p.scale_log2;
+    const float out_scale = kFp8 ? p.v_scale[kvh] : 1.f;
     const uint16_t* q_base = reinterpret_cast<const uint16_t*>(p.q) + (int64_t)(h0 + qcol) * D;
 
     // Describe walk positions [base, base + 64).
@@ -320,7 +371,7 @@ __global__ __launch_bounds__(64 * kMaxWavesPerGroup) void decode_bf16_balanced_k
         e.info.slot = __builtin_amdgcn_readlane(cur.slot, li);
     };
 
-    SlotRegs<D> ring[kDepth];
+    Slot ring[kDepth];
     SlotInfo info[kDepth];
     Pending pend[kDepth];
 
@@ -340,24 +391,40 @@ __global__ __launch_bounds__(64 * kMaxWavesPerGroup) void decode_bf16_balanced_k
     // vector loads, so the wait before a block covers only that block's loads.
     auto load_slot = [&](int d, int pb, const SlotInfo& inf) {
         info[d] = inf;
-        const u32x4_t* kt = reinterpret_cast<const u32x4_t*>(k_head + (int64_t)pb * block_stride);
-        const u32x2_t* vt = reinterpret_cast<const u32x2_t*>(v_head + (int64_t)pb * block_stride);
         const uint4* qr = reinterpret_cast<const uint4*>(q_base + (int64_t)info[d].seq * Hq * D);
-        // Streaming (the default): each KV tile is read once, so non-temporal
-        // loads keep it from displacing reusable lines (q, tables) and
-        // measurably raise the rate.  kCached: sequences share blocks, so
-        // ordinary loads leave them in the caches for the next reader.
+        if constexpr (kFp8) {
+            const u32x4_t* kt = reinterpret_cast<const u32x4_t*>(k_head + (int64_t)pb * block_stride);
+            const uint32_t* vt = reinterpret_cast<const uint32_t*>(v_head + (int64_t)pb * block_stride);
 #pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk)
-            ring[d].k[kk] = __builtin_bit_cast(uint4, kCached ? kt[kk * 64 + lane]
-                                                              : __builtin_nontemporal_load(kt + kk * 64 + lane));
+            for (int i = 0; i < D / 64; ++i)
+                ring[d].k[i] = __builtin_bit_cast(uint4, kCached ? kt[i * 64 + lane]
+                                                                 : __builtin_nontemporal_load(kt + i * 64 + lane));
 #pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk) ring[d].q[kk] = __builtin_bit_cast(bf16x8_t, qr[4 * kk + g]);
-        const int vo = (lane & 15) * 4 + (lane >> 4);
+            for (int kk = 0; kk < D / 32; ++kk)
+                ring[d].q[kk] = __builtin_bit_cast(bf16x8_t, qr[8 * (kk >> 1) + 2 * g + (kk & 1)]);
+            const int vo = (lane & 15) * 4 + (lane >> 4);
 #pragma unroll
-        for (int c = 0; c < D / 16; ++c)
-            ring[d].v[c] = __builtin_bit_cast(uint2, kCached ? vt[c * 64 + vo]
-                                                             : __builtin_nontemporal_load(vt + c * 64 + vo));
+            for (int c = 0; c < D / 16; ++c)
+                ring[d].v[c] = kCached ? vt[c * 64 + vo] : __builtin_nontemporal_load(vt + c * 64 + vo);
+        } else {
+            const u32x4_t* kt = reinterpret_cast<const u32x4_t*>(k_head + (int64_t)pb * block_stride);
+            const u32x2_t* vt = reinterpret_cast<const u32x2_t*>(v_head + (int64_t)pb * block_stride);
+            // Streaming (the default): each KV tile is read once, so non-temporal
+            // loads keep it from displacing reusable lines (q, tables) and
+            // measurably raise the rate.  kCached: sequences share blocks, so
+            // ordinary loads leave them in the caches for the next reader.
+#pragma unroll
+            for (int kk = 0; kk < D / 32; ++kk)
+                ring[d].k[kk] = __builtin_bit_cast(uint4, kCached ? kt[kk * 64 + lane]
+                                                                  : __builtin_nontemporal_load(kt + kk * 64 + lane));
+#pragma unroll
+            for (int kk = 0; kk < D / 32; ++kk) ring[d].q[kk] = __builtin_bit_cast(bf16x8_t, qr[4 * kk + g]);
+            const int vo = (lane & 15) * 4 + (lane >> 4);
+#pragma unroll
+            for (int c = 0; c < D / 16; ++c)
+                ring[d].v[c] = __builtin_bit_cast(uint2, kCached ? vt[c * 64 + vo]
+                                                                 : __builtin_nontemporal_load(vt + c * 64 + vo));
+        }
     };
 
     float4_t acc[D / 16];
@@ -375,8 +442,12 @@ __global__ __launch_bounds__(64 * kMaxWavesPerGroup) void decode_bf16_balanced_k
         const float l_tot = sum_over_groups(st.l);
         if (col < nh) {
             if (slot < 0) {
-                store_out(seq, acc, l_tot > 0.f ? 1.f / l_tot : 0.f);
+                store_out(seq, acc, l_tot > 0.f ? out_scale / l_tot : 0.f);
             } else {
+                if constexpr (kFp8) {
+#pragma unroll
+                    for (int c = 0; c < D / 16; ++c) acc[c] *= out_scale;
+                }
                 // write-through stores (sc1): the rows are read once, by the
                 // reduce kernel, so they need not sit dirty in this XCD's L2
                 // (measured faster than plain stores when pieces are many)
@@ -435,7 +506,7 @@ __global__ __launch_bounds__(64 * kMaxWavesPerGroup) void decode_bf16_balanced_k
 #pragma unroll
         for (int d = 0; d < kDepth; ++d) {
             if (!kFinal || i + d < K) {
-                compute_block<D>(ring[d], acc, st, info[d].meta & 31, p.scale_log2, g);
+                compute_block<D>(ring[d], acc, st, info[d].meta & 31, score_scale, g);
                 if (info[d].meta & kSegLast) finish_segment(info[d].seq, info[d].slot);
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -456,24 +527,31 @@ size_t balanced_lds_bytes(int32_t num_seqs) { return (size_t)(2 * num_seqs + 1) 
 const void* balanced_kernel(int32_t head_dim) {
     // the plan sizes the grid from the streaming variant's occupancy; the
     // cached variant needs no more registers or LDS
-    return head_dim == 128 ? reinterpret_cast<const void*>(&decode_bf16_balanced_kernel<128, kPrefetchBlocks, false>)
-                           : reinterpret_cast<const void*>(&decode_bf16_balanced_kernel<64, kPrefetchBlocks, false>);
+    return head_dim == 128 ? reinterpret_cast<const void*>(&decode_bf16_balanced_kernel<128, kPrefetchBlocks, false, false>)
+                           : reinterpret_cast<const void*>(&decode_bf16_balanced_kernel<64, kPrefetchBlocks, false, false>);
 }
 
-template <int D>
+template <int D, bool kFp8>
 void launch_balanced(const DecodeParams& p, dim3 grid, dim3 block, size_t lds, hipStream_t stream) {
     if (p.cached_kv)
-        hipLaunchKernelGGL((decode_bf16_balanced_kernel<D, kPrefetchBlocks, true>), grid, block, lds, stream, p);
+        hipLaunchKernelGGL((decode_bf16_balanced_kernel<D, kFp8 ? kPrefetchBlocksFp8 : kPrefetchBlocks, true, kFp8>),
+                           grid, block, lds, stream, p);
     else
-        hipLaunchKernelGGL((decode_bf16_balanced_kernel<D, kPrefetchBlocks, false>), grid, block, lds, stream, p);
+        hipLaunchKernelGGL((decode_bf16_balanced_kernel<D, kFp8 ? kPrefetchBlocksFp8 : kPrefetchBlocks, false, kFp8>),
+                           grid, block, lds, stream, p);
 }
 
 hipError_t launch_decode_bf16_balanced(const DecodeParams& p, hipStream_t stream) {
     if (p.num_seqs == 0) return hipSuccess;
     const dim3 grid((unsigned)((int64_t)p.walkers * p.head_unit_groups)), block(64 * p.waves_per_group);
     const size_t lds = balanced_lds_bytes(p.num_seqs);
-    if (p.head_dim == 128) launch_balanced<128>(p, grid, block, lds, stream);
-    else launch_balanced<64>(p, grid, block, lds, stream);
+    if (p.kv_fp8) {
+        if (p.head_dim == 128) launch_balanced<128, true>(p, grid, block, lds, stream);
+        else launch_balanced<64, true>(p, grid, block, lds, stream);
+    } else {
+        if (p.head_dim == 128) launch_balanced<128, false>(p, grid, block, lds, stream);
+        else launch_balanced<64, false>(p, grid, block, lds, stream);
+    }
     return hipGetLastError();
 }
 

@@ -40,6 +40,9 @@ struct DecodeParams {
     int32_t ctx_cap;             // context lengths are clamped to [0, ctx_cap]
     int32_t out_bf16;            // 1: bf16 output, 0: f32 output
     int32_t cached_kv;           // 1: read K/V with cache-resident loads (blocks shared between sequences)
+    int32_t kv_fp8;              // 1: pools hold E4M3 codes (balanced path only)
+    const float* k_scale;        // fp8: [Hkv] K dequantisation scale
+    const float* v_scale;        // fp8: [Hkv] V dequantisation scale
     // partitioned path (fp32 KV): fixed partitions of part_blocks blocks,
     // partials laid out [B][P][Hq](×D), merged by the reduce kernel
     int32_t part_blocks;
@@ -116,6 +119,10 @@ const void* balanced_kernel(int32_t head_dim);
 hipError_t launch_decode_bf16_balanced(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeParams& p, bool bf16, hipStream_t stream);
 hipError_t launch_splitk_reduce(const DecodeParams& p, bool balanced, hipStream_t stream);
+hipError_t launch_cache_write_fp8(const void* k_new, const void* v_new, const int64_t* slot_mapping, void* k_cache,
+                                  void* v_cache, const float* k_scale, const float* v_scale, int64_t num_tokens,
+                                  int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks, bool src_bf16,
+                                  hipStream_t stream);
 hipError_t launch_cache_write(const void* k_new, const void* v_new, const int64_t* slot_mapping,
                               void* k_cache, void* v_cache, int64_t num_tokens, int32_t num_kv_heads,
                               int32_t head_dim, int64_t num_blocks, bool bf16, hipStream_t stream);

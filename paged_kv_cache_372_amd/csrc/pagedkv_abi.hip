@@ -27,6 +27,7 @@ pkv_status from_hip(hipError_t e, const char* what) {
 }
 
 bool dtype_ok(pkv_dtype d) { return d == PKV_F32 || d == PKV_BF16; }
+bool kv_dtype_ok(pkv_dtype d) { return d == PKV_F32 || d == PKV_BF16 || d == PKV_FP8_E4M3; }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -85,7 +86,7 @@ pkv_status make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads
                     num_kv_heads);
     if (head_dim != 64 && head_dim != 128) return fail(PKV_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", head_dim);
     if (block_size != pkv::kBlockSize) return fail(PKV_ERR_UNSUPPORTED, "block_size %d (supported: 16)", block_size);
-    if (!dtype_ok(kv_dtype)) return fail(PKV_ERR_UNSUPPORTED, "unknown KV dtype");
+    if (!kv_dtype_ok(kv_dtype)) return fail(PKV_ERR_UNSUPPORTED, "unknown KV dtype");
     if (max_blocks_per_seq < 0 || max_context_len < 0)
         return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq and max_context_len must be >= 0");
     if (partition_size != 0 &&
@@ -96,7 +97,7 @@ pkv_status make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads
     const int64_t by_table = (int64_t)max_blocks_per_seq * block_size;
     pl->ctx_cap = (int32_t)(max_context_len < by_table ? max_context_len : by_table);
     pl->group = num_q_heads / num_kv_heads;
-    pl->balanced = kv_dtype == PKV_BF16;
+    pl->balanced = kv_dtype != PKV_F32;  // bf16 and fp8 caches
     const int32_t heads_per_wave = pl->balanced ? pkv::kMfmaHeadsPerUnit : pkv::kValuHeadsPerUnit;
     pl->n_head_groups = (int32_t)ceil_div(pl->group, heads_per_wave);
     if (!pl->balanced) {
@@ -153,7 +154,8 @@ pkv_status prepare(const void* q, const void* k_cache, const void* v_cache, cons
                    const int32_t* context_lens, float scale, void* out, int32_t num_seqs, int32_t num_q_heads,
                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
                    int32_t max_blocks_per_seq, int32_t max_context_len, int32_t partition_size, void* workspace,
-                   size_t workspace_bytes, pkv_dtype kv_dtype, pkv_dtype out_dtype, uint32_t flags, Call* c) {
+                   size_t workspace_bytes, pkv_dtype kv_dtype, pkv_dtype out_dtype, uint32_t flags,
+                   const float* k_scale, const float* v_scale, Call* c) {
     pkv_status st = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                               max_context_len, partition_size, kv_dtype, &c->plan);
     if (st != PKV_OK) return st;
@@ -192,6 +194,9 @@ pkv_status prepare(const void* q, const void* k_cache, const void* v_cache, cons
     p.ctx_cap = pl.ctx_cap;
     p.out_bf16 = out_dtype == PKV_BF16;
     p.cached_kv = (flags & PKV_DECODE_SHARED_BLOCKS) ? 1 : 0;
+    p.kv_fp8 = kv_dtype == PKV_FP8_E4M3;
+    p.k_scale = k_scale;
+    p.v_scale = v_scale;
     float* ws = static_cast<float*>(workspace);
     if (pl.balanced) {
         p.walkers = pl.walkers;
@@ -209,7 +214,7 @@ pkv_status prepare(const void* q, const void* k_cache, const void* v_cache, cons
         p.l_part = pl.workspace ? ws + rows * (head_dim + 1) : nullptr;
     }
     c->kv_dtype = kv_dtype;
-    c->q_row_bytes = (size_t)num_q_heads * head_dim * (kv_dtype == PKV_BF16 ? 2 : 4);
+    c->q_row_bytes = (size_t)num_q_heads * head_dim * (kv_dtype == PKV_F32 ? 4 : 2);  // q is bf16 for fp8 caches
     c->out_row_bytes = (size_t)num_q_heads * head_dim * (out_dtype == PKV_BF16 ? 2 : 4);
     c->workspace = static_cast<char*>(workspace);
     return PKV_OK;
@@ -262,7 +267,7 @@ pkv_status run_reduce_kernels(const Call& c, hipStream_t stream) {
 
 extern "C" {
 
-int32_t pkv_abi_version(void) { return 3; }
+int32_t pkv_abi_version(void) { return 4; }
 
 const char* pkv_status_string(pkv_status status) {
     switch (status) {
@@ -316,10 +321,13 @@ pkv_status pkv_paged_attention_decode_partitions(const void* q, const void* k_ca
                                                  pkv_dtype kv_dtype, pkv_dtype out_dtype, uint32_t flags,
                                                  void* stream) {
     g_last_error[0] = 0;
+    if (kv_dtype == PKV_FP8_E4M3)
+        return fail(PKV_ERR_UNSUPPORTED, "an fp8 cache needs its scales: use pkv_paged_attention_decode_fp8");
     Call c;
     pkv_status st = prepare(q, k_cache, v_cache, block_tables, context_lens, scale, out, num_seqs, num_q_heads,
                             num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len,
-                            partition_size, workspace, workspace_bytes, kv_dtype, out_dtype, flags, &c);
+                            partition_size, workspace, workspace_bytes, kv_dtype, out_dtype, flags, nullptr, nullptr,
+                            &c);
     if (st != PKV_OK) return st;
     return run_decode_kernels(c, static_cast<hipStream_t>(stream));
 }
@@ -336,7 +344,7 @@ pkv_status pkv_paged_attention_decode_reduce(const int32_t* context_lens, void* 
     const void* unused = context_lens;
     pkv_status st = prepare(unused, unused, unused, context_lens, context_lens, 1.0f, out, num_seqs, num_q_heads,
                             num_kv_heads, head_dim, block_size, 1, max_blocks_per_seq, max_context_len,
-                            partition_size, workspace, workspace_bytes, kv_dtype, out_dtype, 0, &c);
+                            partition_size, workspace, workspace_bytes, kv_dtype, out_dtype, 0, nullptr, nullptr, &c);
     if (st != PKV_OK) return st;
     return run_reduce_kernels(c, static_cast<hipStream_t>(stream));
 }
@@ -349,15 +357,83 @@ pkv_status pkv_paged_attention_decode(const void* q, const void* k_cache, const 
                                       size_t workspace_bytes, pkv_dtype kv_dtype, pkv_dtype out_dtype, uint32_t flags,
                                       void* stream) {
     g_last_error[0] = 0;
+    if (kv_dtype == PKV_FP8_E4M3)
+        return fail(PKV_ERR_UNSUPPORTED, "an fp8 cache needs its scales: use pkv_paged_attention_decode_fp8");
     Call c;
     pkv_status st = prepare(q, k_cache, v_cache, block_tables, context_lens, scale, out, num_seqs, num_q_heads,
                             num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len,
-                            partition_size, workspace, workspace_bytes, kv_dtype, out_dtype, flags, &c);
+                            partition_size, workspace, workspace_bytes, kv_dtype, out_dtype, flags, nullptr, nullptr,
+                            &c);
     if (st != PKV_OK) return st;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     st = run_decode_kernels(c, s);
     if (st != PKV_OK) return st;
     return run_reduce_kernels(c, s);
+}
+
+pkv_status pkv_reshape_and_cache_fp8(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                                     void* k_cache, void* v_cache, const float* k_scale, const float* v_scale,
+                                     int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                     int64_t num_blocks, pkv_dtype src_dtype, void* stream) {
+    g_last_error[0] = 0;
+    if (num_tokens < 0) return fail(PKV_ERR_INVALID_ARG, "num_tokens must be >= 0");
+    if (num_kv_heads <= 0) return fail(PKV_ERR_INVALID_ARG, "num_kv_heads must be positive");
+    if (head_dim != 64 && head_dim != 128) return fail(PKV_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", head_dim);
+    if (block_size != pkv::kBlockSize) return fail(PKV_ERR_UNSUPPORTED, "block_size %d (supported: 16)", block_size);
+    if (!dtype_ok(src_dtype)) return fail(PKV_ERR_UNSUPPORTED, "input rows must be f32 or bf16");
+    if (num_blocks <= 0) return fail(PKV_ERR_INVALID_ARG, "num_blocks must be positive");
+    if (num_tokens == 0) return PKV_OK;
+    if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache || !k_scale || !v_scale)
+        return fail(PKV_ERR_INVALID_ARG, "null pointer");
+    if (((uintptr_t)k_new | (uintptr_t)v_new | (uintptr_t)k_cache) % 16)
+        return fail(PKV_ERR_INVALID_ARG, "k_new, v_new and k_cache must be 16-byte aligned");
+    return from_hip(pkv::launch_cache_write_fp8(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale,
+                                                num_tokens, num_kv_heads, head_dim, num_blocks, src_dtype == PKV_BF16,
+                                                static_cast<hipStream_t>(stream)),
+                    "reshape_and_cache_fp8 launch");
+}
+
+pkv_status pkv_paged_attention_decode_fp8(const void* q, const void* k_cache, const void* v_cache,
+                                          const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                                          const int32_t* context_lens, float scale, void* out, int32_t num_seqs,
+                                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                          int32_t block_size, int64_t num_blocks, int32_t max_blocks_per_seq,
+                                          int32_t max_context_len, int32_t partition_size, void* workspace,
+                                          size_t workspace_bytes, pkv_dtype out_dtype, uint32_t flags, void* stream) {
+    g_last_error[0] = 0;
+    if (num_seqs > 0 && (!k_scale || !v_scale))
+        return fail(PKV_ERR_INVALID_ARG, "an fp8 cache needs k_scale and v_scale");
+    Call c;
+    pkv_status st = prepare(q, k_cache, v_cache, block_tables, context_lens, scale, out, num_seqs, num_q_heads,
+                            num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len,
+                            partition_size, workspace, workspace_bytes, PKV_FP8_E4M3, out_dtype, flags, k_scale,
+                            v_scale, &c);
+    if (st != PKV_OK) return st;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    st = run_decode_kernels(c, s);
+    if (st != PKV_OK) return st;
+    return run_reduce_kernels(c, s);
+}
+
+pkv_status pkv_paged_attention_decode_partitions_fp8(const void* q, const void* k_cache, const void* v_cache,
+                                                     const float* k_scale, const float* v_scale,
+                                                     const int32_t* block_tables, const int32_t* context_lens,
+                                                     float scale, void* out, int32_t num_seqs, int32_t num_q_heads,
+                                                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                                     int64_t num_blocks, int32_t max_blocks_per_seq,
+                                                     int32_t max_context_len, int32_t partition_size,
+                                                     void* workspace, size_t workspace_bytes, pkv_dtype out_dtype,
+                                                     uint32_t flags, void* stream) {
+    g_last_error[0] = 0;
+    if (num_seqs > 0 && (!k_scale || !v_scale))
+        return fail(PKV_ERR_INVALID_ARG, "an fp8 cache needs k_scale and v_scale");
+    Call c;
+    pkv_status st = prepare(q, k_cache, v_cache, block_tables, context_lens, scale, out, num_seqs, num_q_heads,
+                            num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len,
+                            partition_size, workspace, workspace_bytes, PKV_FP8_E4M3, out_dtype, flags, k_scale,
+                            v_scale, &c);
+    if (st != PKV_OK) return st;
+    return run_decode_kernels(c, static_cast<hipStream_t>(stream));
 }
 
 pkv_status pkv_paged_attention_prefill(const void* q, const void* k_cache, const void* v_cache,

@@ -22,7 +22,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
 BLOCK_SIZE = 16
 
-PKV_F32, PKV_BF16 = 0, 1
+PKV_F32, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
+FP8_POOL_DTYPES = (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8))
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace", 4: "HIP error"}
 
 _lib = None
@@ -42,6 +43,12 @@ _SIGNATURES = {
                                                      _i64, _i32, _i32, _i32, _vp, _sz, _i32, _i32, _u32, _vp]),
     "pkv_paged_attention_decode_reduce": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _sz,
                                                  _i32, _i32, _vp]),
+    "pkv_reshape_and_cache_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _i32, _vp]),
+    "pkv_paged_attention_decode_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _i32, _i32, _i32, _i32, _i32,
+                                              _i64, _i32, _i32, _i32, _vp, _sz, _i32, _u32, _vp]),
+    "pkv_paged_attention_decode_partitions_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _i32, _i32,
+                                                         _i32, _i32, _i32, _i64, _i32, _i32, _i32, _vp, _sz, _i32,
+                                                         _u32, _vp]),
     "pkv_paged_attention_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                            _i64, _i32, _i32, _i32, _i32, _vp]),
     "pkv_status_string": (ctypes.c_char_p, [_i32]),
@@ -139,7 +146,7 @@ def reshape_and_cache(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: to
 def decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
                            max_context_len: int, partition_size: int = 0, kv_dtype: torch.dtype = torch.bfloat16) -> int:
     """Workspace bytes a decode of these sizes needs on the current device."""
-    code = PKV_BF16 if kv_dtype == torch.bfloat16 else PKV_F32
+    code = PKV_BF16 if kv_dtype == torch.bfloat16 else (PKV_FP8_E4M3 if kv_dtype in FP8_POOL_DTYPES else PKV_F32)
     return int(load_library().pkv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                                          max_context_len, partition_size, code))
 
@@ -148,15 +155,21 @@ class _DecodeArgs:
     """Validated decode arguments, reused by the one-call and two-phase entry points."""
 
     def __init__(self, q, k_cache, v_cache, block_tables, context_lens, scale, out, partition_size,
-                 max_context_len, workspace, shared_blocks=False):
+                 max_context_len, workspace, shared_blocks=False, k_scale=None, v_scale=None):
         dev = q.device
+        self.fp8 = k_cache.dtype in FP8_POOL_DTYPES
         for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (block_tables, "block_tables"),
                      (context_lens, "context_lens"), (out, "out")):
             _check_tensor(t, n, dev)
         nb, hkv, D = _pool_dims(k_cache, v_cache)
         _require(q.dim() == 3 and q.shape[2] == D, f"q must be [B, Hq, {D}]")
         B, hq = q.shape[0], q.shape[1]
-        _require(q.dtype == k_cache.dtype, "q dtype must match the pools")
+        if self.fp8:
+            _require(q.dtype == torch.bfloat16, "q must be bf16 over an fp8 cache")
+            _require(k_scale is not None and v_scale is not None, "an fp8 cache needs k_scale and v_scale")
+            _check_scales(k_scale, v_scale, hkv, dev)
+        else:
+            _require(q.dtype == k_cache.dtype, "q dtype must match the pools")
         _require(tuple(out.shape) == tuple(q.shape), "out must have q's shape")
         _require(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and block_tables.shape[0] == B,
                  "block_tables must be int32 [B, max_blocks_per_seq]")
@@ -174,13 +187,20 @@ class _DecodeArgs:
         self.workspace = workspace
         self.ws_ptr = _ptr(workspace) if workspace is not None else None
         self.ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-        self.args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), float(scale),
-                     _ptr(out), B, hq, hkv, D, BLOCK_SIZE, nb, block_tables.shape[1], self.max_context_len,
-                     self.partition_size, self.ws_ptr, self.ws_bytes, _dtype_code(k_cache), _dtype_code(out),
-                     DECODE_SHARED_BLOCKS if shared_blocks else 0, _stream(dev))
+        flags = DECODE_SHARED_BLOCKS if shared_blocks else 0
+        if self.fp8:
+            self.args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
+                         _ptr(context_lens), float(scale), _ptr(out), B, hq, hkv, D, BLOCK_SIZE, nb,
+                         block_tables.shape[1], self.max_context_len, self.partition_size, self.ws_ptr,
+                         self.ws_bytes, _dtype_code(out), flags, _stream(dev))
+        else:
+            self.args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+                         float(scale), _ptr(out), B, hq, hkv, D, BLOCK_SIZE, nb, block_tables.shape[1],
+                         self.max_context_len, self.partition_size, self.ws_ptr, self.ws_bytes,
+                         _dtype_code(k_cache), _dtype_code(out), flags, _stream(dev))
         self.reduce_args = (_ptr(context_lens), _ptr(out), B, hq, hkv, D, BLOCK_SIZE, block_tables.shape[1],
                             self.max_context_len, self.partition_size, self.ws_ptr, self.ws_bytes,
-                            _dtype_code(k_cache), _dtype_code(out), _stream(dev))
+                            PKV_FP8_E4M3 if self.fp8 else _dtype_code(k_cache), _dtype_code(out), _stream(dev))
 
 
 def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
@@ -201,18 +221,28 @@ def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
 
 
 def prepare_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out, *, partition_size=0,
-                   max_context_len=None, workspace=None, shared_blocks=False) -> _DecodeArgs:
-    """Validate once; the returned object drives ``run_partitions`` / ``run_reduce`` repeatedly."""
+                   max_context_len=None, workspace=None, shared_blocks=False, k_scale=None,
+                   v_scale=None) -> _DecodeArgs:
+    """Validate once; the returned object drives ``run_partitions`` / ``run_reduce`` repeatedly.
+    fp8 pools (uint8 / float8_e4m3fn) take ``k_scale`` / ``v_scale``."""
     return _DecodeArgs(q, k_cache, v_cache, block_tables, context_lens, scale, out, partition_size, max_context_len,
-                       workspace, shared_blocks)
+                       workspace, shared_blocks, k_scale, v_scale)
 
 
 def run_decode(a: _DecodeArgs) -> None:
-    _check(load_library().pkv_paged_attention_decode(*a.args), "paged_attention_decode")
+    lib = load_library()
+    if a.fp8:
+        _check(lib.pkv_paged_attention_decode_fp8(*a.args), "paged_attention_decode_fp8")
+    else:
+        _check(lib.pkv_paged_attention_decode(*a.args), "paged_attention_decode")
 
 
 def run_partitions(a: _DecodeArgs) -> None:
-    _check(load_library().pkv_paged_attention_decode_partitions(*a.args), "paged_attention_decode_partitions")
+    lib = load_library()
+    if a.fp8:
+        _check(lib.pkv_paged_attention_decode_partitions_fp8(*a.args), "paged_attention_decode_partitions_fp8")
+    else:
+        _check(lib.pkv_paged_attention_decode_partitions(*a.args), "paged_attention_decode_partitions")
 
 
 def run_reduce(a: _DecodeArgs) -> None:
@@ -251,3 +281,66 @@ def paged_attention_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: tor
                                          hq, hkv, D, BLOCK_SIZE, nb, block_tables.shape[1], int(max_context_len),
                                          _dtype_code(k_cache), _dtype_code(out), _stream(dev))
     _check(st, "paged_attention_prefill")
+
+
+def _check_scales(k_scale: torch.Tensor, v_scale: torch.Tensor, hkv: int, device) -> None:
+    for t, n in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+        _check_tensor(t, n, device)
+        _require(t.dtype == torch.float32 and tuple(t.shape) == (hkv,), f"{n} must be float32 [{hkv}]")
+
+
+def reshape_and_cache_fp8(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
+                          k_cache: torch.Tensor, v_cache: torch.Tensor, k_scale: torch.Tensor,
+                          v_scale: torch.Tensor) -> None:
+    """Quantise k_new/v_new ``[T, Hkv, D]`` (f32 or bf16) into fp8 (E4M3) pools with per-KV-head scales."""
+    lib = load_library()
+    dev = k_cache.device
+    for t, n in ((k_new, "k_new"), (v_new, "v_new"), (slot_mapping, "slot_mapping"), (k_cache, "k_cache"),
+                 (v_cache, "v_cache")):
+        _check_tensor(t, n, dev)
+    _require(k_cache.dtype in FP8_POOL_DTYPES and v_cache.dtype == k_cache.dtype, "fp8 pools must be uint8 or float8_e4m3fn")
+    nb, hkv, D = _pool_dims(k_cache, v_cache)
+    _require(k_new.dim() == 3 and tuple(k_new.shape[1:]) == (hkv, D), f"k_new must be [T, {hkv}, {D}]")
+    _require(v_new.shape == k_new.shape and v_new.dtype == k_new.dtype, "v_new must match k_new")
+    _require(slot_mapping.dtype == torch.int64 and slot_mapping.shape == (k_new.shape[0],),
+             "slot_mapping must be int64 [T]")
+    _check_scales(k_scale, v_scale, hkv, dev)
+    st = lib.pkv_reshape_and_cache_fp8(_ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(k_cache), _ptr(v_cache),
+                                       _ptr(k_scale), _ptr(v_scale), k_new.shape[0], hkv, D, BLOCK_SIZE, nb,
+                                       _dtype_code(k_new), _stream(dev))
+    _check(st, "reshape_and_cache_fp8")
+
+
+def paged_attention_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, k_scale: torch.Tensor,
+                               v_scale: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+                               scale: float, out: torch.Tensor, *, partition_size: int = 0,
+                               max_context_len: Optional[int] = None, workspace: Optional[torch.Tensor] = None,
+                               shared_blocks: bool = False) -> None:
+    """Decode attention of bf16 ``q [B, Hq, D]`` over fp8 (E4M3) pools with per-KV-head scales."""
+    lib = load_library()
+    dev = q.device
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (block_tables, "block_tables"),
+                 (context_lens, "context_lens"), (out, "out")):
+        _check_tensor(t, n, dev)
+    _require(k_cache.dtype in FP8_POOL_DTYPES and v_cache.dtype == k_cache.dtype, "fp8 pools must be uint8 or float8_e4m3fn")
+    nb, hkv, D = _pool_dims(k_cache, v_cache)
+    _require(q.dim() == 3 and q.shape[2] == D and q.dtype == torch.bfloat16, f"q must be bf16 [B, Hq, {D}]")
+    B, hq = q.shape[0], q.shape[1]
+    _require(tuple(out.shape) == tuple(q.shape), "out must have q's shape")
+    _require(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and block_tables.shape[0] == B,
+             "block_tables must be int32 [B, max_blocks_per_seq]")
+    _require(context_lens.dtype == torch.int32 and tuple(context_lens.shape) == (B,), "context_lens must be int32 [B]")
+    _check_scales(k_scale, v_scale, hkv, dev)
+    if max_context_len is None:
+        max_context_len = int(context_lens.max().item()) if B else 0
+    need = decode_workspace_bytes(B, hq, hkv, D, int(max_context_len), int(partition_size), torch.uint8)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_ptr = _ptr(workspace) if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.pkv_paged_attention_decode_fp8(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                                            _ptr(block_tables), _ptr(context_lens), float(scale), _ptr(out), B, hq,
+                                            hkv, D, BLOCK_SIZE, nb, block_tables.shape[1], int(max_context_len),
+                                            int(partition_size), ws_ptr, ws_bytes, _dtype_code(out),
+                                            DECODE_SHARED_BLOCKS if shared_blocks else 0, _stream(dev))
+    _check(st, "paged_attention_decode_fp8")

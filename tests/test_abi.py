@@ -51,7 +51,7 @@ def test_single_hip_runtime_in_process(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pkv_abi_version() == 3
+    assert lib.pkv_abi_version() == 4
     for code in range(5):
         assert lib.pkv_status_string(code)
     assert lib.pkv_status_string(99) == b"unknown status"
@@ -141,6 +141,37 @@ def test_prefill_validation(lib):
     assert pre(lib, T=0, q=None, kc=None, vc=None, bt=None, lens=None, qsl=None, out=None) == OK
     assert pre(lib, B=0, q=None) == OK
     assert lib.pkv_last_error() == b""
+
+
+def test_fp8_validation(lib):
+    FP8 = 2
+    # the plain decode entry points need the scales of an fp8 cache
+    assert dec(lib, kvd=FP8) == UNSUPPORTED
+    assert b"fp8" in lib.pkv_last_error()
+    a = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, 4, 32, 8, 128, 16, 100, 128, 2000, 0, FAKE, 0, BF16, 0, None)
+    need = lib.pkv_decode_workspace_bytes(4, 32, 8, 128, 2000, 0, FP8)
+    assert need == lib.pkv_decode_workspace_bytes(4, 32, 8, 128, 2000, 0, BF16) > 0
+    no_scale = list(a)
+    no_scale[3] = None
+    assert lib.pkv_paged_attention_decode_fp8(*no_scale) == INVALID
+    assert lib.pkv_paged_attention_decode_fp8(*a) == WORKSPACE          # workspace of 0 bytes
+    assert lib.pkv_paged_attention_decode_partitions_fp8(*a) == WORKSPACE
+    # quantising cache write: inputs must be f32 or bf16, scales given
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 128, 16, 10, BF16, None]
+    bad = list(args)
+    bad[12] = FP8
+    assert lib.pkv_reshape_and_cache_fp8(*bad) == UNSUPPORTED
+    bad = list(args)
+    bad[5] = None
+    assert lib.pkv_reshape_and_cache_fp8(*bad) == INVALID
+    bad = list(args)
+    bad[9] = 96
+    assert lib.pkv_reshape_and_cache_fp8(*bad) == UNSUPPORTED
+    bad = list(args)
+    bad[7] = 0
+    assert lib.pkv_reshape_and_cache_fp8(*bad) == OK
+    # prefill over an fp8 cache is not offered
+    assert pre(lib, kvd=FP8) == UNSUPPORTED
 
 
 def _align(x, a=256):

@@ -69,7 +69,7 @@ _STREAMS = {"k_pool": 1, "v_pool": 2, "q": 3, "k_new": 4, "v_new": 5, "k_prompt"
 
 
 def element_size(dtype: str) -> int:
-    return {"f32": 4, "bf16": 2}[dtype]
+    return {"f32": 4, "bf16": 2, "fp8": 1}[dtype]
 
 
 def chunk_elems(dtype: str) -> int:
@@ -399,6 +399,48 @@ class ContinuousBatching:
         return BatchingStep(step=i, retired=retired, admitted=admitted, k_write=k_write, v_write=v_write,
                             slot_mapping=slots, q=q, block_tables=bt, context_lens=pack_context_lens(self.seqs),
                             num_prompt_tokens=n_prompt)
+
+
+# --------------------------------------------------------------------------
+# fp8 (E4M3) pools
+# --------------------------------------------------------------------------
+
+E4M3_NAN_CODE = np.uint8(0x7F)
+
+
+def random_e4m3_codes(n: int, seed: int, stream: int) -> np.ndarray:
+    """``n`` E4M3 codes: random sign, exponent field uniform on 4..8 (magnitudes
+    1/8 .. 3.75, the spread of N(0, 1) values), random mantissa.  A draw of
+    codes, not an encoding of values."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, stream, 77])))
+    sign = g.integers(0, 2, size=n, dtype=np.uint8) << 7
+    exp = g.integers(4, 9, size=n, dtype=np.uint8) << 3
+    mant = g.integers(0, 8, size=n, dtype=np.uint8)
+    return sign | exp | mant
+
+
+def fp8_variant(b, seed: Optional[int] = None, scale_range=(0.5, 2.0)):
+    """The same step over an fp8 cache: pools of random E4M3 codes (NaN code
+    0x7F wherever the bf16 batch holds no cached token), K/V scales per KV
+    head uniform on ``scale_range``, new rows kept in bf16 (the cache write
+    quantises them).  ``b`` is a bf16 DecodeBatch or PrefillBatch."""
+    import dataclasses
+    if b.dtype != "bf16":
+        raise ValueError("fp8 variants are built from bf16 batches")
+    seed = b.seed if seed is None else seed
+    NB, Hkv, D, bs = b.num_blocks, b.num_kv_heads, b.head_dim, b.block_size
+    cached = ~(b.v_pool[:, 0, 0, :] == BF16_NAN_BITS)              # [NB, bs]
+    kp = random_e4m3_codes(NB * Hkv * D * bs, seed, 11).reshape(NB, Hkv, D // 16, bs, 16)
+    vp = random_e4m3_codes(NB * Hkv * D * bs, seed, 12).reshape(NB, Hkv, D, bs)
+    blk, off = np.nonzero(~cached)
+    kp[blk, :, :, off, :] = E4M3_NAN_CODE
+    vp[blk, :, :, off] = E4M3_NAN_CODE
+    g = np.random.default_rng([seed, 13])
+    k_scale = g.uniform(*scale_range, size=Hkv).astype(np.float32)
+    v_scale = g.uniform(*scale_range, size=Hkv).astype(np.float32)
+    info = dict(b.info)
+    info.update(k_scale=k_scale, v_scale=v_scale, src_dtype="bf16")
+    return dataclasses.replace(b, name=b.name + "_fp8", dtype="fp8", k_pool=kp, v_pool=vp, info=info)
 
 
 # --------------------------------------------------------------------------
