@@ -16,6 +16,11 @@ This module owns that bookkeeping:
 * ``Sequence``      -- one sequence's logical-to-physical block list and token
                        count; ``append_slot`` allocates a block only when the
                        next token starts a new one (on-demand allocation).
+* ``Sequence.fork`` / ``Sequence.append_slot_cow`` -- sharing a prompt between
+                       forked sequences and the copy-on-write of a shared
+                       block one of them writes into.
+* ``swap_blocks``     -- the bookkeeping of moving a sequence's blocks to
+                       another pool (host memory) and back.
 * ``pack_block_tables`` / ``pack_context_lens`` -- pack the per-sequence
                        state into the int32 arrays the C-ABI consumes.
 * ``tables_share_blocks`` -- whether a packed batch points several sequences
@@ -28,7 +33,7 @@ from __future__ import annotations
 
 from collections import deque
 from dataclasses import dataclass, field
-from typing import Iterable, List, Optional, Sequence as Seq
+from typing import Iterable, List, Optional, Sequence as Seq, Tuple
 
 import numpy as np
 
@@ -134,6 +139,47 @@ class Sequence:
         pool.release(self.blocks)
         self.blocks = []
         self.num_tokens = 0
+
+    def fork(self, pool: BlockPool, seq_id: int) -> "Sequence":
+        """A new sequence sharing every block of this one (parallel sampling,
+        beam search: ai-hpc "2.2 Advantages", item 2)."""
+        pool.share(self.blocks)
+        return Sequence(seq_id, list(self.blocks), self.num_tokens)
+
+    def append_slot_cow(self, pool: BlockPool) -> Tuple[int, Optional[Tuple[int, int]]]:
+        """Reserve the next token's slot, copy-on-write.
+
+        If the token lands in a block that other sequences still own, this
+        sequence first moves to a private copy of that block.  Returns the
+        slot and the (source, destination) block copy that must run before
+        the token is written, or None.
+        """
+        bs = pool.block_size
+        copy = None
+        j = self.num_tokens // bs
+        if j < len(self.blocks) and pool.refcount[self.blocks[j]] > 1:
+            old = self.blocks[j]
+            new = pool.allocate(1)[0]
+            pool.release([old])
+            self.blocks[j] = new
+            copy = (old, new)
+        return self.append_slot(pool), copy
+
+
+def swap_blocks(seq: Sequence, from_pool: BlockPool, to_pool: BlockPool) -> List[Tuple[int, int]]:
+    """Move a sequence's blocks from one pool to another (device -> host to
+    preempt it, host -> device to resume it: architvora "Paged Attention").
+
+    Every block gets a fresh block in ``to_pool``; the sequence then refers
+    to the new blocks, and drops its ownership of the old ones (a block other
+    sequences still share stays where it is for them).  Returns the
+    (old block, new block) pairs the block copy must run, in table order.
+    """
+    new = to_pool.allocate(len(seq.blocks))
+    pairs = list(zip(seq.blocks, new))
+    from_pool.release(seq.blocks)
+    seq.blocks = list(new)
+    return pairs
 
 
 def blocks_needed(num_tokens: int, block_size: int) -> int:
