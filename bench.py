@@ -35,10 +35,17 @@ METRIC = "paged-attn decode: achieved KV-read HBM GB/s (% of peak) + decode toke
 PEAK_BF16_TFLOPS = 2500.0
 PREFILL_METRIC = "paged-attn chunked prefill: attention TFLOP/s (causal flops) + prefill tokens/s"
 PREFILL_CONFIGS = ("chunked_prefill",)
+COPY_CONFIGS = ("block_copy", "swap")
+PEAK_HOST_LINK_GBS = 64.0   # PCIe 5.0 x16, one direction
+COPY_METRIC = "whole-block KV copies: GB/s moved (copy-on-write in HBM: read + write; swap: over the host link)"
 
 
 def family(workload: str) -> str:
-    return "prefill" if workload in PREFILL_CONFIGS else "decode"
+    if workload in PREFILL_CONFIGS:
+        return "prefill"
+    if workload in COPY_CONFIGS:
+        return "copy"
+    return "decode"
 
 
 def traffic_file(workload: str) -> str:
@@ -46,7 +53,7 @@ def traffic_file(workload: str) -> str:
 
 
 def kernel_sources(workload: str):
-    main = "prefill_mfma.hip" if family(workload) == "prefill" else "decode_mfma.hip"
+    main = {"prefill": "prefill_mfma.hip", "copy": "copy_blocks.hip"}.get(family(workload), "decode_mfma.hip")
     return [os.path.join(ROOT, "paged_kv_cache_372_amd", "csrc", f) for f in (main, "kernels.h")]
 
 
@@ -198,6 +205,7 @@ def calibrate_copy(mib: int, reps: int):
 
 DECODE_KERNEL_PREFIX = "void pkv::(anonymous namespace)::decode_bf16_balanced_kernel"
 PREFILL_KERNEL_PREFIX = "void pkv::(anonymous namespace)::prefill_bf16_kernel"
+COPY_KERNEL_PREFIX = "pkv::(anonymous namespace)::copy_blocks_kernel"
 
 
 def _read_counter(dirpath: str, counter: str):
@@ -236,8 +244,9 @@ def summarize_profile(prefix: str, workload: str, partition_size, copy_mib: int,
     copy_name = "__amd_rocclr_copyBuffer"
     f_factor = copy_kib / cal_f[copy_name]
     w_factor = copy_kib / cal_w[copy_name]
-    prefix_k = PREFILL_KERNEL_PREFIX if family(workload) == "prefill" else DECODE_KERNEL_PREFIX
-    dec = [k for k in fetch if k.startswith(prefix_k)][0]
+    prefix_k = {"prefill": PREFILL_KERNEL_PREFIX, "copy": COPY_KERNEL_PREFIX}.get(family(workload), DECODE_KERNEL_PREFIX)
+    short_k = prefix_k.split("::")[-1]
+    dec = [k for k in fetch if short_k in k][0]
     lines = [f"# rocprofv3: decode kernels on the {workload} workload", "",
              "Commands (run from the repository root; `cd /tmp && export TMPDIR=/tmp` first):", "", "```",
              commands.strip(), "```", "", "## Kernel trace (`--kernel-trace --stats`)", "",
@@ -376,6 +385,103 @@ def run_prefill(args):
     print(json.dumps(rec), flush=True)
 
 
+def run_copy(args):
+    """Whole-block copies on the Llama-3-8B shape (8 KV heads x 128 dims,
+    bf16: 32 KiB per block per pool).  block_copy: 4096 copy-on-write pairs
+    inside a 16384-block device pool (random distinct blocks).  swap: 1024
+    blocks out to a pinned host pool, then back into other device blocks;
+    one step is the round trip."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_372_amd import ops
+    import oracle
+
+    rng = np.random.default_rng(3727)
+    hkv, D, nb = 8, 128, 16384
+    block_bytes = hkv * D * 16 * 2
+    kp = torch.randn((nb, hkv, D // 8, 16, 8), dtype=torch.bfloat16, device="cuda")
+    vp = torch.randn((nb, hkv, D, 16), dtype=torch.bfloat16, device="cuda")
+    perm = rng.permutation(nb)
+    if args.config == "block_copy":
+        n = 4096
+        pairs = torch.from_numpy(np.stack([perm[:n], perm[n:2 * n]], axis=1).astype(np.int64)).cuda()
+        moved = n * 2 * block_bytes                      # bytes copied (K and V)
+        hbm = 2 * moved                                  # read + write
+
+        def step(ev=None):
+            if ev is not None:
+                ev[0].record()
+            ops.copy_blocks(kp, vp, pairs)
+            if ev is not None:
+                ev[1].record()
+        launches = 1
+    else:
+        n = 1024
+        hk = torch.empty((n,) + tuple(kp.shape[1:]), dtype=kp.dtype).pin_memory()
+        hv = torch.empty((n,) + tuple(vp.shape[1:]), dtype=vp.dtype).pin_memory()
+        out_pairs = torch.from_numpy(np.stack([perm[:n], np.arange(n)], axis=1).astype(np.int64)).cuda()
+        in_pairs = torch.from_numpy(np.stack([np.arange(n), perm[n:2 * n]], axis=1).astype(np.int64)).cuda()
+        moved = 2 * n * 2 * block_bytes                  # out and back, K and V
+        hbm = moved
+
+        def step(ev=None):
+            if ev is not None:
+                ev[0].record()
+            ops.swap_blocks(kp, vp, hk, hv, out_pairs)
+            ops.swap_blocks(hk, hv, kp, vp, in_pairs)
+            if ev is not None:
+                ev[1].record()
+        launches = 2
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    k_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    ms = wall / args.steps * 1e3
+    value = moved / (ms / 1e3) / 1e9
+    if args.config == "block_copy":
+        roof = {"bound": "hbm", "achieved": round(hbm / (k_ms / 1e3) / 1e9, 2), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(hbm / (k_ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+                "traffic": measured_traffic(args.config, "none"), "kernel": "copy_blocks_kernel",
+                "bytes_per_launch": hbm}
+    else:
+        per_dir = moved / 2 / (k_ms / 2 / 1e3) / 1e9
+        roof = {"bound": "host-link", "achieved": round(per_dir, 2), "peak": PEAK_HOST_LINK_GBS, "unit": "GB/s",
+                "frac": round(per_dir / PEAK_HOST_LINK_GBS, 4), "traffic": None, "kernel": "copy_blocks_kernel",
+                "bytes_per_launch": moved // 2}
+    rec = {"metric": COPY_METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": args.config, "pairs_per_launch": n, "launches_per_step": launches,
+                      "num_kv_heads": hkv, "head_dim": D, "block_bytes_per_pool": block_bytes,
+                      "bytes_copied_per_step": moved},
+           "kernel_ms": round(k_ms, 5), "roofline": roof}
+    if not args.no_cpu_baseline:
+        ks = (64, hkv, D // 8, 16, 8)
+        vs = (64, hkv, D, 16)
+        hk0 = rng.integers(0, 65535, size=ks, dtype=np.uint16)
+        hv0 = rng.integers(0, 65535, size=vs, dtype=np.uint16)
+        p = np.stack([np.arange(32), np.arange(32, 64)], axis=1)
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < min(args.cpu_budget, 3.0):
+            oracle.ref_copy_blocks(hk0, hv0, hk0, hv0, p)
+            reps += 1
+        dt = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": round(reps * 32 * 2 * block_bytes / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
+                               "kind": "oracle", "sample": f"{reps} oracle calls of 32 block copies in a 64-block "
+                                                           f"pool ({dt:.1f} s, numpy, one thread)"}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -396,7 +502,7 @@ def main():
 
     if args.summarize_profile:
         ps = args.partition_size if args.partition_size > 0 else "balanced"
-        if family(args.config) == "prefill":
+        if family(args.config) != "decode":
             ps = "none"
         summarize_profile(args.summarize_profile, args.config, ps, args.profile_copy_mib,
                           os.path.join(ROOT, "profiles", f"{family(args.config)}_{args.config}.md"),
@@ -423,6 +529,9 @@ def main():
 
     if family(args.config) == "prefill":
         run_prefill(args)
+        return
+    if family(args.config) == "copy":
+        run_copy(args)
         return
 
     t_gen = time.perf_counter()

@@ -247,6 +247,33 @@ pkv_status pkv_paged_attention_decode_partitions_fp8(const void* q, const void* 
                                                      uint32_t flags, void* stream);
 
 /*
+ * Whole-block copies between KV pools: copy-on-write and swapping.
+ * Sequences forked from one prompt (parallel sampling, beam search) share its
+ * physical blocks copy-on-write ("Deep Dive into vLLM", 2.2 "Advantages"): a
+ * shared block is copied to a fresh one when an owner writes into it.  A
+ * preempted sequence's blocks can be moved to CPU memory and back (architvora,
+ * "Paged Attention").  Both copy, for each pair (src, dst) in `pairs`, the
+ * whole block src of the source pools into block dst of the destination
+ * pools: every KV head and token slot of K and of V, bit for bit.
+ *
+ *   src_k, src_v   source pools (layout above, num_src_blocks blocks)
+ *   dst_k, dst_v   destination pools (num_dst_blocks blocks); the same
+ *                  pointers as src_* for copy-on-write inside one pool
+ *   pairs          int64 [num_pairs][2] (src block, dst block)
+ * Pools and `pairs` may live in device memory or in pinned host memory that
+ * the device can access (hipHostMalloc / torch pin_memory): the kernel reads
+ * and writes them directly, one launch for all pairs.  Each pointer is looked
+ * up first; anything else (pageable host memory) returns PKV_ERR_INVALID_ARG
+ * before any launch.  A pair with an id
+ * outside its pool is skipped.  Destinations must be distinct, and inside
+ * one pool no destination may also be a source (the order of copies is
+ * unspecified).  dtype: PKV_F32, PKV_BF16 or PKV_FP8_E4M3 (the element size).
+ */
+pkv_status pkv_copy_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v, const int64_t* pairs,
+                           int64_t num_pairs, int64_t num_src_blocks, int64_t num_dst_blocks, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size, pkv_dtype dtype, void* stream);
+
+/*
  * Multi-token-query paged attention (chunked prefill).  Prefill processes a
  * whole prompt at once and is compute-bound (runbyai section 1); long
  * prompts are cut into chunks that share each step with decode requests,

@@ -1,0 +1,75 @@
+// Whole-block copies between KV pools: copy-on-write and swapping.
+//
+// Sequences forked from one prompt share its physical blocks, the way an
+// operating system shares pages copy-on-write; a shared block is copied when
+// one of its owners writes into it ("Deep Dive into vLLM", 2.2 "Advantages",
+// item 2).  A preempted sequence's blocks can be moved to CPU memory and back
+// (architvora, "Paged Attention").  Both are the same operation: for every
+// (source, destination) pair, copy the whole block -- every KV head and
+// token slot, K and V -- from one pool to another (or the same) pool, bit
+// for bit.  A pool in pinned host memory is read or written by the kernel
+// directly, so one launch moves any number of blocks.
+//
+// A (block, pool) is Hkv * D * 16 elements, one contiguous run (32 KiB for
+// 8 heads x 128 dims of bf16).  One workgroup of 256 threads copies up to
+// 32 KiB of one pair and one pool with 16-byte non-temporal loads and
+// stores: the data is not read again by this kernel, and a copy should not
+// displace the blocks decode is about to read.
+#include "kernels.h"
+
+namespace pkv {
+namespace {
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 8;                          // 16-byte units per thread per workgroup
+constexpr int kUnitsPerGroup = kThreads * kUnroll;  // 2048 units = 32 KiB
+
+// Source and destination may be the same pool (copy-on-write), so the
+// pointers carry no restrict qualifier.
+__global__ __launch_bounds__(kThreads) void copy_blocks_kernel(const uint4* src_k, const uint4* src_v, uint4* dst_k,
+                                                               uint4* dst_v, const int64_t* __restrict__ pairs,
+                                                               int64_t num_src, int64_t num_dst, int units,
+                                                               int chunks) {
+    const int64_t pair = blockIdx.x / (2 * chunks);
+    const int rem = (int)(blockIdx.x - pair * 2 * chunks);
+    const int pool = rem / chunks;
+    const int chunk = rem - pool * chunks;
+    const int64_t s = pairs[2 * pair];
+    const int64_t d = pairs[2 * pair + 1];
+    if (s < 0 || s >= num_src || d < 0 || d >= num_dst) return;  // skipped by contract
+    const uint4* src = (pool ? src_v : src_k) + s * units;
+    uint4* dst = (pool ? dst_v : dst_k) + d * units;
+    const int u0 = chunk * kUnitsPerGroup + (int)threadIdx.x;
+    uint4 r[kUnroll];
+#pragma unroll
+    for (int i = 0; i < kUnroll; ++i) {
+        const int u = u0 + i * kThreads;
+        if (u < units) r[i] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(
+                                                            reinterpret_cast<const u32x4_t*>(src) + u));
+    }
+#pragma unroll
+    for (int i = 0; i < kUnroll; ++i) {
+        const int u = u0 + i * kThreads;
+        if (u < units) __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, r[i]),
+                                                   reinterpret_cast<u32x4_t*>(dst) + u);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_copy_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v, const int64_t* pairs,
+                              int64_t num_pairs, int64_t num_src_blocks, int64_t num_dst_blocks,
+                              int64_t block_bytes, hipStream_t stream) {
+    if (num_pairs == 0) return hipSuccess;
+    const int units = (int)(block_bytes / 16);
+    const int chunks = (units + kUnitsPerGroup - 1) / kUnitsPerGroup;
+    const dim3 grid((unsigned)(num_pairs * 2 * chunks)), block(kThreads);
+    hipLaunchKernelGGL(copy_blocks_kernel, grid, block, 0, stream, static_cast<const uint4*>(src_k),
+                       static_cast<const uint4*>(src_v), static_cast<uint4*>(dst_k), static_cast<uint4*>(dst_v),
+                       pairs, num_src_blocks, num_dst_blocks, units, chunks);
+    return hipGetLastError();
+}
+
+}  // namespace pkv

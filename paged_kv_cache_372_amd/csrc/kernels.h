@@ -119,6 +119,9 @@ const void* balanced_kernel(int32_t head_dim);
 hipError_t launch_decode_bf16_balanced(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeParams& p, bool bf16, hipStream_t stream);
 hipError_t launch_splitk_reduce(const DecodeParams& p, bool balanced, hipStream_t stream);
+hipError_t launch_copy_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v, const int64_t* pairs,
+                              int64_t num_pairs, int64_t num_src_blocks, int64_t num_dst_blocks,
+                              int64_t block_bytes, hipStream_t stream);
 hipError_t launch_cache_write_fp8(const void* k_new, const void* v_new, const int64_t* slot_mapping, void* k_cache,
                                   void* v_cache, const float* k_scale, const float* v_scale, int64_t num_tokens,
                                   int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks, bool src_bf16,

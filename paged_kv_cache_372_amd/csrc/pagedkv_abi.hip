@@ -436,6 +436,64 @@ pkv_status pkv_paged_attention_decode_partitions_fp8(const void* q, const void* 
     return run_decode_kernels(c, static_cast<hipStream_t>(stream));
 }
 
+// The address a kernel uses for `p`: device memory as it is; pinned host
+// memory through its device mapping.  Anything else (pageable host memory,
+// an unknown pointer) is refused before launch, because a kernel touching
+// it would fault.
+pkv_status device_view(const void* p, const char* what, const void** out) {
+    hipPointerAttribute_t a;
+    memset(&a, 0, sizeof(a));
+    const hipError_t e = hipPointerGetAttributes(&a, p);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(PKV_ERR_INVALID_ARG, "%s is neither device memory nor pinned host memory", what);
+    }
+    if (a.type == hipMemoryTypeDevice || a.type == hipMemoryTypeManaged) {
+        *out = p;
+        return PKV_OK;
+    }
+    if (a.type == hipMemoryTypeHost && a.devicePointer) {
+        // the attributes may describe the allocation's start: keep p's offset
+        const ptrdiff_t off = a.hostPointer ? static_cast<const char*>(p) - static_cast<const char*>(a.hostPointer) : 0;
+        *out = static_cast<const char*>(a.devicePointer) + off;
+        return PKV_OK;
+    }
+    return fail(PKV_ERR_INVALID_ARG, "%s is neither device memory nor pinned host memory", what);
+}
+
+pkv_status pkv_copy_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v, const int64_t* pairs,
+                           int64_t num_pairs, int64_t num_src_blocks, int64_t num_dst_blocks, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size, pkv_dtype dtype, void* stream) {
+    g_last_error[0] = 0;
+    if (num_pairs < 0) return fail(PKV_ERR_INVALID_ARG, "num_pairs must be >= 0");
+    if (num_kv_heads <= 0) return fail(PKV_ERR_INVALID_ARG, "num_kv_heads must be positive");
+    if (head_dim != 64 && head_dim != 128) return fail(PKV_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", head_dim);
+    if (block_size != pkv::kBlockSize) return fail(PKV_ERR_UNSUPPORTED, "block_size %d (supported: 16)", block_size);
+    if (!kv_dtype_ok(dtype)) return fail(PKV_ERR_UNSUPPORTED, "unknown dtype");
+    if (num_src_blocks <= 0 || num_dst_blocks <= 0) return fail(PKV_ERR_INVALID_ARG, "pool sizes must be positive");
+    if (num_pairs == 0) return PKV_OK;
+    if (!src_k || !src_v || !dst_k || !dst_v || !pairs) return fail(PKV_ERR_INVALID_ARG, "null pointer");
+    if (((uintptr_t)src_k | (uintptr_t)src_v | (uintptr_t)dst_k | (uintptr_t)dst_v) % 16)
+        return fail(PKV_ERR_INVALID_ARG, "pools must be 16-byte aligned");
+    const void* views[5];
+    const void* ptrs[5] = {src_k, src_v, dst_k, dst_v, pairs};
+    const char* names[5] = {"src_k", "src_v", "dst_k", "dst_v", "pairs"};
+    for (int i = 0; i < 5; ++i) {
+        pkv_status st = device_view(ptrs[i], names[i], &views[i]);
+        if (st != PKV_OK) return st;
+    }
+    const int64_t es = dtype == PKV_F32 ? 4 : (dtype == PKV_BF16 ? 2 : 1);
+    const int64_t block_bytes = (int64_t)num_kv_heads * head_dim * block_size * es;
+    const int64_t chunks = ceil_div(block_bytes / 16, 2048);
+    if (num_pairs * 2 * chunks >= ((int64_t)1 << 31))
+        return fail(PKV_ERR_UNSUPPORTED, "%lld block pairs: too many for one launch", (long long)num_pairs);
+    return from_hip(pkv::launch_copy_blocks(views[0], views[1], const_cast<void*>(views[2]),
+                                            const_cast<void*>(views[3]), static_cast<const int64_t*>(views[4]),
+                                            num_pairs, num_src_blocks, num_dst_blocks, block_bytes,
+                                            static_cast<hipStream_t>(stream)),
+                    "copy_blocks launch");
+}
+
 pkv_status pkv_paged_attention_prefill(const void* q, const void* k_cache, const void* v_cache,
                                        const int32_t* block_tables, const int32_t* context_lens,
                                        const int32_t* query_start_loc, float scale, void* out, int32_t num_seqs,

@@ -49,6 +49,7 @@ _SIGNATURES = {
     "pkv_paged_attention_decode_partitions_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _i32, _i32,
                                                          _i32, _i32, _i32, _i64, _i32, _i32, _i32, _vp, _sz, _i32,
                                                          _u32, _vp]),
+    "pkv_copy_blocks": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _vp]),
     "pkv_paged_attention_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                            _i64, _i32, _i32, _i32, _i32, _vp]),
     "pkv_status_string": (ctypes.c_char_p, [_i32]),
@@ -344,3 +345,35 @@ def paged_attention_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: 
                                             int(partition_size), ws_ptr, ws_bytes, _dtype_code(out),
                                             DECODE_SHARED_BLOCKS if shared_blocks else 0, _stream(dev))
     _check(st, "paged_attention_decode_fp8")
+
+
+def _pool_code(t: torch.Tensor) -> int:
+    return PKV_FP8_E4M3 if t.dtype in FP8_POOL_DTYPES else _dtype_code(t)
+
+
+def swap_blocks(src_k: torch.Tensor, src_v: torch.Tensor, dst_k: torch.Tensor, dst_v: torch.Tensor,
+                pairs: torch.Tensor) -> None:
+    """Copy whole blocks ``pairs[i] = (src, dst)`` from the source pools to the destination pools.
+
+    Pools may be device tensors or pinned host tensors (``pin_memory=True``);
+    ``pairs`` is int64 ``[n, 2]`` on the device or pinned.  The launch goes on
+    the current stream of the device that holds a device-side pool.
+    """
+    lib = load_library()
+    dev_t = next((t for t in (src_k, dst_k) if t.is_cuda), None)
+    _require(dev_t is not None, "at least one side must be a device pool")
+    for t, n in ((src_k, "src_k"), (src_v, "src_v"), (dst_k, "dst_k"), (dst_v, "dst_v"), (pairs, "pairs")):
+        _require(isinstance(t, torch.Tensor) and t.is_contiguous(), f"{n} must be a contiguous tensor")
+        _require(t.is_cuda or t.is_pinned(), f"{n} must be on the device or in pinned host memory")
+    nbs, hkv, D = _pool_dims(src_k, src_v)
+    nbd, hkv2, D2 = _pool_dims(dst_k, dst_v)
+    _require((hkv, D) == (hkv2, D2) and src_k.dtype == dst_k.dtype, "source and destination pools differ in shape")
+    _require(pairs.dtype == torch.int64 and pairs.dim() == 2 and pairs.shape[1] == 2, "pairs must be int64 [n, 2]")
+    st = lib.pkv_copy_blocks(_ptr(src_k), _ptr(src_v), _ptr(dst_k), _ptr(dst_v), _ptr(pairs), pairs.shape[0], nbs,
+                             nbd, hkv, D, BLOCK_SIZE, _pool_code(src_k), _stream(dev_t.device))
+    _check(st, "copy_blocks")
+
+
+def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, pairs: torch.Tensor) -> None:
+    """Copy-on-write inside one pool: block ``src`` to block ``dst`` for every pair of ``pairs`` (int64 ``[n, 2]``)."""
+    swap_blocks(k_cache, v_cache, k_cache, v_cache, pairs)

@@ -174,6 +174,25 @@ def test_fp8_validation(lib):
     assert pre(lib, kvd=FP8) == UNSUPPORTED
 
 
+def test_copy_blocks_validation(lib):
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 4, 10, 10, 8, 128, 16, BF16, None]
+
+    def call(**kw):
+        a = list(args)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return lib.pkv_copy_blocks(*a)
+    assert call(a11=9) == UNSUPPORTED
+    assert call(a9=96) == UNSUPPORTED
+    assert call(a10=32) == UNSUPPORTED
+    assert call(a5=-1) == INVALID
+    assert call(a6=0) == INVALID
+    assert call(a4=None) == INVALID
+    assert call(a2=FAKE + 4) == INVALID
+    assert call(a5=0, a0=None, a4=None) == OK        # nothing to copy: no launch
+    assert lib.pkv_last_error() == b""
+
+
 def _align(x, a=256):
     return -(-x // a) * a
 
