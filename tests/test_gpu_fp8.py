@@ -164,3 +164,10 @@ def test_fp8_matches_bf16_on_dequantised_pools():
                                max_context_len=b.max_context_len)
     torch.cuda.synchronize()
     assert np.max(np.abs(out_f64(out8) - out_f64(out16))) <= 8e-3
+
+
+def test_fp8_more_than_4096_sequences():
+    rng = np.random.default_rng(18)
+    lens = rng.integers(1, 60, size=4200)
+    b = W.build_static("fp8_many", 23, "bf16", 8, 2, 64, lens, num_blocks=W.pool_blocks_for(lens, 16))
+    run_fp8(W.fp8_variant(b), seqs=[0, 1, 4095, 4096, 4199], what="4200 sequences")

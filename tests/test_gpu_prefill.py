@@ -154,3 +154,14 @@ def test_more_queries_than_context_gives_zeros():
     got = out_f64(d.out)
     assert np.isfinite(got).all()
     assert np.array_equal(got[5:10], np.zeros_like(got[5:10]))   # positions < 0
+
+
+def test_more_than_4096_requests():
+    """Requests are processed 4096 per launch: the split must not shift any row."""
+    rng = np.random.default_rng(17)
+    n = 4100
+    cached = rng.integers(0, 40, size=n).tolist()
+    new = [1] * n
+    new[5], new[4097], new[4099] = 20, 17, 3
+    b = W.build_prefill("prefill_many", 19, 8, 2, 64, cached, new)
+    check(b, seqs=[0, 5, 4095, 4096, 4097, 4099], what="4100 requests")
