@@ -6,8 +6,10 @@
 //     out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p,   M = max_p m_p,
 // an identity of the exponential (nothing here is an approximation beyond
 // fp32 rounding).  Pieces with no valid token (m = -inf, l = 0) weigh 0.
-// One 256-thread workgroup per (sequence, query head).  All sums run in a
-// fixed order, so the result does not depend on scheduling.
+// One 256-thread workgroup per (sequence, query head); its 256 / (D / 4)
+// slots each merge every SLOTS-th piece with a running maximum (the same
+// identity applied one piece at a time), then slot 0 merges the slots.  All
+// sums run in a fixed order, so the result does not depend on scheduling.
 //
 // Where the pieces are depends on the decode path:
 //   partitioned (fp32 KV): partition i of sequence s at row (s * P + i) * Hq + h;
@@ -23,31 +25,9 @@ namespace {
 
 constexpr int kThreads = 256;
 
-__device__ __forceinline__ float block_max(float v, float* red) {
-    const int tid = threadIdx.x;
-    red[tid] = v;
-    __syncthreads();
-    for (int off = kThreads / 2; off > 0; off >>= 1) {
-        if (tid < off) red[tid] = fmaxf(red[tid], red[tid + off]);
-        __syncthreads();
-    }
-    const float r = red[0];
-    __syncthreads();
-    return r;
-}
-
-__device__ __forceinline__ float block_sum(float v, float* red) {
-    const int tid = threadIdx.x;
-    red[tid] = v;
-    __syncthreads();
-    for (int off = kThreads / 2; off > 0; off >>= 1) {
-        if (tid < off) red[tid] = red[tid] + red[tid + off];
-        __syncthreads();
-    }
-    const float r = red[0];
-    __syncthreads();
-    return r;
-}
+// Weight 2^(m - M) of a piece with reference max m against a running max M;
+// an empty piece (m = -inf) weighs 0 whatever M is.
+__device__ __forceinline__ float piece_weight(float m, float M) { return m == -INFINITY ? 0.f : exp2_fast(m - M); }
 
 template <int D>
 __device__ __forceinline__ void write_row(const DecodeParams& p, int64_t row, int c4, float4 v) {
@@ -65,8 +45,8 @@ template <int D, bool kBalanced>
 __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(DecodeParams p) {
     constexpr int LPR = D / 4;             // threads per output row (float4 each)
     constexpr int SLOTS = kThreads / LPR;  // pieces in flight per step
-    __shared__ float red[kThreads];
     __shared__ float4 part_acc[SLOTS][LPR];
+    __shared__ float part_m[SLOTS], part_l[SLOTS];
 
     const int Hq = p.num_q_heads;
     const int s = blockIdx.x / Hq;
@@ -109,39 +89,47 @@ __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(DecodeParams p)
     }
     auto row_of = [&](int i) -> int64_t { return i == 0 ? first_row : row0 + (int64_t)i * stride; };
 
-    float mx = -INFINITY;
-    for (int i = tid; i < n_pieces; i += kThreads) mx = fmaxf(mx, p.m_part[row_of(i)]);
-    const float M = block_max(mx, red);
-    const float M_use = (M == -INFINITY) ? 0.f : M;
-
-    float den = 0.f;
-    for (int i = tid; i < n_pieces; i += kThreads) {
-        const int64_t r = row_of(i);
-        den += exp2_fast(p.m_part[r] - M_use) * p.l_part[r];
-    }
-    den = block_sum(den, red);
-
+    // Each slot merges its pieces i = slot, slot + SLOTS, ... in order with a
+    // running (max, sum, output): the loads of a piece need nothing from the
+    // previous one, so they are all in flight at once.
+    float M = -INFINITY, den = 0.f;
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll 4
     for (int i = slot; i < n_pieces; i += SLOTS) {
         const int64_t r = row_of(i);
-        const float w = exp2_fast(p.m_part[r] - M_use);
+        const float m = p.m_part[r];
+        const float l = p.l_part[r];
         const float4 v = reinterpret_cast<const float4*>(p.o_part + r * D)[c4];
-        a.x = fmaf(w, v.x, a.x);
-        a.y = fmaf(w, v.y, a.y);
-        a.z = fmaf(w, v.z, a.z);
-        a.w = fmaf(w, v.w, a.w);
+        const float Mn = fmaxf(M, m);
+        const float wa = piece_weight(M, Mn);  // rescale of what is merged so far
+        const float wb = piece_weight(m, Mn);
+        den = den * wa + l * wb;
+        a.x = a.x * wa + v.x * wb;
+        a.y = a.y * wa + v.y * wb;
+        a.z = a.z * wa + v.z * wb;
+        a.w = a.w * wa + v.w * wb;
+        M = Mn;
     }
     part_acc[slot][c4] = a;
+    if (c4 == 0) {
+        part_m[slot] = M;
+        part_l[slot] = den;
+    }
     __syncthreads();
     if (slot != 0) return;
-    float4 sum = part_acc[0][c4];
-    for (int k = 1; k < SLOTS; ++k) {
+    // slots in order: a fixed summation order, independent of scheduling
+    float Mt = part_m[0];
+    for (int k = 1; k < SLOTS; ++k) Mt = fmaxf(Mt, part_m[k]);
+    den = 0.f;
+    float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k = 0; k < SLOTS; ++k) {
+        const float w = piece_weight(part_m[k], Mt);
         const float4 v = part_acc[k][c4];
-        sum.x += v.x;
-        sum.y += v.y;
-        sum.z += v.z;
-        sum.w += v.w;
+        den = fmaf(w, part_l[k], den);
+        sum.x = fmaf(w, v.x, sum.x);
+        sum.y = fmaf(w, v.y, sum.y);
+        sum.z = fmaf(w, v.z, sum.z);
+        sum.w = fmaf(w, v.w, sum.w);
     }
     const float inv = den > 0.f ? 1.f / den : 0.f;
     write_row<D>(p, out_row, c4, make_float4(sum.x * inv, sum.y * inv, sum.z * inv, sum.w * inv));
