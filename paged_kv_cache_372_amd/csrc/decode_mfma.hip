@@ -58,8 +58,8 @@ namespace {
 #define PKV_PREFETCH_BLOCKS 3
 #endif
 constexpr int kPrefetchBlocks = PKV_PREFETCH_BLOCKS;  // KV blocks each wave keeps in flight
-// An fp8 ring slot takes 2/3 of the registers, but a deeper ring was
-// measured no faster, so fp8 keeps the same depth.
+// An fp8 ring slot takes 3/4 of the registers of a bf16 one; a 4-deep fp8
+// ring measured no faster, so fp8 keeps the same depth.
 constexpr int kPrefetchBlocksFp8 = kPrefetchBlocks;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -81,12 +81,13 @@ struct SlotRegs {
 // when the block is used (the conversion is exact).  K: load i holds the
 // 16-dim chunk 4i + lane/16 of token lane%16; the QK contraction takes dims in
 // the order that makes step kk read half (kk & 1) of load kk/2, and q is
-// loaded in that order.  V: load c holds dim 16c + lane%16, tokens
-// 4(lane/16)..+3, one code each.
+// loaded in that order.  V: load i holds the whole 16-token row of dim
+// 64i + lane (16 bytes, a contiguous 1 KiB per wave); fp8_v_words regroups
+// the rows across lanes into the PV operand layout.
 template <int D>
 struct SlotRegs8 {
     uint4 k[D / 64];
-    uint32_t v[D / 16];
+    uint4 v[D / 64];
     bf16x8_t q[D / 32];    // q step kk, k-group g: dims 64(kk/2) + 16g + 8(kk&1) .. +7
 };
 
@@ -103,10 +104,6 @@ __device__ __forceinline__ bf16x8_t k_operand(const SlotRegs<D>& r, int kk) {
     return __builtin_bit_cast(bf16x8_t, r.k[kk]);
 }
 template <int D>
-__device__ __forceinline__ uint2 v_operand(const SlotRegs<D>& r, int c) {
-    return r.v[c];
-}
-template <int D>
 __device__ __forceinline__ bf16x8_t k_operand(const SlotRegs8<D>& r, int kk) {
     const uint4 w = r.k[kk >> 1];
     const uint32_t a = (kk & 1) ? w.z : w.x;
@@ -114,9 +111,30 @@ __device__ __forceinline__ bf16x8_t k_operand(const SlotRegs8<D>& r, int kk) {
     return __builtin_bit_cast(bf16x8_t, make_uint4(e4m3x2_to_bf16x2<false>(a), e4m3x2_to_bf16x2<true>(a),
                                                    e4m3x2_to_bf16x2<false>(b), e4m3x2_to_bf16x2<true>(b)));
 }
+// The V words of an fp8 slot in the PV operand layout: word c of lane
+// (d = lane % 16, g = lane / 16) holds the codes of tokens 4g..4g+3 of dim
+// 16c + d.  Lane (d, r) loaded dims 64i + 16r + d, word t = tokens 4t..4t+3:
+// a 4 x 4 transpose of words between the four 16-lane rows, done with two
+// rounds of row swaps (rows 2,3 <-> 0,1 of a register pair, then odd <->
+// even rows).
 template <int D>
-__device__ __forceinline__ uint2 v_operand(const SlotRegs8<D>& r, int c) {
-    return make_uint2(e4m3x2_to_bf16x2<false>(r.v[c]), e4m3x2_to_bf16x2<true>(r.v[c]));
+__device__ __forceinline__ void fp8_v_words(const SlotRegs8<D>& r, uint32_t* w) {
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) {
+        uint32_t x0 = r.v[i].x, x1 = r.v[i].y, x2 = r.v[i].z, x3 = r.v[i].w;
+        const auto a = __builtin_amdgcn_permlane32_swap(x0, x2, false, false);
+        const auto b = __builtin_amdgcn_permlane32_swap(x1, x3, false, false);
+        x0 = a[0];
+        x2 = a[1];
+        x1 = b[0];
+        x3 = b[1];
+        const auto c = __builtin_amdgcn_permlane16_swap(x0, x1, false, false);
+        const auto e = __builtin_amdgcn_permlane16_swap(x2, x3, false, false);
+        w[4 * i + 0] = c[0];
+        w[4 * i + 1] = c[1];
+        w[4 * i + 2] = e[0];
+        w[4 * i + 3] = e[1];
+    }
 }
 
 // Uniform facts about the block a ring slot holds.
@@ -143,11 +161,11 @@ struct SoftmaxState {
 // moves less often.
 constexpr float kRescaleSlack = 8.f;
 
-// The raw V codes of an fp8 slot with the tokens past valid_n zeroed: one
-// byte per token (tokens 4g..4g+3 of the load), so one mask serves all loads.
-template <int D>
-__device__ __forceinline__ uint2 v_operand_masked(const SlotRegs8<D>& r, int c, uint32_t vm) {
-    const uint32_t w = r.v[c] & vm;
+// An fp8 V word (fp8_v_words) as a bf16 operand with the tokens past
+// valid_n zeroed: one byte per token (tokens 4g..4g+3), so one mask serves
+// all words.
+__device__ __forceinline__ uint2 v_operand_fp8(uint32_t w, uint32_t vm) {
+    w &= vm;
     return make_uint2(e4m3x2_to_bf16x2<false>(w), e4m3x2_to_bf16x2<true>(w));
 }
 template <int D>
@@ -227,13 +245,17 @@ __device__ __forceinline__ void compute_block(const Slot& r, float4_t* acc, Soft
     };
     // tokens past the end hold stale or NaN data: zero them (0 * NaN = NaN);
     // only the last block of a sequence has such tokens
-    const auto vm = [&] {
-        if constexpr (std::is_same_v<Slot, SlotRegs<D>>)
-            return valid_n < 16 ? v_mask_bf16(valid_n, g) : make_uint2(0xFFFFFFFFu, 0xFFFFFFFFu);
-        else return valid_n < 16 ? v_mask_fp8(valid_n, g) : 0xFFFFFFFFu;
-    }();
+    if constexpr (std::is_same_v<Slot, SlotRegs<D>>) {
+        const uint2 vm = valid_n < 16 ? v_mask_bf16(valid_n, g) : make_uint2(0xFFFFFFFFu, 0xFFFFFFFFu);
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) pv(c, v_operand_masked<D>(r, c, vm));
+        for (int c = 0; c < D / 16; ++c) pv(c, v_operand_masked<D>(r, c, vm));
+    } else {
+        const uint32_t vm = valid_n < 16 ? v_mask_fp8(valid_n, g) : 0xFFFFFFFFu;
+        uint32_t w[D / 16];
+        fp8_v_words<D>(r, w);
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) pv(c, v_operand_fp8(w[c], vm));
+    }
 }
 
 // Walk-position window: lane i describes position base + i of the wave's
@@ -437,7 +459,7 @@ __global__ __launch_bounds__(64 * kMaxWavesPerGroup) void decode_bf16_balanced_k
         const uint4* qr = reinterpret_cast<const uint4*>(q_base + (int64_t)info[d].seq * Hq * D);
         if constexpr (kFp8) {
             const u32x4_t* kt = reinterpret_cast<const u32x4_t*>(k_head + (int64_t)pb * block_stride);
-            const uint32_t* vt = reinterpret_cast<const uint32_t*>(v_head + (int64_t)pb * block_stride);
+            const u32x4_t* vt = reinterpret_cast<const u32x4_t*>(v_head + (int64_t)pb * block_stride);
 #pragma unroll
             for (int i = 0; i < D / 64; ++i)
                 ring[d].k[i] = __builtin_bit_cast(uint4, kCached ? kt[i * 64 + lane]
@@ -445,10 +467,10 @@ __global__ __launch_bounds__(64 * kMaxWavesPerGroup) void decode_bf16_balanced_k
 #pragma unroll
             for (int kk = 0; kk < D / 32; ++kk)
                 ring[d].q[kk] = __builtin_bit_cast(bf16x8_t, qr[8 * (kk >> 1) + 2 * g + (kk & 1)]);
-            const int vo = (lane & 15) * 4 + (lane >> 4);
 #pragma unroll
-            for (int c = 0; c < D / 16; ++c)
-                ring[d].v[c] = kCached ? vt[c * 64 + vo] : __builtin_nontemporal_load(vt + c * 64 + vo);
+            for (int i = 0; i < D / 64; ++i)
+                ring[d].v[i] = __builtin_bit_cast(uint4, kCached ? vt[i * 64 + lane]
+                                                                 : __builtin_nontemporal_load(vt + i * 64 + lane));
         } else {
             const u32x4_t* kt = reinterpret_cast<const u32x4_t*>(k_head + (int64_t)pb * block_stride);
             const u32x2_t* vt = reinterpret_cast<const u32x2_t*>(v_head + (int64_t)pb * block_stride);
@@ -462,6 +484,8 @@ __global__ __launch_bounds__(64 * kMaxWavesPerGroup) void decode_bf16_balanced_k
                                                                   : __builtin_nontemporal_load(kt + kk * 64 + lane));
 #pragma unroll
             for (int kk = 0; kk < D / 32; ++kk) ring[d].q[kk] = __builtin_bit_cast(bf16x8_t, qr[4 * kk + g]);
+            // (bf16 V in 16-byte loads, regrouped across lanes as for fp8,
+            // measured slightly slower: 8-byte loads are kept here)
             const int vo = (lane & 15) * 4 + (lane >> 4);
 #pragma unroll
             for (int c = 0; c < D / 16; ++c)
