@@ -56,6 +56,20 @@ __global__ __launch_bounds__(kThreads) void cache_write_kernel(const E* __restri
         tile_of[tid] = tile;
         off_of[tid] = off;
     }
+    // K chunks of this thread (thread (c, t), t fastest), loaded now: their
+    // address does not depend on the slot, so the loads overlap the slot
+    // and V loads instead of following the barrier
+    constexpr int K_IT = (kTokens * NCH + kThreads - 1) / kThreads;
+    uint4 kw[K_IT];
+#pragma unroll
+    for (int it = 0; it < K_IT; ++it) {
+        const int i = tid + it * kThreads;
+        const int t = i % kTokens;
+        const int c = i / kTokens;
+        kw[it] = make_uint4(0, 0, 0, 0);
+        if (i < kTokens * NCH && t0 + t < num_tokens)
+            kw[it] = reinterpret_cast<const uint4*>(k_new + ((t0 + t) * num_kv_heads + h) * (int64_t)D)[c];
+    }
     // V rows into LDS: thread (t, c) reads 16-byte chunk c of token t
     for (int i = tid; i < kTokens * NCH; i += kThreads) {
         const int t = i / NCH;
@@ -67,14 +81,16 @@ __global__ __launch_bounds__(kThreads) void cache_write_kernel(const E* __restri
     }
     __syncthreads();
 
-    // K: thread (c, t), t fastest
-    for (int i = tid; i < kTokens * NCH; i += kThreads) {
+    // K stores
+#pragma unroll
+    for (int it = 0; it < K_IT; ++it) {
+        const int i = tid + it * kThreads;
+        if (i >= kTokens * NCH) continue;
         const int t = i % kTokens;
         const int c = i / kTokens;
         const int64_t tile = tile_of[t];
         if (tile < 0) continue;
-        const uint4 w = reinterpret_cast<const uint4*>(k_new + ((t0 + t) * num_kv_heads + h) * (int64_t)D)[c];
-        reinterpret_cast<uint4*>(k_cache + tile)[c * kBlockSize + off_of[t]] = w;
+        reinterpret_cast<uint4*>(k_cache + tile)[c * kBlockSize + off_of[t]] = kw[it];
     }
     // V: thread (d, t), t fastest
     for (int i = tid; i < kTokens * D; i += kThreads) {
@@ -143,6 +159,24 @@ __global__ __launch_bounds__(kThreads) void cache_write_fp8_kernel(const E* __re
         off_of[tid] = off;
     }
     constexpr int X = 16 / (int)sizeof(E);            // input elements per 16-byte load
+    // K inputs of this thread (thread (c, t), t fastest: the 16 elements of
+    // output chunk c of token t), loaded before the barrier as for bf16
+    constexpr int K_IT = (kTokens * NCH + kThreads - 1) / kThreads;
+    constexpr int KW = 16 / X;                        // 16-byte loads per output chunk
+    uint4 kraw[K_IT][KW];
+#pragma unroll
+    for (int it = 0; it < K_IT; ++it) {
+        const int i = tid + it * kThreads;
+        const int t = i % kTokens;
+        const int c = i / kTokens;
+#pragma unroll
+        for (int u = 0; u < KW; ++u) kraw[it][u] = make_uint4(0, 0, 0, 0);
+        if (i < kTokens * NCH && t0 + t < num_tokens) {
+            const uint4* src = reinterpret_cast<const uint4*>(k_new + ((t0 + t) * num_kv_heads + h) * (int64_t)D + 16 * c);
+#pragma unroll
+            for (int u = 0; u < KW; ++u) kraw[it][u] = src[u];
+        }
+    }
     for (int i = tid; i < kTokens * (D / X); i += kThreads) {
         const int t = i / (D / X);
         const int c = i % (D / X);
@@ -157,13 +191,16 @@ __global__ __launch_bounds__(kThreads) void cache_write_fp8_kernel(const E* __re
         if constexpr (sizeof(E) == 2) return __uint_as_float((uint32_t)e << 16);
         else return __uint_as_float((uint32_t)e);
     };
-    // K: thread (c, t), t fastest: 16 codes of chunk c of token t
-    for (int i = tid; i < kTokens * NCH; i += kThreads) {
+    // K: 16 codes of chunk c of token t
+#pragma unroll
+    for (int it = 0; it < K_IT; ++it) {
+        const int i = tid + it * kThreads;
+        if (i >= kTokens * NCH) continue;
         const int t = i % kTokens;
         const int c = i / kTokens;
         const int64_t tile = tile_of[t];
         if (tile < 0) continue;
-        const E* src = k_new + ((t0 + t) * num_kv_heads + h) * (int64_t)D + 16 * c;
+        const E* src = reinterpret_cast<const E*>(kraw[it]);
         uint32_t w[4];
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
