@@ -14,6 +14,9 @@
 * F6  attention over an fp8 cache equals the bf16 oracle over the
       dequantised values when the scales are powers of two (then every
       dequantised value is exact in bf16): bit-identical.
+* F7  the same for multi-token (chunked prefill) attention: causal queries
+      over an fp8 cache equal the bf16 prefill oracle over the dequantised
+      pools, bit for bit, and a single-query request equals fp8 decode.
 
 ``test_planted_fp8_mistakes_are_caught`` plants mistakes in the oracle.
 """
@@ -25,6 +28,7 @@ import torch
 
 import oracle.fp8 as of8
 import oracle.paged_attention as opa
+import oracle.prefill as opp
 from test_oracle_pins import k_flat_offset, v_flat_offset
 from workloads import bf16_bits_rne, pool_shapes
 
@@ -126,7 +130,40 @@ def pin_f6():
     assert np.array_equal(got, ref)
 
 
-PINS = {"F1": pin_f1, "F2": pin_f2, "F3": pin_f3, "F4": pin_f4, "F5": pin_f5, "F6": pin_f6}
+def as_bf16_pools(kp, vp, ks, vs):
+    """The dequantised values of fp8 pools in the bf16 pool layout (K chunks of 8)."""
+    NB, Hkv, _, bs, _ = kp.shape
+    D = vp.shape[2]
+    kval = np.transpose(of8.dequantize_pool(kp, ks), (0, 1, 3, 2, 4)).reshape(NB, Hkv, bs, D)
+    kb = bf16_bits_rne(kval.astype(np.float32)).reshape(NB, Hkv, bs, D // 8, 8).transpose(0, 1, 3, 2, 4).copy()
+    vb = bf16_bits_rne(of8.dequantize_pool(vp, vs).astype(np.float32))
+    return kb, vb
+
+
+def pin_f7():
+    rng = np.random.default_rng(11)
+    NB, Hq, Hkv, D, bs = 10, 4, 2, 32, 16
+    kp = rng.integers(0, 0x7F, size=(NB, Hkv, D // 16, bs, 16), dtype=np.uint8) | \
+        (rng.integers(0, 2, size=(NB, Hkv, D // 16, bs, 16), dtype=np.uint8) << 7)
+    vp = rng.integers(0, 0x7F, size=(NB, Hkv, D, bs), dtype=np.uint8) | \
+        (rng.integers(0, 2, size=(NB, Hkv, D, bs), dtype=np.uint8) << 7)
+    ks, vs = np.array([0.5, 2.0 ** -4]), np.array([2.0, 0.25])
+    lens = np.array([20, 33, 7])
+    new = np.array([6, 1, 7])                       # request 1 is a decode row
+    qsl = np.concatenate([[0], np.cumsum(new)])
+    q = bf16_bits_rne(rng.standard_normal((int(qsl[-1]), Hq, D)).astype(np.float32) * 0.1)
+    tables = rng.permutation(NB)[:9].reshape(3, 3).astype(np.int32)
+    got = opp.ref_paged_attention_prefill(q, kp, vp, tables, lens, qsl, 0.3, "fp8", k_scale=ks, v_scale=vs)
+    kb, vb = as_bf16_pools(kp, vp, ks, vs)
+    assert np.array_equal(opa.widen(vb, "bf16"), of8.dequantize_pool(vp, vs))   # exact in bf16
+    ref = opp.ref_paged_attention_prefill(q, kb, vb, tables, lens, qsl, 0.3, "bf16")
+    assert np.array_equal(got, ref)
+    dec = opa.ref_paged_attention_decode(q[qsl[1]:qsl[2]], kp, vp, tables[1:2], lens[1:2], 0.3, "fp8",
+                                         k_scale=ks, v_scale=vs)
+    assert np.array_equal(got[qsl[1]:qsl[2]], dec)
+
+
+PINS = {"F1": pin_f1, "F2": pin_f2, "F3": pin_f3, "F4": pin_f4, "F5": pin_f5, "F6": pin_f6, "F7": pin_f7}
 
 
 @pytest.mark.parametrize("name", sorted(PINS))
