@@ -34,7 +34,7 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "paged-attn decode: achieved KV-read HBM GB/s (% of peak) + decode tokens/s"
 PEAK_BF16_TFLOPS = 2500.0
 PREFILL_METRIC = "paged-attn chunked prefill: attention TFLOP/s (causal flops) + prefill tokens/s"
-PREFILL_CONFIGS = ("chunked_prefill",)
+PREFILL_CONFIGS = ("chunked_prefill", "chunked_prefill_fp8")
 COPY_CONFIGS = ("block_copy", "swap")
 PEAK_HOST_LINK_GBS = 64.0   # PCIe 5.0 x16, one direction
 COPY_METRIC = "whole-block KV copies: GB/s moved (copy-on-write in HBM: read + write; swap: over the host link)"
@@ -247,7 +247,7 @@ def summarize_profile(prefix: str, workload: str, partition_size, copy_mib: int,
     prefix_k = {"prefill": PREFILL_KERNEL_PREFIX, "copy": COPY_KERNEL_PREFIX}.get(family(workload), DECODE_KERNEL_PREFIX)
     short_k = prefix_k.split("::")[-1]
     dec = [k for k in fetch if short_k in k][0]
-    lines = [f"# rocprofv3: decode kernels on the {workload} workload", "",
+    lines = [f"# rocprofv3: {family(workload)} kernels on the {workload} workload", "",
              "Commands (run from the repository root; `cd /tmp && export TMPDIR=/tmp` first):", "", "```",
              commands.strip(), "```", "", "## Kernel trace (`--kernel-trace --stats`)", "",
              "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
@@ -291,14 +291,22 @@ def cpu_baseline_prefill(b, budget_s: float = 12.0):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         threads = 1
-    kp, vp = oracle.ref_reshape_and_cache(b.k_new, b.v_new, b.slot_mapping, b.k_pool, b.v_pool)
+    fp8 = b.dtype == "fp8"
+    if fp8:
+        ks, vs = b.info["k_scale"], b.info["v_scale"]
+        kp, vp = oracle.ref_reshape_and_cache_fp8(b.k_new, b.v_new, b.slot_mapping, b.k_pool, b.v_pool, ks, vs,
+                                                  b.info["src_dtype"])
+        scales = dict(k_scale=ks, v_scale=vs)
+    else:
+        kp, vp = oracle.ref_reshape_and_cache(b.k_new, b.v_new, b.slot_mapping, b.k_pool, b.v_pool)
+        scales = {}
     n = b.query_lens()
     L = b.context_lens.astype(np.int64)
     t0 = time.perf_counter()
     done, flops, tokens = 0, 0, 0
     for s in range(b.num_seqs):
         oracle.ref_paged_attention_prefill(b.q, kp, vp, b.block_tables, b.context_lens, b.query_start_loc, b.scale,
-                                           b.dtype, seqs=[s])
+                                           b.dtype, seqs=[s], **scales)
         done += 1
         tokens += int(n[s])
         flops += 4 * b.head_dim * b.num_q_heads * int(n[s] * (L[s] - n[s]) + n[s] * (n[s] + 1) // 2)
@@ -320,8 +328,11 @@ def run_prefill(args):
     from paged_kv_cache_372_amd import ops
     import workloads as W
 
+    fp8 = args.config == "chunked_prefill_fp8"
     t_gen = time.perf_counter()
     b = W.chunked_prefill()
+    if fp8:  # the same step over an fp8 (E4M3) cache with per-KV-head scales
+        b = W.fp8_variant(b)
     gen_s = time.perf_counter() - t_gen
 
     def dev(a):
@@ -331,17 +342,28 @@ def run_prefill(args):
         return torch.from_numpy(np.ascontiguousarray(a, dtype=dt)).cuda()
 
     q, k_new, v_new = dev(b.q), dev(b.k_new), dev(b.v_new)
-    kc, vc = dev(b.k_pool), dev(b.v_pool)
+    if fp8:
+        kc, vc = ints(b.k_pool, np.uint8), ints(b.v_pool, np.uint8)
+        ks, vs = ints(b.info["k_scale"], np.float32), ints(b.info["v_scale"], np.float32)
+    else:
+        kc, vc = dev(b.k_pool), dev(b.v_pool)
     slots = ints(b.slot_mapping, np.int64)
     bt, lens, qsl = ints(b.block_tables, np.int32), ints(b.context_lens, np.int32), ints(b.query_start_loc, np.int32)
     out = torch.empty_like(q)
     flops = b.flops()
 
     def step(ev=None):
-        ops.reshape_and_cache(k_new, v_new, slots, kc, vc)
+        if fp8:
+            ops.reshape_and_cache_fp8(k_new, v_new, slots, kc, vc, ks, vs)
+        else:
+            ops.reshape_and_cache(k_new, v_new, slots, kc, vc)
         if ev is not None:
             ev[0].record()
-        ops.paged_attention_prefill(q, kc, vc, bt, lens, qsl, b.scale, out, max_context_len=b.max_context_len)
+        if fp8:
+            ops.paged_attention_prefill_fp8(q, kc, vc, ks, vs, bt, lens, qsl, b.scale, out,
+                                            max_context_len=b.max_context_len)
+        else:
+            ops.paged_attention_prefill(q, kc, vc, bt, lens, qsl, b.scale, out, max_context_len=b.max_context_len)
         if ev is not None:
             ev[1].record()
 
@@ -371,7 +393,8 @@ def run_prefill(args):
                    "num_q_heads": b.num_q_heads, "num_kv_heads": b.num_kv_heads, "head_dim": b.head_dim,
                    "block_size": b.block_size, "chunk": int(b.query_lens().max()),
                    "cached_mean": round(float(np.mean(b.info["cached"])), 1),
-                   "context_len_max": b.max_context_len, "flops_per_step": flops},
+                   "context_len_max": b.max_context_len, "flops_per_step": flops,
+                   "kv_dtype": "fp8_e4m3" if fp8 else "bf16"},
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "tokens_per_s": round(b.num_tokens / (ms / 1e3), 1),
         "prefill_kernel_ms": round(k_ms, 5),

@@ -303,7 +303,7 @@ pkv_status pkv_copy_blocks(const void* src_k, const void* src_v, void* dst_k, vo
  *   max_context_len  host-known bound of context_lens (larger are clamped)
  * No workspace.  Requests are processed 4096 per launch.  Results do not
  * depend on where blocks sit in the pool.  fp32 KV returns
- * PKV_ERR_UNSUPPORTED.
+ * PKV_ERR_UNSUPPORTED; fp8 pools take pkv_paged_attention_prefill_fp8.
  */
 pkv_status pkv_paged_attention_prefill(const void* q, const void* k_cache, const void* v_cache,
                                        const int32_t* block_tables, const int32_t* context_lens,
@@ -312,6 +312,27 @@ pkv_status pkv_paged_attention_prefill(const void* q, const void* k_cache, const
                                        int32_t head_dim, int32_t block_size, int64_t num_blocks,
                                        int32_t max_blocks_per_seq, int32_t max_context_len, pkv_dtype kv_dtype,
                                        pkv_dtype out_dtype, void* stream);
+
+/*
+ * Chunked prefill over an fp8 cache: pkv_paged_attention_prefill with K =
+ * decode(code) * k_scale[g] and V = decode(code) * v_scale[g] for KV head g
+ * (fp8 format and pool layout as for pkv_reshape_and_cache_fp8).  The pages
+ * name KV quantisation for long contexts (runbyai section 5) and chunked
+ * prefill as the step that shares the batch with decode (architvora
+ * "Continuous Batching"); this is the two together.  q is bf16; out is
+ * out_dtype.  The codes are converted to bf16 exactly, so the products are
+ * those of a bf16 cache holding the dequantised values.
+ *   k_scale, v_scale  [device] fp32 [num_kv_heads], positive
+ * Null scales return PKV_ERR_INVALID_ARG; otherwise as the bf16 entry point
+ * (no workspace, requests 4096 per launch).
+ */
+pkv_status pkv_paged_attention_prefill_fp8(const void* q, const void* k_cache, const void* v_cache,
+                                           const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                                           const int32_t* context_lens, const int32_t* query_start_loc, float scale,
+                                           void* out, int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                           int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                                           pkv_dtype out_dtype, void* stream);
 
 /* Static description of a status code.  Never NULL. */
 const char* pkv_status_string(pkv_status status);

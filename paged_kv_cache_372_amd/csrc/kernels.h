@@ -102,6 +102,9 @@ struct PrefillParams {
     int32_t ctx_cap;
     int32_t out_bf16;
     int32_t tile_bound;             // workgroup tiles launched per KV head (>= the tiles needed)
+    int32_t kv_fp8;                 // 1: pools hold E4M3 codes ([NB][Hkv][D/16][16][16] and [NB][Hkv][D][16])
+    const float* k_scale;           // fp8: [Hkv] K dequantisation scale
+    const float* v_scale;           // fp8: [Hkv] V dequantisation scale
 };
 
 // Rows (query token x head of a KV group) one prefill workgroup covers.

@@ -267,7 +267,7 @@ pkv_status run_reduce_kernels(const Call& c, hipStream_t stream) {
 
 extern "C" {
 
-int32_t pkv_abi_version(void) { return 4; }
+int32_t pkv_abi_version(void) { return 5; }
 
 const char* pkv_status_string(pkv_status status) {
     switch (status) {
@@ -494,14 +494,16 @@ pkv_status pkv_copy_blocks(const void* src_k, const void* src_v, void* dst_k, vo
                     "copy_blocks launch");
 }
 
-pkv_status pkv_paged_attention_prefill(const void* q, const void* k_cache, const void* v_cache,
-                                       const int32_t* block_tables, const int32_t* context_lens,
-                                       const int32_t* query_start_loc, float scale, void* out, int32_t num_seqs,
-                                       int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
-                                       int32_t head_dim, int32_t block_size, int64_t num_blocks,
-                                       int32_t max_blocks_per_seq, int32_t max_context_len, pkv_dtype kv_dtype,
-                                       pkv_dtype out_dtype, void* stream) {
-    g_last_error[0] = 0;
+namespace {
+
+// Shared body of the bf16 and fp8 prefill entry points (kv_fp8: E4M3 pools
+// with per-KV-head scales k_scale / v_scale).
+pkv_status prefill_impl(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                        const int32_t* context_lens, const int32_t* query_start_loc, float scale, void* out,
+                        int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t block_size, int64_t num_blocks, int32_t max_blocks_per_seq,
+                        int32_t max_context_len, bool kv_fp8, const float* k_scale, const float* v_scale,
+                        pkv_dtype out_dtype, void* stream) {
     if (num_seqs < 0 || num_tokens < 0) return fail(PKV_ERR_INVALID_ARG, "num_seqs and num_tokens must be >= 0");
     if (num_q_heads <= 0 || num_kv_heads <= 0)
         return fail(PKV_ERR_INVALID_ARG, "head counts must be positive (q %d, kv %d)", num_q_heads, num_kv_heads);
@@ -510,7 +512,6 @@ pkv_status pkv_paged_attention_prefill(const void* q, const void* k_cache, const
                     num_kv_heads);
     if (head_dim != 64 && head_dim != 128) return fail(PKV_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", head_dim);
     if (block_size != pkv::kBlockSize) return fail(PKV_ERR_UNSUPPORTED, "block_size %d (supported: 16)", block_size);
-    if (kv_dtype != PKV_BF16) return fail(PKV_ERR_UNSUPPORTED, "prefill supports bf16 KV only");
     if (!dtype_ok(out_dtype)) return fail(PKV_ERR_UNSUPPORTED, "unknown output dtype");
     if (max_blocks_per_seq < 0 || max_context_len < 0)
         return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq and max_context_len must be >= 0");
@@ -518,6 +519,7 @@ pkv_status pkv_paged_attention_prefill(const void* q, const void* k_cache, const
     if (num_seqs == 0 || num_tokens == 0) return PKV_OK;
     if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start_loc || !out)
         return fail(PKV_ERR_INVALID_ARG, "null tensor pointer");
+    if (kv_fp8 && (!k_scale || !v_scale)) return fail(PKV_ERR_INVALID_ARG, "an fp8 cache needs k_scale and v_scale");
     if (num_blocks <= 0) return fail(PKV_ERR_INVALID_ARG, "num_blocks must be positive");
     if (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)out) % 16)
         return fail(PKV_ERR_INVALID_ARG, "q, k_cache, v_cache and out must be 16-byte aligned");
@@ -540,6 +542,9 @@ pkv_status pkv_paged_attention_prefill(const void* q, const void* k_cache, const
     p.max_blocks_per_seq = max_blocks_per_seq;
     p.ctx_cap = (int32_t)(max_context_len < by_table ? max_context_len : by_table);
     p.out_bf16 = out_dtype == PKV_BF16;
+    p.kv_fp8 = kv_fp8 ? 1 : 0;
+    p.k_scale = k_scale;
+    p.v_scale = v_scale;
     const hipStream_t st = static_cast<hipStream_t>(stream);
     for (int32_t s0 = 0; s0 < num_seqs; s0 += pkv::kMaxSeqsPerLaunch) {
         const int32_t n = num_seqs - s0 < pkv::kMaxSeqsPerLaunch ? num_seqs - s0 : pkv::kMaxSeqsPerLaunch;
@@ -556,6 +561,36 @@ pkv_status pkv_paged_attention_prefill(const void* q, const void* k_cache, const
         if (rc != PKV_OK) return rc;
     }
     return PKV_OK;
+}
+
+}  // namespace
+
+pkv_status pkv_paged_attention_prefill(const void* q, const void* k_cache, const void* v_cache,
+                                       const int32_t* block_tables, const int32_t* context_lens,
+                                       const int32_t* query_start_loc, float scale, void* out, int32_t num_seqs,
+                                       int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                       int32_t max_blocks_per_seq, int32_t max_context_len, pkv_dtype kv_dtype,
+                                       pkv_dtype out_dtype, void* stream) {
+    g_last_error[0] = 0;
+    if (kv_dtype != PKV_BF16)
+        return fail(PKV_ERR_UNSUPPORTED, "prefill takes bf16 KV (fp8 pools: pkv_paged_attention_prefill_fp8)");
+    return prefill_impl(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, scale, out, num_seqs,
+                        num_tokens, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                        max_context_len, false, nullptr, nullptr, out_dtype, stream);
+}
+
+pkv_status pkv_paged_attention_prefill_fp8(const void* q, const void* k_cache, const void* v_cache,
+                                           const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                                           const int32_t* context_lens, const int32_t* query_start_loc, float scale,
+                                           void* out, int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                           int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                                           pkv_dtype out_dtype, void* stream) {
+    g_last_error[0] = 0;
+    return prefill_impl(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, scale, out, num_seqs,
+                        num_tokens, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                        max_context_len, true, k_scale, v_scale, out_dtype, stream);
 }
 
 }  // extern "C"

@@ -62,6 +62,61 @@ struct PairRegs {
     u32x4_t v[D / 16];   // dim 16c + l%16: A's tokens 4(l/16)..+3 in .xy, B's in .zw
 };
 
+// The same pair from an fp8 (E4M3) cache, as loaded: K load i holds the
+// 16-dim chunk 4i + l/16 of token l%16; V load i holds the 16-token row of
+// dim 64i + l.  widen_pair turns it into the bf16 operands above (every
+// E4M3 value is exact in bf16).
+template <int D>
+struct PairRegs8 {
+    uint4 k[2][D / 64];
+    uint4 v[2][D / 64];
+};
+
+template <bool kHigh>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+    // codes of bytes 2*kHigh, 2*kHigh + 1; scale 1.0: the exact value of each code
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHigh));
+}
+
+// K: the QK contraction takes dims in the order that makes step kk read half
+// (kk & 1) of chunk load kk / 2 (q is loaded in the same order).  V: word c
+// of lane (d, g) must hold tokens 4g..4g+3 of dim 16c + d, while lane
+// (d, r) loaded dims 64i + 16r + d: a 4 x 4 transpose of words between the
+// four 16-lane rows, in two rounds of row swaps.
+template <int D>
+__device__ __forceinline__ PairRegs<D> widen_pair(const PairRegs8<D>& r) {
+    PairRegs<D> o;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk) {
+            const uint4 w = r.k[b][kk >> 1];
+            const uint32_t x = (kk & 1) ? w.z : w.x;
+            const uint32_t y = (kk & 1) ? w.w : w.y;
+            o.k[b][kk] = make_uint4(e4m3x2_to_bf16x2<false>(x), e4m3x2_to_bf16x2<true>(x),
+                                    e4m3x2_to_bf16x2<false>(y), e4m3x2_to_bf16x2<true>(y));
+        }
+    uint32_t w[2][D / 16];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < D / 64; ++i) {
+            const auto a = __builtin_amdgcn_permlane32_swap(r.v[b][i].x, r.v[b][i].z, false, false);
+            const auto c = __builtin_amdgcn_permlane32_swap(r.v[b][i].y, r.v[b][i].w, false, false);
+            const auto e = __builtin_amdgcn_permlane16_swap(a[0], c[0], false, false);
+            const auto f = __builtin_amdgcn_permlane16_swap(a[1], c[1], false, false);
+            w[b][4 * i + 0] = e[0];
+            w[b][4 * i + 1] = e[1];
+            w[b][4 * i + 2] = f[0];
+            w[b][4 * i + 3] = f[1];
+        }
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+        o.v[c] = u32x4_t{e4m3x2_to_bf16x2<false>(w[0][c]), e4m3x2_to_bf16x2<true>(w[0][c]),
+                         e4m3x2_to_bf16x2<false>(w[1][c]), e4m3x2_to_bf16x2<true>(w[1][c])};
+    return o;
+}
+
 // Uniform facts about a pair: first logical block and valid tokens of A, B.
 struct PairInfo {
     int blk;
@@ -92,8 +147,10 @@ __device__ __forceinline__ uint32_t tail_mask(int nv, int first) {
     return nv >= first + 2 ? 0xFFFFFFFFu : (nv == first + 1 ? 0x0000FFFFu : 0u);
 }
 
-template <int D>
+template <int D, bool kFp8>
 __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(PrefillParams p) {
+    using Elem = std::conditional_t<kFp8, uint8_t, uint16_t>;  // one K/V pool element
+    using Ring = std::conditional_t<kFp8, PairRegs8<D>, PairRegs<D>>;
     extern __shared__ int32_t t_off[];  // [B + 1] first workgroup tile of each request
     __shared__ int32_t wave_total[kPrefillWaves];
     const int B = p.num_seqs;
@@ -192,8 +249,10 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(Prefil
     // Q^T operands: column tile j, k-group g holds dims 32kk + 8g .. +7.
     // A negative scale is carried by q (negating bf16 is exact), so the
     // softmax below works with c = |scale * log2 e| >= 0.
-    const float c_scale = fabsf(p.scale_log2);
-    const uint32_t qsign = p.scale_log2 < 0.f ? 0x80008000u : 0u;
+    // (an fp8 cache: K's scale joins the score scale, V's the output)
+    const float eff_scale = kFp8 ? p.scale_log2 * p.k_scale[kvh] : p.scale_log2;
+    const float c_scale = fabsf(eff_scale);
+    const uint32_t qsign = eff_scale < 0.f ? 0x80008000u : 0u;
     bf16x8_t qv[kNQ][D / 32];
     const uint16_t* qb = reinterpret_cast<const uint16_t*>(p.q);
 #pragma unroll
@@ -201,7 +260,9 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(Prefil
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk) {
             uint4 w = make_uint4(0, 0, 0, 0);
-            if (orow[j] >= 0) w = *reinterpret_cast<const uint4*>(qb + orow[j] + 32 * kk + 8 * g);
+            // fp8: step kk, group g takes dims 64(kk/2) + 16g + 8(kk&1) .. +7
+            const int dq = kFp8 ? 64 * (kk >> 1) + 16 * g + 8 * (kk & 1) : 32 * kk + 8 * g;
+            if (orow[j] >= 0) w = *reinterpret_cast<const uint4*>(qb + orow[j] + dq);
             w.x ^= qsign;
             w.y ^= qsign;
             w.z ^= qsign;
@@ -226,12 +287,12 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(Prefil
 
     if (NP > 0) {
         const int64_t block_stride = (int64_t)p.num_kv_heads * D * kBlockSize;
-        const uint16_t* k_head = reinterpret_cast<const uint16_t*>(p.k_cache) + (int64_t)kvh * D * kBlockSize;
-        const uint16_t* v_head = reinterpret_cast<const uint16_t*>(p.v_cache) + (int64_t)kvh * D * kBlockSize;
+        const Elem* k_head = reinterpret_cast<const Elem*>(p.k_cache) + (int64_t)kvh * D * kBlockSize;
+        const Elem* v_head = reinterpret_cast<const Elem*>(p.v_cache) + (int64_t)kvh * D * kBlockSize;
         const scalar_i32_ptr bt = (scalar_i32_ptr)(p.block_tables + (int64_t)s * p.max_blocks_per_seq);
         const int vo = (lane & 15) * 4 + (lane >> 4);
 
-        PairRegs<D> ring[kPairDepth];
+        Ring ring[kPairDepth];
         PairInfo info[kPairDepth];
         PairPending pend[kPairDepth];
 
@@ -256,27 +317,46 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(Prefil
         };
         auto load_pair = [&](int d, int pa, int pb, const PairInfo& inf) __attribute__((always_inline)) {
             info[d] = inf;
-            const u32x4_t* ka = reinterpret_cast<const u32x4_t*>(k_head + (int64_t)pa * block_stride);
-            const u32x4_t* kb = reinterpret_cast<const u32x4_t*>(k_head + (int64_t)pb * block_stride);
-            const u32x2_t* va = reinterpret_cast<const u32x2_t*>(v_head + (int64_t)pa * block_stride);
-            const u32x2_t* vb = reinterpret_cast<const u32x2_t*>(v_head + (int64_t)pb * block_stride);
             // ordinary loads: the other waves and workgroups of this request
             // read the same blocks
+            const u32x4_t* ka = reinterpret_cast<const u32x4_t*>(k_head + (int64_t)pa * block_stride);
+            const u32x4_t* kb = reinterpret_cast<const u32x4_t*>(k_head + (int64_t)pb * block_stride);
+            if constexpr (kFp8) {
+                const u32x4_t* va = reinterpret_cast<const u32x4_t*>(v_head + (int64_t)pa * block_stride);
+                const u32x4_t* vb = reinterpret_cast<const u32x4_t*>(v_head + (int64_t)pb * block_stride);
 #pragma unroll
-            for (int kk = 0; kk < D / 32; ++kk) ring[d].k[0][kk] = __builtin_bit_cast(uint4, ka[kk * 64 + lane]);
+                for (int i = 0; i < D / 64; ++i) ring[d].k[0][i] = __builtin_bit_cast(uint4, ka[i * 64 + lane]);
 #pragma unroll
-            for (int kk = 0; kk < D / 32; ++kk) ring[d].k[1][kk] = __builtin_bit_cast(uint4, kb[kk * 64 + lane]);
+                for (int i = 0; i < D / 64; ++i) ring[d].k[1][i] = __builtin_bit_cast(uint4, kb[i * 64 + lane]);
 #pragma unroll
-            for (int c = 0; c < D / 16; ++c) ring[d].v[c].xy = va[c * 64 + vo];
+                for (int i = 0; i < D / 64; ++i) ring[d].v[0][i] = __builtin_bit_cast(uint4, va[i * 64 + lane]);
 #pragma unroll
-            for (int c = 0; c < D / 16; ++c) ring[d].v[c].zw = vb[c * 64 + vo];
+                for (int i = 0; i < D / 64; ++i) ring[d].v[1][i] = __builtin_bit_cast(uint4, vb[i * 64 + lane]);
+            } else {
+                const u32x2_t* va = reinterpret_cast<const u32x2_t*>(v_head + (int64_t)pa * block_stride);
+                const u32x2_t* vb = reinterpret_cast<const u32x2_t*>(v_head + (int64_t)pb * block_stride);
+#pragma unroll
+                for (int kk = 0; kk < D / 32; ++kk) ring[d].k[0][kk] = __builtin_bit_cast(uint4, ka[kk * 64 + lane]);
+#pragma unroll
+                for (int kk = 0; kk < D / 32; ++kk) ring[d].k[1][kk] = __builtin_bit_cast(uint4, kb[kk * 64 + lane]);
+#pragma unroll
+                for (int c = 0; c < D / 16; ++c) ring[d].v[c].xy = va[c * 64 + vo];
+#pragma unroll
+                for (int c = 0; c < D / 16; ++c) ring[d].v[c].zw = vb[c * 64 + vo];
+            }
         };
 
         // One pair.  kMasked: the pair holds tokens past the context end or
         // past some row's position (the causal diagonal); otherwise every
         // score is live and the mask work is skipped.
-        auto compute_pair = [&](PairRegs<D>& r, const PairInfo& inf, auto masked_tag) __attribute__((always_inline)) {
+        auto compute_pair = [&](Ring& rr, const PairInfo& inf, auto masked_tag) __attribute__((always_inline)) {
             constexpr bool kMasked = decltype(masked_tag)::value;
+            PairRegs<D> rw;
+            if constexpr (kFp8) rw = widen_pair<D>(rr);
+            PairRegs<D>& r = [&]() -> PairRegs<D>& {
+                if constexpr (kFp8) return rw;
+                else return rr;
+            }();
             if constexpr (kMasked) {
                 // tokens past a block's valid count are zeroed in place (they
                 // may hold NaN, and 0 * NaN = NaN)
@@ -422,7 +502,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void prefill_bf16_kernel(Prefil
 #pragma unroll
     for (int j = 0; j < kNQ; ++j) {
         const float lt = sum_over_groups(st[j].l);
-        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        const float inv = lt > 0.f ? (kFp8 ? p.v_scale[kvh] : 1.f) / lt : 0.f;
         if (orow[j] < 0) continue;
         if (obf) {
             uint16_t* ob = reinterpret_cast<uint16_t*>(p.out) + orow[j] + 4 * g;
@@ -449,8 +529,13 @@ hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream) {
     if (p.num_seqs == 0 || p.tile_bound == 0) return hipSuccess;
     const dim3 grid((unsigned)((int64_t)p.tile_bound * p.num_kv_heads)), block(64 * kPrefillWaves);
     const size_t lds = prefill_lds_bytes(p.num_seqs);
-    if (p.head_dim == 128) hipLaunchKernelGGL((prefill_bf16_kernel<128>), grid, block, lds, stream, p);
-    else hipLaunchKernelGGL((prefill_bf16_kernel<64>), grid, block, lds, stream, p);
+    if (p.kv_fp8) {
+        if (p.head_dim == 128) hipLaunchKernelGGL((prefill_bf16_kernel<128, true>), grid, block, lds, stream, p);
+        else hipLaunchKernelGGL((prefill_bf16_kernel<64, true>), grid, block, lds, stream, p);
+    } else {
+        if (p.head_dim == 128) hipLaunchKernelGGL((prefill_bf16_kernel<128, false>), grid, block, lds, stream, p);
+        else hipLaunchKernelGGL((prefill_bf16_kernel<64, false>), grid, block, lds, stream, p);
+    }
     return hipGetLastError();
 }
 

@@ -52,6 +52,8 @@ _SIGNATURES = {
     "pkv_copy_blocks": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _vp]),
     "pkv_paged_attention_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                            _i64, _i32, _i32, _i32, _i32, _vp]),
+    "pkv_paged_attention_prefill_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _i32, _i32, _i32,
+                                               _i32, _i32, _i32, _i64, _i32, _i32, _i32, _vp]),
     "pkv_status_string": (ctypes.c_char_p, [_i32]),
     "pkv_last_error": (ctypes.c_char_p, []),
 }
@@ -250,23 +252,19 @@ def run_reduce(a: _DecodeArgs) -> None:
     _check(load_library().pkv_paged_attention_decode_reduce(*a.reduce_args), "paged_attention_decode_reduce")
 
 
-def paged_attention_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
-                            block_tables: torch.Tensor, context_lens: torch.Tensor, query_start_loc: torch.Tensor,
-                            scale: float, out: torch.Tensor, *, max_context_len: Optional[int] = None) -> None:
-    """Multi-token-query (chunked prefill) attention of ``q [T, Hq, D]`` into ``out``.
-
-    Request ``s`` owns rows ``query_start_loc[s] .. query_start_loc[s+1]-1``:
-    the last ``n_s`` of its ``context_lens[s]`` cached tokens, each attending
-    causally over its sequence.  bf16 KV only.
-    """
-    lib = load_library()
+def _prefill_args(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, out, max_context_len, fp8):
+    """Validated shapes of a prefill call: (B, T, Hq, Hkv, D, num_blocks, max_context_len)."""
     dev = q.device
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (block_tables, "block_tables"),
                  (context_lens, "context_lens"), (query_start_loc, "query_start_loc"), (out, "out")):
         _check_tensor(t, n, dev)
     nb, hkv, D = _pool_dims(k_cache, v_cache)
-    _require(k_cache.dtype == torch.bfloat16, "prefill supports bf16 KV only")
-    _require(q.dim() == 3 and q.shape[2] == D and q.dtype == k_cache.dtype, f"q must be bf16 [T, Hq, {D}]")
+    if fp8:
+        _require(k_cache.dtype in FP8_POOL_DTYPES and v_cache.dtype == k_cache.dtype,
+                 "fp8 pools must be uint8 or float8_e4m3fn")
+    else:
+        _require(k_cache.dtype == torch.bfloat16, "prefill takes bf16 pools (fp8: paged_attention_prefill_fp8)")
+    _require(q.dim() == 3 and q.shape[2] == D and q.dtype == torch.bfloat16, f"q must be bf16 [T, Hq, {D}]")
     T, hq = q.shape[0], q.shape[1]
     B = context_lens.shape[0] if context_lens.dim() == 1 else -1
     _require(context_lens.dtype == torch.int32 and B >= 0, "context_lens must be int32 [B]")
@@ -277,11 +275,42 @@ def paged_attention_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: tor
     _require(tuple(out.shape) == tuple(q.shape), "out must have q's shape")
     if max_context_len is None:  # costs a device->host synchronisation
         max_context_len = int(context_lens.max().item()) if B else 0
+    return B, T, hq, hkv, D, nb, int(max_context_len)
+
+
+def paged_attention_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                            block_tables: torch.Tensor, context_lens: torch.Tensor, query_start_loc: torch.Tensor,
+                            scale: float, out: torch.Tensor, *, max_context_len: Optional[int] = None) -> None:
+    """Multi-token-query (chunked prefill) attention of ``q [T, Hq, D]`` into ``out``.
+
+    Request ``s`` owns rows ``query_start_loc[s] .. query_start_loc[s+1]-1``:
+    the last ``n_s`` of its ``context_lens[s]`` cached tokens, each attending
+    causally over its sequence.  bf16 pools (fp8: ``paged_attention_prefill_fp8``).
+    """
+    lib = load_library()
+    B, T, hq, hkv, D, nb, mcl = _prefill_args(q, k_cache, v_cache, block_tables, context_lens, query_start_loc,
+                                              out, max_context_len, False)
     st = lib.pkv_paged_attention_prefill(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                                          _ptr(context_lens), _ptr(query_start_loc), float(scale), _ptr(out), B, T,
-                                         hq, hkv, D, BLOCK_SIZE, nb, block_tables.shape[1], int(max_context_len),
-                                         _dtype_code(k_cache), _dtype_code(out), _stream(dev))
+                                         hq, hkv, D, BLOCK_SIZE, nb, block_tables.shape[1], mcl,
+                                         _dtype_code(k_cache), _dtype_code(out), _stream(q.device))
     _check(st, "paged_attention_prefill")
+
+
+def paged_attention_prefill_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                k_scale: torch.Tensor, v_scale: torch.Tensor, block_tables: torch.Tensor,
+                                context_lens: torch.Tensor, query_start_loc: torch.Tensor, scale: float,
+                                out: torch.Tensor, *, max_context_len: Optional[int] = None) -> None:
+    """Chunked-prefill attention of bf16 ``q [T, Hq, D]`` over fp8 (E4M3) pools with per-KV-head scales."""
+    lib = load_library()
+    B, T, hq, hkv, D, nb, mcl = _prefill_args(q, k_cache, v_cache, block_tables, context_lens, query_start_loc,
+                                              out, max_context_len, True)
+    _check_scales(k_scale, v_scale, hkv, q.device)
+    st = lib.pkv_paged_attention_prefill_fp8(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                                             _ptr(block_tables), _ptr(context_lens), _ptr(query_start_loc),
+                                             float(scale), _ptr(out), B, T, hq, hkv, D, BLOCK_SIZE, nb,
+                                             block_tables.shape[1], mcl, _dtype_code(out), _stream(q.device))
+    _check(st, "paged_attention_prefill_fp8")
 
 
 def _check_scales(k_scale: torch.Tensor, v_scale: torch.Tensor, hkv: int, device) -> None:

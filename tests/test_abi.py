@@ -51,7 +51,7 @@ def test_single_hip_runtime_in_process(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pkv_abi_version() == 4
+    assert lib.pkv_abi_version() == 5
     for code in range(5):
         assert lib.pkv_status_string(code)
     assert lib.pkv_status_string(99) == b"unknown status"
@@ -170,8 +170,20 @@ def test_fp8_validation(lib):
     bad = list(args)
     bad[7] = 0
     assert lib.pkv_reshape_and_cache_fp8(*bad) == OK
-    # prefill over an fp8 cache is not offered
+    # prefill over an fp8 cache has its own entry point, which needs the scales
     assert pre(lib, kvd=FP8) == UNSUPPORTED
+    assert b"fp8" in lib.pkv_last_error()
+
+    def pre8(ks=FAKE, vs=FAKE, T=64, D=128, outd=BF16):
+        return lib.pkv_paged_attention_prefill_fp8(FAKE, FAKE, FAKE, ks, vs, FAKE, FAKE, FAKE, 0.1, FAKE, 4, T, 32, 8,
+                                                   D, 16, 100, 128, 2000, outd, None)
+    assert pre8(ks=None) == INVALID
+    assert b"k_scale" in lib.pkv_last_error()
+    assert pre8(vs=None) == INVALID
+    assert pre8(D=96) == UNSUPPORTED
+    assert pre8(outd=9) == UNSUPPORTED
+    assert pre8(T=0, ks=None, vs=None) == OK        # nothing to do: no launch
+    assert lib.pkv_last_error() == b""
 
 
 def test_copy_blocks_validation(lib):
