@@ -12,9 +12,11 @@
 //
 // A (block, pool) is Hkv * D * 16 elements, one contiguous run (32 KiB for
 // 8 heads x 128 dims of bf16).  One workgroup of 256 threads copies up to
-// 32 KiB of one pair and one pool with 16-byte non-temporal loads and
-// stores: the data is not read again by this kernel, and a copy should not
-// displace the blocks decode is about to read.
+// 32 KiB of one pair and one pool with 16-byte loads and stores.  Loads are
+// non-temporal and stores ordinary: the destination block is the one its
+// sequence writes and reads next.  (On 4096 pairs of the Llama shape this
+// measured 86 us, against 108 us with non-temporal stores too and 163 us
+// with ordinary loads and stores.)
 #include "kernels.h"
 
 namespace pkv {
@@ -52,8 +54,7 @@ __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(const uint4* src_
 #pragma unroll
     for (int i = 0; i < kUnroll; ++i) {
         const int u = u0 + i * kThreads;
-        if (u < units) __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, r[i]),
-                                                   reinterpret_cast<u32x4_t*>(dst) + u);
+        if (u < units) dst[u] = r[i];
     }
 }
 
