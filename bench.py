@@ -3,8 +3,12 @@
     python bench.py [--steps K] [--warmup W] [--config NAME] [--partition-size PS]
 
 One step is one pass of the whole hot path over one batch: the cache write of
-every sequence's new token (reshape_and_cache), the block-table-driven decode
-partitions, and the split-K reduce.  The default workload is the
+every sequence's new token, the block-table-driven decode partitions, and the
+split-K reduce: reshape_and_cache, then paged_attention_decode.  Where every
+sequence gains one bf16 token at position L - 1 (the static decode
+workloads), the fused form of the same step, whose decode launch stores the
+new tokens itself (paged_attention_decode_append), is timed beside it and
+reported under ``fused``; ``--fused`` makes it the measured step.  The default workload is the
 Llama-3-8B-shaped decode layer (64 sequences, 32 q / 8 KV heads, head_dim 128,
 bf16 KV, context lengths uniform on [128, 4096]).  Inputs are resident in HBM
 before timing starts.  To keep the 256 MB Infinity Cache from serving KV
@@ -48,8 +52,9 @@ def family(workload: str) -> str:
     return "decode"
 
 
-def traffic_file(workload: str) -> str:
-    return os.path.join(ROOT, "profiles", f"{family(workload)}_traffic_{workload}.json")
+def traffic_file(workload: str, fused: bool = False) -> str:
+    tag = "_fused" if fused else ""
+    return os.path.join(ROOT, "profiles", f"{family(workload)}_traffic_{workload}{tag}.json")
 
 
 def kernel_sources(workload: str):
@@ -64,14 +69,14 @@ def kernel_source_hash(workload: str = "llama3_8b_decode") -> str:
     return h.hexdigest()
 
 
-def measured_traffic(workload: str, partition_size: int):
+def measured_traffic(workload: str, partition_size: int, fused: bool = False):
     """Per-launch HBM bytes of the decode kernel from committed rocprofv3 counters.
 
     Null unless the counters were taken on this exact kernel source and
-    workload configuration.
+    workload configuration (and the same form of the step: fused or not).
     """
     try:
-        rec = json.load(open(traffic_file(workload)))
+        rec = json.load(open(traffic_file(workload, fused)))
     except (OSError, ValueError):
         return None
     if rec.get("source_sha256") != kernel_source_hash(workload):
@@ -227,7 +232,7 @@ def _short_kernel_name(k: str) -> str:
 
 
 def summarize_profile(prefix: str, workload: str, partition_size, copy_mib: int, out_md: str, out_json: str,
-                      commands: str) -> None:
+                      commands: str, fused: bool = False) -> None:
     """Turn rocprofv3 csv output (``<prefix>_trace``, ``_fetch``, ``_write``,
     ``_cal_fetch``, ``_cal_write``) into a short markdown summary and the
     per-launch traffic record ``measured_traffic`` reads."""
@@ -247,7 +252,8 @@ def summarize_profile(prefix: str, workload: str, partition_size, copy_mib: int,
     prefix_k = {"prefill": PREFILL_KERNEL_PREFIX, "copy": COPY_KERNEL_PREFIX}.get(family(workload), DECODE_KERNEL_PREFIX)
     short_k = prefix_k.split("::")[-1]
     dec = [k for k in fetch if short_k in k][0]
-    lines = [f"# rocprofv3: {family(workload)} kernels on the {workload} workload", "",
+    form = " (fused append step)" if fused else ""
+    lines = [f"# rocprofv3: {family(workload)} kernels on the {workload} workload{form}", "",
              "Commands (run from the repository root; `cd /tmp && export TMPDIR=/tmp` first):", "", "```",
              commands.strip(), "```", "", "## Kernel trace (`--kernel-trace --stats`)", "",
              "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
@@ -270,7 +276,8 @@ def summarize_profile(prefix: str, workload: str, partition_size, copy_mib: int,
     if os.path.exists(bench_log):
         last = [ln for ln in open(bench_log).read().splitlines() if ln.startswith("{")]
         if last:
-            lines += ["", f"## Bench line of the same build (`python bench.py --config {workload}`)", "", "```",
+            flag = " --fused" if fused else ""
+            lines += ["", f"## Bench line of the same build (`python bench.py --config {workload}{flag}`)", "", "```",
                       last[-1], "```"]
     rec = {"source_sha256": kernel_source_hash(workload), "workload": workload, "partition_size": partition_size,
            "kernel": dec, "fetch_kib_per_dispatch": fetch[dec], "write_kib_per_dispatch": write.get(dec, 0.0),
@@ -521,16 +528,22 @@ def main():
                     "_fetch, _write, _cal_fetch, _cal_write into profiles/ (no GPU needed)")
     ap.add_argument("--profile-copy-mib", type=int, default=1024)
     ap.add_argument("--profile-commands", default="")
+    ap.add_argument("--no-compare", action="store_true",
+                    help="run only the measured form of the step (for profiles: the kernel counts one form)")
+    ap.add_argument("--fused", action="store_true",
+                    help="measure the fused step (paged_attention_decode_append: the cache write inside the decode "
+                         "launch) where it applies")
     args = ap.parse_args()
 
     if args.summarize_profile:
         ps = args.partition_size if args.partition_size > 0 else "balanced"
         if family(args.config) != "decode":
             ps = "none"
+        tag = "_fused" if args.fused else ""
         summarize_profile(args.summarize_profile, args.config, ps, args.profile_copy_mib,
-                          os.path.join(ROOT, "profiles", f"{family(args.config)}_{args.config}.md"),
-                          traffic_file(args.config),
-                          open(args.profile_commands).read() if args.profile_commands else "")
+                          os.path.join(ROOT, "profiles", f"{family(args.config)}_{args.config}{tag}.md"),
+                          traffic_file(args.config, args.fused),
+                          open(args.profile_commands).read() if args.profile_commands else "", args.fused)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -614,7 +627,27 @@ def main():
                                              shared_blocks=g["shared"], k_scale=k_scale, v_scale=v_scale)
     resolved_ps = ps if ps else ("auto" if b.dtype == "f32" else "balanced")
 
-    def step(i, ev=None):
+    # The fused step applies when each sequence gains exactly one bf16 token,
+    # stored at position L - 1 of its table (the static decode workloads).
+    def append_slots(bt, lens):
+        lens = np.asarray(lens, dtype=np.int64)
+        pos = lens - 1
+        return np.asarray(bt, dtype=np.int64)[np.arange(len(lens)), pos // b.block_size] * b.block_size \
+            + pos % b.block_size
+    fusable = (b.dtype == "bf16" and b.num_q_heads // b.num_kv_heads <= 16 and
+               all(len(h[2]) == len(h[5]) and int(np.min(h[5])) >= 1 and
+                   np.array_equal(np.asarray(h[2], dtype=np.int64), append_slots(h[4], h[5])) for h in host_steps))
+    fused = fusable and args.fused
+    compare = fusable and not args.no_compare
+    fplans = {}
+    if fusable:
+        for j, g in enumerate(gpu_steps):
+            for r in range(R):
+                fplans[j, r] = ops.prepare_decode(g["q"], kcs[r], vcs[r], g["bt"], g["lens"], b.scale, g["out"],
+                                                  partition_size=ps, max_context_len=g["max_ctx"], workspace=ws,
+                                                  shared_blocks=g["shared"], k_new=g["k_new"], v_new=g["v_new"])
+
+    def step_two_call(i, ev=None):
         j, r = i % n_in, i % R
         g = gpu_steps[j]
         if fp8:
@@ -628,8 +661,21 @@ def main():
             ev[1].record()
         ops.run_reduce(plans[j, r])
 
+    def step_fused(i, ev=None):
+        j, r = i % n_in, i % R
+        if ev is not None:
+            ev[0].record()
+        ops.run_partitions(fplans[j, r])
+        if ev is not None:
+            ev[1].record()
+        ops.run_reduce(fplans[j, r])
+
+    step = step_fused if fused else step_two_call
+
     for i in range(args.warmup):
         step(i)
+        if compare:
+            (step_two_call if fused else step_fused)(i)
     torch.cuda.synchronize()
 
     # timed region 1: K whole steps, nothing but the kernels on the stream
@@ -639,6 +685,23 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     timed_kv = sum(step_kv[(args.warmup + i) % n_in] for i in range(args.steps))
+
+    # the other form of the same steps, for comparison: wall time, then the
+    # decode launch by events
+    other_wall = other_dec = None
+    if compare:
+        other = step_two_call if fused else step_fused
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for i in range(args.steps):
+            other(args.warmup + i)
+        torch.cuda.synchronize()
+        other_wall = time.perf_counter() - t1
+        oev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            other(args.warmup + i, oev[i])
+        torch.cuda.synchronize()
+        other_dec = sum(e[0].elapsed_time(e[1]) for e in oev) / args.steps
 
     # timed region 2: the same K steps with HIP events around each decode
     # launch (on the launch stream), for the decode kernel's own duration
@@ -653,7 +716,7 @@ def main():
     ms_per_step = wall / args.steps * 1e3
     value = timed_kv / wall / 1e9
     achieved = dec_kv / (sum(dec_times) / 1e3) / 1e9
-    traffic = measured_traffic(b.name, resolved_ps)
+    traffic = measured_traffic(b.name, resolved_ps, fused)
 
     rec = {
         "metric": METRIC,
@@ -675,6 +738,7 @@ def main():
                    "kv_bytes_per_step": int(round(kv_bytes)), "distinct_steps": n_in, "pool_bytes": pool_bytes,
                    "pool_replicas": R, "shared_blocks": any(g["shared"] for g in gpu_steps),
                    "kv_dtype": "fp8_e4m3" if fp8 else b.dtype},
+        "step": "fused append + decode + reduce" if fused else "cache write + decode + reduce",
         "frac_of_peak": round(value / PEAK_HBM_GBS, 4),
         "tokens_per_s": round(b.num_seqs / (ms_per_step / 1e3), 1),
         "decode_kernel_ms": round(dec, 5),
@@ -684,6 +748,11 @@ def main():
                      "bytes_per_launch": int(round(kv_bytes))},
         "input_generation_s": round(gen_s, 2),
     }
+    if other_wall is not None:
+        key = "two_call" if fused else "fused"
+        rec[key] = {"ms_per_step": round(other_wall / args.steps * 1e3, 5),
+                    "value": round(timed_kv / other_wall / 1e9, 2),
+                    "decode_kernel_ms": round(other_dec, 5)}
     try:
         rec["host_pack_h2d_ms"] = round(host_pack_ms(b), 4)
     except Exception as e:  # aux figure only

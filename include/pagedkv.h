@@ -197,6 +197,56 @@ pkv_status pkv_paged_attention_decode_reduce(const int32_t* context_lens, void* 
                                              void* stream);
 
 /*
+ * One decode step with the cache write fused into the decode launch: for
+ * every sequence s with L = context_lens[s] >= 1, store the token it gains
+ * this step, k_new[s][h][:] and v_new[s][h][:] for every KV head h, at
+ * position L - 1 of s (block_tables[s][(L - 1) / block_size], offset
+ * (L - 1) % block_size), then attend as pkv_paged_attention_decode.  The
+ * result, pool and out, is bit for bit that of pkv_reshape_and_cache with
+ * slot_mapping[s] = block_tables[s][(L - 1) / 16] * 16 + (L - 1) % 16
+ * followed by pkv_paged_attention_decode with the same sizes.  The decode
+ * step appends one token per sequence and then attends over the whole
+ * cache, the new token included (runbyai sections 1-2; architvora "Paged
+ * Attention": a new block is taken when the last one is full); the two
+ * steps share one launch here because, for each KV head, the workgroup
+ * that reads a sequence's last block is the one that stores its token.
+ *
+ *   k_new, v_new   [device] [num_seqs][num_kv_heads][head_dim], kv_dtype;
+ *                  k_new 16-byte aligned
+ *   k_cache, v_cache [device] pools, written at the appended slots
+ *   kv_dtype       PKV_BF16 only (others: PKV_ERR_UNSUPPORTED)
+ *   num_q_heads    at most 16 query heads per KV head (else
+ *                  PKV_ERR_UNSUPPORTED)
+ * All other arguments, the workspace and the flags as for
+ * pkv_paged_attention_decode.  The caller must have made the block that
+ * holds position L - 1 private to s (copy-on-write), as for any cache
+ * write; a table entry outside the pool is skipped, as the decode skips it.
+ * A context length above max_context_len (undefined for the decode) places
+ * the token at the clamped length.
+ */
+pkv_status pkv_paged_attention_decode_append(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                                             void* v_cache, const int32_t* block_tables,
+                                             const int32_t* context_lens, float scale, void* out, int32_t num_seqs,
+                                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                             int32_t block_size, int64_t num_blocks, int32_t max_blocks_per_seq,
+                                             int32_t max_context_len, int32_t partition_size, void* workspace,
+                                             size_t workspace_bytes, pkv_dtype kv_dtype, pkv_dtype out_dtype,
+                                             uint32_t flags, void* stream);
+
+/* The decode launch of pkv_paged_attention_decode_append on its own (the
+ * append included); follow it with pkv_paged_attention_decode_reduce on the
+ * same stream with the same sizes and workspace. */
+pkv_status pkv_paged_attention_decode_append_partitions(const void* q, const void* k_new, const void* v_new,
+                                                        void* k_cache, void* v_cache, const int32_t* block_tables,
+                                                        const int32_t* context_lens, float scale, void* out,
+                                                        int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                                        int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                                        int32_t max_blocks_per_seq, int32_t max_context_len,
+                                                        int32_t partition_size, void* workspace,
+                                                        size_t workspace_bytes, pkv_dtype kv_dtype,
+                                                        pkv_dtype out_dtype, uint32_t flags, void* stream);
+
+/*
  * fp8 KV cache.  The pages name quantisation of the KV cache as the lever for
  * long contexts (runbyai section 5); they fix no format.  Here a pool element
  * is an OCP E4M3 code (1 sign bit, 4 exponent bits with bias 7, 3 mantissa

@@ -140,11 +140,14 @@ __device__ __forceinline__ void fp8_v_words(const SlotRegs8<D>& r, uint32_t* w) 
 // Uniform facts about the block a ring slot holds.
 struct SlotInfo {
     int seq;    // sequence
-    int meta;   // valid tokens (0..16) | kSegLast
+    int meta;   // valid tokens (0..16) | kSegLast | kSeqEnd
     int slot;   // partial row pair index, or -1 when the sequence completes here
+    int pb;     // physical block loaded into the slot
 };
 
 constexpr int kSegLast = 1 << 5;  // this block ends a segment (sequence or range)
+constexpr int kSeqEnd = 1 << 6;   // fused append: the sequence's last block, which holds its new token
+constexpr int kAppendSlots = 4;   // fused append: new-token rows a wave keeps in LDS
 constexpr int kCoherent = 16;     // buffer cache policy: sc1 (device scope, write-through)
 constexpr int kBufferWord3 = 0x00020000;  // buffer descriptor word 3: 32-bit raw data
 
@@ -264,7 +267,7 @@ __device__ __forceinline__ void compute_block(const Slot& r, float4_t* acc, Soft
 struct Window {
     int seq;    // sequence
     int blk;    // logical block within the sequence
-    int meta;   // valid tokens (1..16) | kSegLast
+    int meta;   // valid tokens (1..16) | kSegLast | kSeqEnd
     int slot;   // partial row pair index, -1 = the sequence completes in this range
 };
 
@@ -277,11 +280,17 @@ struct Pending {
 
 typedef const int32_t __attribute__((address_space(4)))* scalar_i32_ptr;
 
+// Dynamic LDS of the balanced kernel: the flattened offsets and lengths of
+// the batch ([B + 1] and [B] int32), then, with the fused append, each
+// wave's kAppendSlots new-token rows (K and V, D bf16 each) from a 16-byte
+// boundary.
+__host__ __device__ inline int append_rows_offset(int num_seqs) { return (2 * num_seqs + 1 + 3) & ~3; }
+
 template <int D, int kDepth, bool kCached, bool kFp8, bool kPackLo>
 __global__ __launch_bounds__(64 * kMaxWavesPerGroup) void decode_bf16_balanced_kernel(DecodeParams p) {
     using Elem = std::conditional_t<kFp8, uint8_t, uint16_t>;  // one K/V pool element
     using Slot = std::conditional_t<kFp8, SlotRegs8<D>, SlotRegs<D>>;
-    extern __shared__ int32_t tables[];
+    extern __shared__ __align__(16) int32_t tables[];
     __shared__ int32_t wave_total[kMaxWavesPerGroup];
     const int B = p.num_seqs;
     int32_t* s_off = tables;          // [B + 1] first flattened block of each sequence
@@ -363,6 +372,7 @@ __global__ __launch_bounds__(64 * kMaxWavesPerGroup) void decode_bf16_balanced_k
     const int n_ranges = (NR - 1 - walker) / NG + 1;
     const int r_final = walker + NG * (n_ranges - 1);
     const int K = (n_ranges - 1) * CS + min(CS, T - r_final * CS);  // blocks this workgroup walks
+    const bool appending = !kFp8 && p.k_new != nullptr;  // fused append of the new tokens
 
     // last sequence starting at or before flattened block f (it holds block f)
     auto seq_of_block = [&](int f) {
@@ -407,7 +417,8 @@ __global__ __launch_bounds__(64 * kMaxWavesPerGroup) void decode_bf16_balanced_k
             const int j = f - o0;
             w.seq = lo;
             w.blk = j;
-            w.meta = min(kBlockSize, s_len[lo] - j * kBlockSize) | ((f == re - 1 || f == o1 - 1) ? kSegLast : 0);
+            w.meta = min(kBlockSize, s_len[lo] - j * kBlockSize) | ((f == re - 1 || f == o1 - 1) ? kSegLast : 0) |
+                     (appending && f == o1 - 1 ? kSeqEnd : 0);
             w.slot = (o0 >= rs && o1 <= re) ? -1 : range_slot(r, CS, o0);
         }
     };
@@ -436,6 +447,146 @@ __global__ __launch_bounds__(64 * kMaxWavesPerGroup) void decode_bf16_balanced_k
         e.info.slot = __builtin_amdgcn_readlane(cur.slot, li);
     };
 
+    // Fused append (p.k_new set): the token each sequence gains this step
+    // goes to position L - 1, in the sequence's last block.  For each KV
+    // head that block is walked by exactly one wave (the launch has one
+    // head group per KV head), the one whose range holds it, so that wave
+    // does the whole append: it keeps the token's K/V rows in its LDS rows
+    // (the first kAppendSlots tokens of its walk), writes them into the
+    // block's registers once the block's loads have arrived, and stores
+    // them into the pool when its walk is done.  The wave never reads pool
+    // lines it has written, and no other wave reads the slot.  Tokens past the
+    // first kAppendSlots of a walk (short sequences) are stored into the
+    // pool before the walk instead, and read back from it.  A table entry
+    // outside the pool is skipped, as the walk skips it.
+    using Row = uint16_t;  // bf16 pools
+    Row* const ap_rows = reinterpret_cast<Row*>(tables + append_rows_offset(B)) + wave * (kAppendSlots * 2 * D);
+    // next sequence, from cursor (ri, s) on, whose last block lies in range
+    // ri of this walk; -1 when none is left
+    auto next_append = [&](int& ri, int& s) -> int {
+        for (; ri < n_ranges; ++ri) {
+            const int rs = (walker + NG * ri) * CS;
+            const int re = min(rs + CS, T);
+            if (s < 0) s = __builtin_amdgcn_readfirstlane(seq_of_block(rs));
+            for (; s < B; ++s) {
+                const int o0 = __builtin_amdgcn_readfirstlane(s_off[s]);
+                if (o0 >= re) break;
+                const int o1 = __builtin_amdgcn_readfirstlane(s_off[s + 1]);
+                if (o1 > o0 && o1 > rs && o1 <= re) return s++;
+            }
+            s = -1;
+        }
+        return -1;
+    };
+    struct NewRow {
+        uint4 k;                    // lanes < D/8: 16-byte chunk `lane` of the K row
+        uint32_t v[(D + 63) / 64];  // dim lane + 64i of the V row
+    };
+    auto load_new_row = [&](int s, NewRow& a) {
+        const int64_t src = ((int64_t)s * p.num_kv_heads + kvh) * D;
+        a.k = lane < D / 8 ? reinterpret_cast<const uint4*>(reinterpret_cast<const Row*>(p.k_new) + src)[lane]
+                           : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < (D + 63) / 64; ++i)
+            a.v[i] = lane + 64 * i < D ? reinterpret_cast<const Row*>(p.v_new)[src + lane + 64 * i] : 0u;
+    };
+    Row* const kc_base = reinterpret_cast<Row*>(const_cast<void*>(p.k_cache)) + (int64_t)kvh * D * kBlockSize;
+    Row* const vc_base = reinterpret_cast<Row*>(const_cast<void*>(p.v_cache)) + (int64_t)kvh * D * kBlockSize;
+    int ap_ri = 0, ap_s = -1;
+    int ap_count = 0;  // rows kept in LDS
+    int ap_used = 0;   // sequence ends the walk has reached
+    NewRow ap_row[kAppendSlots];
+    if constexpr (!kFp8) {
+        if (appending) {
+            // rows of the first kAppendSlots ends, requested before the
+            // walk's first table fetches and written to LDS after them
+#pragma unroll
+            for (int j = 0; j < kAppendSlots; ++j) {
+                const int s = ap_count == j ? next_append(ap_ri, ap_s) : -1;
+                if (s >= 0) {
+                    load_new_row(s, ap_row[j]);
+                    ++ap_count;
+                }
+            }
+        }
+    }
+    // Rows to LDS; then the ends past the first kAppendSlots, stored into
+    // the pool before the walk.
+    auto append_prologue = [&]() {
+#pragma unroll
+        for (int j = 0; j < kAppendSlots; ++j) {
+            if (j < ap_count) {
+                Row* r = ap_rows + j * 2 * D;
+                if (lane < D / 8) reinterpret_cast<uint4*>(r)[lane] = ap_row[j].k;
+#pragma unroll
+                for (int i = 0; i < (D + 63) / 64; ++i)
+                    if (lane + 64 * i < D) r[D + lane + 64 * i] = (Row)ap_row[j].v[i];
+            }
+        }
+        if (ap_count < kAppendSlots) return;
+        for (int s = next_append(ap_ri, ap_s); s >= 0; s = next_append(ap_ri, ap_s)) {
+            const int pos = __builtin_amdgcn_readfirstlane(s_len[s]) - 1;
+            const int e = bt[(int64_t)s * p.max_blocks_per_seq + pos / kBlockSize];
+            NewRow a;
+            load_new_row(s, a);
+            if (e < 0 || (int64_t)e >= p.num_blocks) continue;
+            const int o = pos % kBlockSize;
+            Row* kc = kc_base + (int64_t)e * block_stride;
+            Row* vc = vc_base + (int64_t)e * block_stride;
+            // K tile [D/8][16][8]: chunk c of token o at (16c + o) * 8;
+            // V tile [D][16]: dim d of token o at 16d + o
+            if (lane < D / 8) reinterpret_cast<uint4*>(kc)[lane * kBlockSize + o] = a.k;
+#pragma unroll
+            for (int i = 0; i < (D + 63) / 64; ++i)
+                if (lane + 64 * i < D) vc[(lane + 64 * i) * kBlockSize + o] = (Row)a.v[i];
+        }
+    };
+    // The new token (position o of the block in ring slot r, LDS row j) in
+    // the slot's operand registers: K chunk 4kk + g of token lane % 16, and
+    // V dims 16c + lane % 16 of tokens 4g..4g+3 (two per 32-bit word).
+    auto patch_slot = [&](SlotRegs<D>& r, int j, int o) {
+        const Row* row = ap_rows + j * 2 * D;
+        const bool kt = (lane & 15) == o;
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk) {
+            const uint4 w = reinterpret_cast<const uint4*>(row)[4 * kk + g];
+            if (kt) r.k[kk] = w;
+        }
+        const bool vt = g == (o >> 2);
+        const uint32_t sh = (o & 1) * 16;
+        const uint32_t keep = ~(0xFFFFu << sh);
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) {
+            const uint32_t x = (uint32_t)row[D + 16 * c + (lane & 15)] << sh;
+            if (vt) {
+                if (o & 2) r.v[c].y = (r.v[c].y & keep) | x;
+                else r.v[c].x = (r.v[c].x & keep) | x;
+            }
+        }
+    };
+    // The new token of LDS row j into position o of pool block pb, after
+    // the walk's last wait.  On this chip stores share the in-order counter
+    // of the loads, so a store issued inside the walk makes the next waits
+    // for KV blocks wait on it too.  Measured on the Llama-shaped batch
+    // (decode launch): stores after the walk 100.6 us; the token stored
+    // when its block is reached 103.9 us; the whole patched tile written
+    // back there 105.5 us; the token stored into the pool before the walk
+    // and read back 102.6 us (streaming stores) or 108.5 us (ordinary).
+    auto store_token = [&](int j, int pb, int o) {
+        const Row* row = ap_rows + j * 2 * D;
+        Row* kc = kc_base + (int64_t)pb * block_stride;
+        Row* vc = vc_base + (int64_t)pb * block_stride;
+        if (lane < D / 8)
+            __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, reinterpret_cast<const uint4*>(row)[lane]),
+                                        reinterpret_cast<u32x4_t*>(kc) + lane * kBlockSize + o);
+#pragma unroll
+        for (int i = 0; i < (D + 63) / 64; ++i)
+            if (lane + 64 * i < D) __builtin_nontemporal_store(row[D + lane + 64 * i], vc + (lane + 64 * i) * kBlockSize + o);
+    };
+    int ap_pb[kAppendSlots], ap_o[kAppendSlots];
+#pragma unroll
+    for (int j = 0; j < kAppendSlots; ++j) ap_pb[j] = ap_o[j] = -1;
+
     Slot ring[kDepth];
     SlotInfo info[kDepth];
     Pending pend[kDepth];
@@ -448,7 +599,7 @@ __global__ __launch_bounds__(64 * kMaxWavesPerGroup) void decode_bf16_balanced_k
         const bool ok = e.raw >= 0 && (int64_t)e.raw < p.num_blocks;
         pb = ok ? e.raw : 0;
         inf = e.info;
-        if (!ok) inf.meta &= kSegLast;
+        if (!ok) inf.meta &= kSegLast | kSeqEnd;
         asm volatile("" : "+s"(pb));
     };
 
@@ -456,6 +607,7 @@ __global__ __launch_bounds__(64 * kMaxWavesPerGroup) void decode_bf16_balanced_k
     // vector loads, so the wait before a block covers only that block's loads.
     auto load_slot = [&](int d, int pb, const SlotInfo& inf) {
         info[d] = inf;
+        info[d].pb = pb;
         const uint4* qr = reinterpret_cast<const uint4*>(q_base + (int64_t)info[d].seq * Hq * D);
         if constexpr (kFp8) {
             const u32x4_t* kt = reinterpret_cast<const u32x4_t*>(k_head + (int64_t)pb * block_stride);
@@ -559,6 +711,9 @@ __global__ __launch_bounds__(64 * kMaxWavesPerGroup) void decode_bf16_balanced_k
     SlotInfo next_info[kDepth];
 #pragma unroll
     for (int d = 0; d < kDepth; ++d) fetch(d, pend[d]);
+    if constexpr (!kFp8) {
+        if (appending) append_prologue();
+    }
 #pragma unroll
     for (int d = 0; d < kDepth; ++d) accept(pend[d], next_pb[d], next_info[d]);
 #pragma unroll
@@ -583,8 +738,30 @@ __global__ __launch_bounds__(64 * kMaxWavesPerGroup) void decode_bf16_balanced_k
 #pragma unroll
         for (int d = 0; d < kDepth; ++d) {
             if (!kFinal || i + d < K) {
+                // fused append: the block that holds a sequence's new token
+                bool patched = false;
+                if constexpr (!kFp8) {
+                    if (info[d].meta & kSeqEnd) {
+                        const int nv = info[d].meta & 31;
+                        patched = ap_used < ap_count && nv > 0;
+                        if (patched) patch_slot(ring[d], ap_used, nv - 1);
+                        ++ap_used;
+                    }
+                }
                 compute_block<D, kPackLo>(ring[d], acc, st, info[d].meta & 31, score_scale, g, lo_mask);
-                if (info[d].meta & kSegLast) finish_segment(info[d].seq, info[d].slot);
+                if (info[d].meta & kSegLast) {
+                    finish_segment(info[d].seq, info[d].slot);
+                    if constexpr (!kFp8) {
+                        if (patched) {  // stored after the walk
+#pragma unroll
+                            for (int j = 0; j < kAppendSlots; ++j)
+                                if (j == ap_used - 1) {
+                                    ap_pb[j] = info[d].pb;
+                                    ap_o[j] = (info[d].meta & 31) - 1;
+                                }
+                        }
+                    }
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
             if (!kFinal || i + d + kDepth < K) load_slot(d, next_pb[d], next_info[d]);
@@ -594,6 +771,12 @@ __global__ __launch_bounds__(64 * kMaxWavesPerGroup) void decode_bf16_balanced_k
     int i = 0;
     for (; i + 2 * kDepth <= K; i += kDepth) round(i, std::false_type{});
     for (; i < K; i += kDepth) round(i, std::true_type{});
+    // fused append: the new tokens patched in above, into the pool
+    if constexpr (!kFp8) {
+#pragma unroll
+        for (int j = 0; j < kAppendSlots; ++j)
+            if (ap_pb[j] >= 0) store_token(j, ap_pb[j], ap_o[j]);
+    }
 
 }
 
@@ -601,12 +784,19 @@ __global__ __launch_bounds__(64 * kMaxWavesPerGroup) void decode_bf16_balanced_k
 
 size_t balanced_lds_bytes(int32_t num_seqs) { return (size_t)(2 * num_seqs + 1) * sizeof(int32_t); }
 
+size_t balanced_lds_bytes(const DecodeParams& p) {
+    if (p.k_new == nullptr || p.kv_fp8) return balanced_lds_bytes(p.num_seqs);
+    return (size_t)append_rows_offset(p.num_seqs) * sizeof(int32_t) +
+           (size_t)p.waves_per_group * kAppendSlots * 2 * p.head_dim * sizeof(uint16_t);
+}
+
 const void* balanced_kernel(int32_t head_dim) {
-    // the plan sizes the grid from the streaming variant's occupancy; the
-    // cached variant needs no more registers or LDS
+    // the plan sizes the grid from the occupancy of the streaming bf16
+    // variant with packed lo terms (the one bf16 groups of up to 8 heads
+    // run); the other variants need no more registers or LDS
     return head_dim == 128
-               ? reinterpret_cast<const void*>(&decode_bf16_balanced_kernel<128, kPrefetchBlocks, false, false, false>)
-               : reinterpret_cast<const void*>(&decode_bf16_balanced_kernel<64, kPrefetchBlocks, false, false, false>);
+               ? reinterpret_cast<const void*>(&decode_bf16_balanced_kernel<128, kPrefetchBlocks, false, false, true>)
+               : reinterpret_cast<const void*>(&decode_bf16_balanced_kernel<64, kPrefetchBlocks, false, false, true>);
 }
 
 template <int D, bool kFp8, bool kPackLo>
@@ -630,7 +820,7 @@ void launch_balanced(const DecodeParams& p, dim3 grid, dim3 block, size_t lds, h
 hipError_t launch_decode_bf16_balanced(const DecodeParams& p, hipStream_t stream) {
     if (p.num_seqs == 0) return hipSuccess;
     const dim3 grid((unsigned)((int64_t)p.walkers * p.head_unit_groups)), block(64 * p.waves_per_group);
-    const size_t lds = balanced_lds_bytes(p.num_seqs);
+    const size_t lds = balanced_lds_bytes(p);
     if (p.kv_fp8) {
         if (p.head_dim == 128) launch_balanced<128, true>(p, grid, block, lds, stream);
         else launch_balanced<64, true>(p, grid, block, lds, stream);

@@ -147,6 +147,7 @@ struct Call {
     pkv_dtype kv_dtype;
     size_t q_row_bytes;    // bytes of q per sequence
     size_t out_row_bytes;  // bytes of out per sequence
+    size_t new_row_bytes;  // fused append: bytes of k_new / v_new per sequence
     char* workspace;
 };
 
@@ -216,6 +217,7 @@ pkv_status prepare(const void* q, const void* k_cache, const void* v_cache, cons
     c->kv_dtype = kv_dtype;
     c->q_row_bytes = (size_t)num_q_heads * head_dim * (kv_dtype == PKV_F32 ? 4 : 2);  // q is bf16 for fp8 caches
     c->out_row_bytes = (size_t)num_q_heads * head_dim * (out_dtype == PKV_BF16 ? 2 : 4);
+    c->new_row_bytes = 0;
     c->workspace = static_cast<char*>(workspace);
     return PKV_OK;
 }
@@ -232,6 +234,10 @@ pkv::DecodeParams chunk_params(const Call& c, int32_t i) {
     p.out = static_cast<char*>(c.base.out) + (size_t)s0 * c.out_row_bytes;
     p.block_tables = c.base.block_tables + (int64_t)s0 * c.base.max_blocks_per_seq;
     p.context_lens = c.base.context_lens + s0;
+    if (c.base.k_new) {
+        p.k_new = static_cast<const char*>(c.base.k_new) + (size_t)s0 * c.new_row_bytes;
+        p.v_new = static_cast<const char*>(c.base.v_new) + (size_t)s0 * c.new_row_bytes;
+    }
     char* w = c.workspace + (size_t)i * pl.chunk_bytes;
     p.seq_off = reinterpret_cast<int32_t*>(w);
     const size_t rows = (size_t)(2 * pl.max_ranges) * c.base.num_q_heads;
@@ -263,11 +269,36 @@ pkv_status run_reduce_kernels(const Call& c, hipStream_t stream) {
     return PKV_OK;
 }
 
+// A decode call with the new tokens' append fused into its decode launch.
+pkv_status prepare_append(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                          const int32_t* block_tables, const int32_t* context_lens, float scale, void* out,
+                          int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t block_size, int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                          int32_t partition_size, void* workspace, size_t workspace_bytes, pkv_dtype kv_dtype,
+                          pkv_dtype out_dtype, uint32_t flags, Call* c) {
+    if (kv_dtype != PKV_BF16)
+        return fail(PKV_ERR_UNSUPPORTED, "the fused append takes bf16 pools (use pkv_reshape_and_cache and the decode)");
+    pkv_status st = prepare(q, k_cache, v_cache, block_tables, context_lens, scale, out, num_seqs, num_q_heads,
+                            num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len,
+                            partition_size, workspace, workspace_bytes, kv_dtype, out_dtype, flags, nullptr, nullptr,
+                            c);
+    if (st != PKV_OK) return st;
+    if (c->plan.n_head_groups != 1)
+        return fail(PKV_ERR_UNSUPPORTED, "the fused append takes at most %d query heads per KV head (got %d)",
+                    pkv::kMfmaHeadsPerUnit, c->plan.group);
+    if (num_seqs > 0 && (!k_new || !v_new)) return fail(PKV_ERR_INVALID_ARG, "null k_new or v_new");
+    if ((uintptr_t)k_new % 16) return fail(PKV_ERR_INVALID_ARG, "k_new must be 16-byte aligned");
+    c->base.k_new = k_new;
+    c->base.v_new = v_new;
+    c->new_row_bytes = (size_t)num_kv_heads * head_dim * sizeof(uint16_t);
+    return PKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
-int32_t pkv_abi_version(void) { return 5; }
+int32_t pkv_abi_version(void) { return 6; }
 
 const char* pkv_status_string(pkv_status status) {
     switch (status) {
@@ -369,6 +400,45 @@ pkv_status pkv_paged_attention_decode(const void* q, const void* k_cache, const 
     st = run_decode_kernels(c, s);
     if (st != PKV_OK) return st;
     return run_reduce_kernels(c, s);
+}
+
+pkv_status pkv_paged_attention_decode_append(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                                             void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                                             float scale, void* out, int32_t num_seqs, int32_t num_q_heads,
+                                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                             int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                                             int32_t partition_size, void* workspace, size_t workspace_bytes,
+                                             pkv_dtype kv_dtype, pkv_dtype out_dtype, uint32_t flags, void* stream) {
+    g_last_error[0] = 0;
+    Call c;
+    pkv_status st = prepare_append(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, out, num_seqs,
+                                   num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                                   max_context_len, partition_size, workspace, workspace_bytes, kv_dtype, out_dtype,
+                                   flags, &c);
+    if (st != PKV_OK) return st;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    st = run_decode_kernels(c, s);
+    if (st != PKV_OK) return st;
+    return run_reduce_kernels(c, s);
+}
+
+pkv_status pkv_paged_attention_decode_append_partitions(const void* q, const void* k_new, const void* v_new,
+                                                        void* k_cache, void* v_cache, const int32_t* block_tables,
+                                                        const int32_t* context_lens, float scale, void* out,
+                                                        int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                                        int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                                        int32_t max_blocks_per_seq, int32_t max_context_len,
+                                                        int32_t partition_size, void* workspace,
+                                                        size_t workspace_bytes, pkv_dtype kv_dtype,
+                                                        pkv_dtype out_dtype, uint32_t flags, void* stream) {
+    g_last_error[0] = 0;
+    Call c;
+    pkv_status st = prepare_append(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, out, num_seqs,
+                                   num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                                   max_context_len, partition_size, workspace, workspace_bytes, kv_dtype, out_dtype,
+                                   flags, &c);
+    if (st != PKV_OK) return st;
+    return run_decode_kernels(c, static_cast<hipStream_t>(stream));
 }
 
 pkv_status pkv_reshape_and_cache_fp8(const void* k_new, const void* v_new, const int64_t* slot_mapping,

@@ -43,6 +43,11 @@ _SIGNATURES = {
                                                      _i64, _i32, _i32, _i32, _vp, _sz, _i32, _i32, _u32, _vp]),
     "pkv_paged_attention_decode_reduce": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _sz,
                                                  _i32, _i32, _vp]),
+    "pkv_paged_attention_decode_append": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _i32, _i32, _i32, _i32,
+                                                 _i32, _i64, _i32, _i32, _i32, _vp, _sz, _i32, _i32, _u32, _vp]),
+    "pkv_paged_attention_decode_append_partitions": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _i32, _i32,
+                                                            _i32, _i32, _i32, _i64, _i32, _i32, _i32, _vp, _sz, _i32,
+                                                            _i32, _u32, _vp]),
     "pkv_reshape_and_cache_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _i32, _vp]),
     "pkv_paged_attention_decode_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _i32, _i32, _i32, _i32, _i32,
                                               _i64, _i32, _i32, _i32, _vp, _sz, _i32, _u32, _vp]),
@@ -158,9 +163,11 @@ class _DecodeArgs:
     """Validated decode arguments, reused by the one-call and two-phase entry points."""
 
     def __init__(self, q, k_cache, v_cache, block_tables, context_lens, scale, out, partition_size,
-                 max_context_len, workspace, shared_blocks=False, k_scale=None, v_scale=None):
+                 max_context_len, workspace, shared_blocks=False, k_scale=None, v_scale=None, k_new=None,
+                 v_new=None):
         dev = q.device
         self.fp8 = k_cache.dtype in FP8_POOL_DTYPES
+        self.append = k_new is not None or v_new is not None
         for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (block_tables, "block_tables"),
                      (context_lens, "context_lens"), (out, "out")):
             _check_tensor(t, n, dev)
@@ -191,7 +198,19 @@ class _DecodeArgs:
         self.ws_ptr = _ptr(workspace) if workspace is not None else None
         self.ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
         flags = DECODE_SHARED_BLOCKS if shared_blocks else 0
-        if self.fp8:
+        if self.append:
+            _require(not self.fp8 and k_cache.dtype == torch.bfloat16, "the fused append takes bf16 pools")
+            _require(k_new is not None and v_new is not None, "the fused append needs both k_new and v_new")
+            _check_tensor(k_new, "k_new", dev)
+            _check_tensor(v_new, "v_new", dev)
+            _require(tuple(k_new.shape) == (B, hkv, D) and tuple(v_new.shape) == (B, hkv, D),
+                     f"k_new and v_new must be [B, {hkv}, {D}]")
+            _require(k_new.dtype == k_cache.dtype and v_new.dtype == k_cache.dtype, "new K/V dtype must match the pools")
+            self.args = (_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                         _ptr(context_lens), float(scale), _ptr(out), B, hq, hkv, D, BLOCK_SIZE, nb,
+                         block_tables.shape[1], self.max_context_len, self.partition_size, self.ws_ptr,
+                         self.ws_bytes, _dtype_code(k_cache), _dtype_code(out), flags, _stream(dev))
+        elif self.fp8:
             self.args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
                          _ptr(context_lens), float(scale), _ptr(out), B, hq, hkv, D, BLOCK_SIZE, nb,
                          block_tables.shape[1], self.max_context_len, self.partition_size, self.ws_ptr,
@@ -223,18 +242,37 @@ def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
     _check(load_library().pkv_paged_attention_decode(*a.args), "paged_attention_decode")
 
 
+def paged_attention_decode_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                                  k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
+                                  context_lens: torch.Tensor, scale: float, out: torch.Tensor, *,
+                                  partition_size: int = 0, max_context_len: Optional[int] = None,
+                                  workspace: Optional[torch.Tensor] = None, shared_blocks: bool = False) -> None:
+    """One decode step in one launch pair: store ``k_new``/``v_new [B, Hkv, D]`` (bf16) at position
+    ``context_lens[s] - 1`` of each sequence, then attend as ``paged_attention_decode``.
+
+    Pool and output equal ``reshape_and_cache`` with the slots of those positions followed by
+    ``paged_attention_decode``, bit for bit; at most 16 query heads per KV head.
+    """
+    a = _DecodeArgs(q, k_cache, v_cache, block_tables, context_lens, scale, out, partition_size, max_context_len,
+                    workspace, shared_blocks, k_new=k_new, v_new=v_new)
+    _check(load_library().pkv_paged_attention_decode_append(*a.args), "paged_attention_decode_append")
+
+
 def prepare_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out, *, partition_size=0,
                    max_context_len=None, workspace=None, shared_blocks=False, k_scale=None,
-                   v_scale=None) -> _DecodeArgs:
+                   v_scale=None, k_new=None, v_new=None) -> _DecodeArgs:
     """Validate once; the returned object drives ``run_partitions`` / ``run_reduce`` repeatedly.
-    fp8 pools (uint8 / float8_e4m3fn) take ``k_scale`` / ``v_scale``."""
+    fp8 pools (uint8 / float8_e4m3fn) take ``k_scale`` / ``v_scale``; ``k_new`` / ``v_new`` select the
+    fused append (``paged_attention_decode_append``)."""
     return _DecodeArgs(q, k_cache, v_cache, block_tables, context_lens, scale, out, partition_size, max_context_len,
-                       workspace, shared_blocks, k_scale, v_scale)
+                       workspace, shared_blocks, k_scale, v_scale, k_new, v_new)
 
 
 def run_decode(a: _DecodeArgs) -> None:
     lib = load_library()
-    if a.fp8:
+    if a.append:
+        _check(lib.pkv_paged_attention_decode_append(*a.args), "paged_attention_decode_append")
+    elif a.fp8:
         _check(lib.pkv_paged_attention_decode_fp8(*a.args), "paged_attention_decode_fp8")
     else:
         _check(lib.pkv_paged_attention_decode(*a.args), "paged_attention_decode")
@@ -242,7 +280,9 @@ def run_decode(a: _DecodeArgs) -> None:
 
 def run_partitions(a: _DecodeArgs) -> None:
     lib = load_library()
-    if a.fp8:
+    if a.append:
+        _check(lib.pkv_paged_attention_decode_append_partitions(*a.args), "paged_attention_decode_append_partitions")
+    elif a.fp8:
         _check(lib.pkv_paged_attention_decode_partitions_fp8(*a.args), "paged_attention_decode_partitions_fp8")
     else:
         _check(lib.pkv_paged_attention_decode_partitions(*a.args), "paged_attention_decode_partitions")

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "pagedkv.h")
 
 OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
-F32, BF16 = 0, 1
+F32, BF16, FP8 = 0, 1, 2
 FAKE = 0x10000  # never dereferenced: only used in calls that fail validation
 
 
@@ -51,7 +51,7 @@ def test_single_hip_runtime_in_process(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pkv_abi_version() == 5
+    assert lib.pkv_abi_version() == 6
     for code in range(5):
         assert lib.pkv_status_string(code)
     assert lib.pkv_status_string(99) == b"unknown status"
@@ -85,6 +85,39 @@ def dec(lib, **kw):
     return lib.pkv_paged_attention_decode(a["q"], a["kc"], a["vc"], a["bt"], a["lens"], a["scale"], a["out"], a["B"],
                                           a["hq"], a["hkv"], a["D"], a["bs"], a["nb"], a["maxblk"], a["maxctx"],
                                           a["ps"], a["ws"], a["wsb"], a["kvd"], a["outd"], a["flags"], None)
+
+
+def dec_append(lib, partitions=False, **kw):
+    a = dict(q=FAKE, kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, lens=FAKE, scale=0.1, out=FAKE, B=4, hq=32, hkv=8,
+             D=128, bs=16, nb=100, maxblk=128, maxctx=2000, ps=0, ws=FAKE, wsb=0, kvd=BF16, outd=BF16, flags=0)
+    a.update(kw)
+    fn = lib.pkv_paged_attention_decode_append_partitions if partitions else lib.pkv_paged_attention_decode_append
+    return fn(a["q"], a["kn"], a["vn"], a["kc"], a["vc"], a["bt"], a["lens"], a["scale"], a["out"], a["B"], a["hq"],
+              a["hkv"], a["D"], a["bs"], a["nb"], a["maxblk"], a["maxctx"], a["ps"], a["ws"], a["wsb"], a["kvd"],
+              a["outd"], a["flags"], None)
+
+
+@pytest.mark.parametrize("partitions", [False, True])
+def test_decode_append_validation(lib, partitions):
+    need = lib.pkv_decode_workspace_bytes(4, 32, 8, 128, 2000, 0, BF16)
+    ok = dict(wsb=need)
+    # only bf16 pools, at most 16 query heads per KV head
+    assert dec_append(lib, partitions, kvd=F32, **ok) == UNSUPPORTED
+    assert b"bf16" in lib.pkv_last_error()
+    assert dec_append(lib, partitions, kvd=FP8, **ok) == UNSUPPORTED
+    need17 = lib.pkv_decode_workspace_bytes(4, 8 * 17, 8, 128, 2000, 0, BF16)
+    assert dec_append(lib, partitions, hq=8 * 17, wsb=need17) == UNSUPPORTED
+    assert b"query heads per KV head" in lib.pkv_last_error()
+    assert dec_append(lib, partitions, kn=None, **ok) == INVALID
+    assert dec_append(lib, partitions, vn=None, **ok) == INVALID
+    assert dec_append(lib, partitions, kn=FAKE + 8, **ok) == INVALID  # misaligned
+    # the decode's own checks still apply
+    assert dec_append(lib, partitions, hq=30, **ok) == INVALID
+    assert dec_append(lib, partitions, D=96, **ok) == UNSUPPORTED
+    assert dec_append(lib, partitions, flags=2, **ok) == INVALID
+    assert dec_append(lib, partitions, ws=None) == WORKSPACE
+    # an empty batch launches nothing
+    assert dec_append(lib, partitions, B=0, kn=None, vn=None) == OK
 
 
 def test_decode_validation(lib):
