@@ -95,6 +95,8 @@ int32_t pkv_abi_version(void);
  *                  slots >= num_blocks * block_size are skipped as well
  *   k_cache, v_cache [device] pools in the layout above, num_blocks blocks
  *   head_dim       64 or 128;  block_size 16;  dtype PKV_F32 or PKV_BF16
+ *   k_new, v_new, k_cache and v_cache 16-byte aligned (else
+ *   PKV_ERR_INVALID_ARG)
  * Two tokens must not name the same slot (the write order between them is
  * unspecified).  num_tokens == 0 is a no-op.
  */

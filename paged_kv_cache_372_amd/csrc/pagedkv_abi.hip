@@ -325,8 +325,8 @@ pkv_status pkv_reshape_and_cache(const void* k_new, const void* v_new, const int
     if (num_blocks <= 0) return fail(PKV_ERR_INVALID_ARG, "num_blocks must be positive");
     if (num_tokens == 0) return PKV_OK;
     if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache) return fail(PKV_ERR_INVALID_ARG, "null pointer");
-    if ((uintptr_t)k_new % 16 || (uintptr_t)k_cache % 16)
-        return fail(PKV_ERR_INVALID_ARG, "k_new and k_cache must be 16-byte aligned");
+    if (((uintptr_t)k_new | (uintptr_t)v_new | (uintptr_t)k_cache | (uintptr_t)v_cache) % 16)
+        return fail(PKV_ERR_INVALID_ARG, "k_new, v_new, k_cache and v_cache must be 16-byte aligned");
     return from_hip(pkv::launch_cache_write(k_new, v_new, slot_mapping, k_cache, v_cache, num_tokens, num_kv_heads,
                                             head_dim, num_blocks, dtype == PKV_BF16, static_cast<hipStream_t>(stream)),
                     "reshape_and_cache launch");

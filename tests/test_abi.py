@@ -74,6 +74,9 @@ def test_reshape_and_cache_validation(lib):
     assert rac(lib, dtype=7) == UNSUPPORTED
     assert rac(lib, k_new=None) == INVALID
     assert rac(lib, kc=FAKE + 8) == INVALID  # misaligned
+    assert rac(lib, vc=FAKE + 8) == INVALID
+    assert rac(lib, v_new=FAKE + 4) == INVALID
+    assert b"aligned" in lib.pkv_last_error()
     assert rac(lib, T=0) == OK              # no-op, nothing launched
     assert lib.pkv_last_error() == b""
 

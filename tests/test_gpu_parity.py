@@ -82,6 +82,53 @@ def test_cache_write_bit_exact(dtype, D):
     assert np.array_equal(to_host_bits(dv).view(bits), vp)
 
 
+@pytest.mark.parametrize("dtype,D", [("f32", 64), ("bf16", 64), ("bf16", 128)])
+def test_cache_write_prompt_runs(dtype, D):
+    """Prompt-like writes: runs of consecutive slots (the 16-byte V store
+    path) mixed with every case that must fall back to element stores."""
+    rng = np.random.default_rng(300 + D)
+    NB, Hkv = 64, 2
+    blocks = [int(b) for b in rng.permutation(NB)]
+    segs = []
+    def run_from(block_i, offset, n):   # n consecutive positions of a sequence laid over blocks
+        out, b, o = [], block_i, offset
+        for _ in range(n):
+            out.append(blocks[b] * 16 + o)
+            o += 1
+            if o == 16:
+                b, o = b + 1, 0
+        return out
+    segs += run_from(0, 0, 40)           # block-aligned prompt of 40 tokens (ends mid-block)
+    segs += run_from(3, 3, 37)           # prompt starting at offset 3: runs straddle the aligned boundaries
+    segs += run_from(6, 0, 16)           # exactly one block
+    r = run_from(7, 0, 16)
+    r[5] = -1                            # a skipped slot inside a run
+    segs += r
+    r = run_from(8, 0, 16)
+    r[10] = NB * 16 + 2                  # a slot outside the pool inside a run
+    segs += r
+    segs += run_from(9, 0, 8)[::-1]      # consecutive slots in reverse order
+    segs += [blocks[10] * 16 + 4, blocks[11] * 16 + 9]   # single appended tokens
+    segs += run_from(12, 0, 13)          # the call ends inside a run
+    slots = np.asarray(segs, dtype=np.int64)
+    T = len(slots)
+    ks, vs = W.pool_shapes(NB, Hkv, D, 16, dtype)
+    bits = np.uint32 if dtype == "f32" else np.uint16
+    k_pool = rng.integers(0, np.iinfo(bits).max, size=ks, dtype=bits, endpoint=True)
+    v_pool = rng.integers(0, np.iinfo(bits).max, size=vs, dtype=bits, endpoint=True)
+    k_new = rng.integers(0, np.iinfo(bits).max, size=(T, Hkv, D), dtype=bits, endpoint=True)
+    v_new = rng.integers(0, np.iinfo(bits).max, size=(T, Hkv, D), dtype=bits, endpoint=True)
+    say(f"[cache_write prompt runs {dtype} D={D} T={T}]")
+    host = (lambda a: a.view(np.float32)) if dtype == "f32" else (lambda a: a)
+    dk, dv = to_dev(host(k_pool), dtype), to_dev(host(v_pool), dtype)
+    ops.reshape_and_cache(to_dev(host(k_new), dtype), to_dev(host(v_new), dtype), int_dev(slots, np.int64), dk, dv)
+    torch.cuda.synchronize()
+    ref_slots = np.where(slots >= NB * 16, -1, slots)
+    kp, vp = oracle.ref_reshape_and_cache(k_new, v_new, ref_slots, k_pool, v_pool)
+    assert np.array_equal(to_host_bits(dk).view(bits), kp)
+    assert np.array_equal(to_host_bits(dv).view(bits), vp)
+
+
 def test_cache_write_empty_is_noop():
     b = W.tiny_fp32()
     db = DeviceBatch(b)
