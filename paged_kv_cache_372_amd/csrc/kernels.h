@@ -113,9 +113,7 @@ struct PrefillParams {
 };
 
 // Rows (query token x head of a KV group) one prefill workgroup covers.
-constexpr int kPrefillRowsPerWave = 64;
-constexpr int kPrefillWaves = 4;
-constexpr int kPrefillRowsPerGroup = kPrefillRowsPerWave * kPrefillWaves;
+constexpr int kPrefillRowsPerGroup = 256;
 
 size_t prefill_lds_bytes(int32_t num_seqs);
 hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream);
