@@ -536,7 +536,12 @@ def main():
     args = ap.parse_args()
 
     if args.summarize_profile:
-        ps = args.partition_size if args.partition_size > 0 else "balanced"
+        # the partition the bench resolves for this workload (its own default
+        # when --partition-size is not given: 512 for the long contexts)
+        ps = args.partition_size
+        if ps < 0:
+            ps = 512 if args.config in ("long_context", "long_context_fp8") else 0
+        ps = ps if ps > 0 else "balanced"
         if family(args.config) != "decode":
             ps = "none"
         tag = "_fused" if args.fused else ""
