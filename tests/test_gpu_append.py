@@ -165,3 +165,28 @@ def test_rejected_shapes():
     with pytest.raises(ValueError):
         ops.paged_attention_decode_append(dt.q, dt.k_new, dt.v_new, dt.k_cache, dt.v_cache, dt.bt, dt.lens, t.scale,
                                           dt.out, max_context_len=t.max_context_len)
+
+
+def test_fp32_output_and_two_phase_calls():
+    b = W.llama3_8b_decode(num_seqs=9, seed=77)
+    say("[append] fp32 output; two-phase calls equal one call")
+    # fp32 output from bf16 pools
+    a = DeviceBatch(b, out_dtype=torch.float32)
+    fused(a, b, 0)
+    torch.cuda.synchronize()
+    kp, vp = oracle.ref_reshape_and_cache(b.k_new, b.v_new, b.slot_mapping, b.k_pool, b.v_pool)
+    assert np.array_equal(to_host_bits(a.k_cache), kp) and np.array_equal(to_host_bits(a.v_cache), vp)
+    ref = oracle.ref_paged_attention_decode(b.q, kp, vp, b.block_tables, b.context_lens, b.scale, b.dtype)
+    compare(out_f64(a.out), ref, b.dtype, "fused, fp32 out")
+    # the decode launch and the reduce called one at a time
+    one = DeviceBatch(b)
+    fused(one, b, 48)
+    two = DeviceBatch(b)
+    plan = ops.prepare_decode(two.q, two.k_cache, two.v_cache, two.bt, two.lens, b.scale, two.out, partition_size=48,
+                              max_context_len=b.max_context_len, k_new=two.k_new, v_new=two.v_new)
+    ops.run_partitions(plan)
+    ops.run_reduce(plan)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host_bits(one.out), to_host_bits(two.out))
+    assert np.array_equal(to_host_bits(one.k_cache), to_host_bits(two.k_cache))
+    assert np.array_equal(to_host_bits(one.v_cache), to_host_bits(two.v_cache))
