@@ -62,10 +62,36 @@ def kernel_sources(workload: str):
     return [os.path.join(ROOT, "paged_kv_cache_372_amd", "csrc", f) for f in (main, "kernels.h")]
 
 
+def _code_only(text: str) -> str:
+    """C++ source with comments removed and whitespace collapsed, so that an
+    edit to comments alone keeps the counters taken on the same code."""
+    import re
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":  # string or character literal, kept whole
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return re.sub(r"\s+", " ", "".join(out)).strip()
+
+
 def kernel_source_hash(workload: str = "llama3_8b_decode") -> str:
     h = hashlib.sha256()
     for p in kernel_sources(workload):
-        h.update(open(p, "rb").read())
+        h.update(_code_only(open(p).read()).encode())
     return h.hexdigest()
 
 

@@ -27,6 +27,10 @@
 // ahead of use, across sequence and range boundaries, so a wave stalls on
 // memory only once, at its start.
 //
+// With the fused append (a decode step's cache write in this launch, bf16
+// pools), the wave that walks a sequence's last block also stores the
+// token the sequence gains this step; see the comment at its prologue.
+//
 // Per 16-token block, per wave:
 //   S[16 tok x 16 heads] = K[16 x D] . Q^T[D x 16]  D/32 x mfma_f32_16x16x32_bf16
 //   online softmax on S (exp2 domain, scale*log2e folded in)

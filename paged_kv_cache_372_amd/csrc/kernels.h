@@ -57,8 +57,9 @@ struct DecodeParams {
     int32_t head_unit_groups;    // ceil(head_units / waves_per_group)
     int64_t part_bytes;          // bytes of the o_part region (buffer-resource extent)
     // fused append (balanced bf16 path, one head group per KV head): the
-    // token each sequence gains this step, [B][Hkv][D], stored at position
-    // L - 1 before the walk; null = no append
+    // token each sequence gains this step, [B][Hkv][D], which the wave that
+    // walks the sequence's last block writes into position L - 1 of it;
+    // null = no append
     const void* k_new;
     const void* v_new;
 };

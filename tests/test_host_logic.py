@@ -269,3 +269,16 @@ def test_pool_exhaustion_raises():
     with pytest.raises(PoolExhausted):
         for i in range(2):
             sim.step(i)
+
+
+def test_kernel_source_hash_ignores_comments_only():
+    """The traffic records bench.py reads are keyed by the kernel's code: a
+    comment edit keeps the key, a code edit changes it."""
+    import bench
+    base = 'int f(int x) { return x + 1; }  // add one\n/* block */ const char* s = "a // b";\n'
+    same = 'int f(int x) {\n  return x + 1;  // plus one\n}\nconst char* s = "a // b"; /* other */\n'
+    diff = 'int f(int x) { return x + 2; }\nconst char* s = "a // b";\n'
+    lit = 'int f(int x) { return x + 1; }\nconst char* s = "a // c";\n'
+    assert bench._code_only(base) == bench._code_only(same)
+    assert bench._code_only(base) != bench._code_only(diff)
+    assert bench._code_only(base) != bench._code_only(lit)
