@@ -485,6 +485,117 @@ __global__ __launch_bounds__(64 * PrefillShape<kFp8>::kWaves) void prefill_bf16_
             load_pair(d, next_pa[d], next_pb[d], next_info[d]);
             __builtin_amdgcn_sched_barrier(0);
         }
+        // bf16, mask-free pairs: the pieces of compute_pair, so that one
+        // pair's QK products can run under the previous pair's softmax
+        auto qk_free = [&](const PairRegs<D>& r, float (*sv)[8], float* mx) __attribute__((always_inline)) {
+#pragma unroll
+            for (int j = 0; j < kNQ; ++j) {
+                float4_t sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < D / 32; ++kk) {
+                    sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.k[0][kk]), qv[j][kk],
+                                                                 sa, 0, 0, 0);
+                    sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.k[1][kk]), qv[j][kk],
+                                                                 sb, 0, 0, 0);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    sv[j][i] = sa[i];
+                    sv[j][4 + i] = sb[i];
+                }
+            }
+        };
+        auto max_free = [&](float (*sv)[8], float* mx) __attribute__((always_inline)) {
+#pragma unroll
+            for (int j = 0; j < kNQ; ++j) {
+                const float m8 = fmaxf(fmaxf(fmaxf(sv[j][0], sv[j][1]), fmaxf(sv[j][2], sv[j][3])),
+                                       fmaxf(fmaxf(sv[j][4], sv[j][5]), fmaxf(sv[j][6], sv[j][7])));
+                mx[j] = max_over_groups(m8) * c_scale;  // all scores live and c >= 0: scale the max only
+            }
+        };
+        auto rescale = [&](const float* mx) __attribute__((always_inline)) {
+            bool raise[kNQ];
+            bool any = false;
+#pragma unroll
+            for (int j = 0; j < kNQ; ++j) {
+                raise[j] = mx[j] > st[j].m + kSlack;
+                any = any || raise[j];
+            }
+            if (__any(any)) {
+#pragma unroll
+                for (int j = 0; j < kNQ; ++j) {
+                    const float alpha = raise[j] ? exp2_fast(st[j].m - mx[j]) : 1.f;
+                    st[j].l *= alpha;
+#pragma unroll
+                    for (int c = 0; c < D / 16; ++c) acc[j][c] *= alpha;
+                    st[j].m = raise[j] ? mx[j] : st[j].m;
+                }
+            }
+        };
+        auto pv_free = [&](const PairRegs<D>& r, float (*sv)[8]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int j = 0; j < kNQ; ++j) {
+                const float m_use = st[j].m == -INFINITY ? 0.f : st[j].m;
+                float pr[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) pr[i] = exp2_fast(fmaf(sv[j][i], c_scale, -m_use));
+                st[j].l += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+                const bf16x8_t pj = __builtin_bit_cast(
+                    bf16x8_t, make_uint4(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
+                                         pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])));
+#pragma unroll
+                for (int c = 0; c < D / 16; ++c)
+                    acc[j][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.v[c]), pj,
+                                                                        acc[j][c], 0, 0, 0);
+            }
+        };
+        // A mask-free round of two pairs, pipelined: QK(0), its rescale
+        // check, then one scheduling region with the weights and PV products
+        // of pair 0 and the QK products and maxima of pair 1, then pair 1's
+        // check and PV products.
+        auto round_pipe = [&](int i) __attribute__((always_inline)) {
+#pragma unroll
+            for (int d = 0; d < kPairDepth; ++d) accept(pend[d], next_pa[d], next_pb[d], next_info[d]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int d = 0; d < kPairDepth; ++d) fetch(i + 2 * kPairDepth + d, pend[d]);
+            if constexpr (!kFp8) {
+                float sv0[kNQ][8], mx0[kNQ], sv1[kNQ][8], mx1[kNQ];
+                qk_free(ring[0], sv0, mx0);
+                max_free(sv0, mx0);
+                rescale(mx0);
+                __builtin_amdgcn_sched_barrier(0);
+                qk_free(ring[1], sv1, mx1);
+                pv_free(ring[0], sv0);
+                max_free(sv1, mx1);
+                // interleave: one MFMA, then three VALU, over the region.
+                // Measured on the chunked-prefill workload (TFLOP/s, same
+                // session): 3 VALU per MFMA 690, 2 685, 4 675, 4 then 2
+                // 673, 5 then 1 668; without the pipelined round 681.
+#pragma unroll
+                for (int t = 0; t < 2 * kNQ * (D / 16); ++t) {
+                    __builtin_amdgcn_sched_group_barrier(0x8, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x2, 3, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                load_pair(0, next_pa[0], next_pb[0], next_info[0]);
+                __builtin_amdgcn_sched_barrier(0);
+                rescale(mx1);
+                __builtin_amdgcn_sched_barrier(0);
+                pv_free(ring[1], sv1);
+                __builtin_amdgcn_sched_group_barrier(0x2, kExpValu, 0);
+#pragma unroll
+                for (int t = 0; t < (kNQ - 1) * (D / 16); ++t) {
+                    __builtin_amdgcn_sched_group_barrier(0x8, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x2, kExpValu / (D / 16), 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x8, D / 16, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                load_pair(1, next_pa[1], next_pb[1], next_info[1]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+
         auto round = [&](int i, auto final_tag, auto masked_tag) __attribute__((always_inline)) {
             constexpr bool kFinal = decltype(final_tag)::value;
 #pragma unroll
@@ -508,8 +619,10 @@ __global__ __launch_bounds__(64 * PrefillShape<kFp8>::kWaves) void prefill_bf16_
         // included, take the masked form.
         const int NPf = min(NP, (qmin + 1) / (2 * kBlockSize));
         int i = 0;
-        for (; i + 2 * kPairDepth <= NP && i + kPairDepth <= NPf; i += kPairDepth)
-            round(i, std::false_type{}, std::false_type{});
+        for (; i + 2 * kPairDepth <= NP && i + kPairDepth <= NPf; i += kPairDepth) {
+            if constexpr (!kFp8 && kPairDepth == 2) round_pipe(i);
+            else round(i, std::false_type{}, std::false_type{});
+        }
         for (; i + 2 * kPairDepth <= NP; i += kPairDepth) round(i, std::false_type{}, std::true_type{});
         for (; i < NP; i += kPairDepth) round(i, std::true_type{}, std::true_type{});
     }
