@@ -146,21 +146,18 @@ def gather_contiguous(k_pool: np.ndarray, v_pool: np.ndarray, table_row: np.ndar
     bs = k_pool.shape[3]
     if heads is None:
         heads = range(k_pool.shape[1])
-    heads = list(heads)
+    heads = np.asarray(list(heads), dtype=np.int64)
     D = k_pool.shape[2] * k_pool.shape[4]
-    kc = np.empty((context_len, len(heads), D), dtype=k_pool.dtype)
-    vc = np.empty((context_len, len(heads), D), dtype=v_pool.dtype)
     nblk = -(-context_len // bs)
-    for j in range(nblk):
-        phys = int(table_row[j])
-        lo, hi = j * bs, min(context_len, (j + 1) * bs)
-        for hi_idx, h in enumerate(heads):
-            # tile of this (physical block, head); take tokens 0 .. hi-lo-1
-            k_tile = k_pool[phys, h]                   # [D/x, bs, x]
-            v_tile = v_pool[phys, h]                   # [D, bs]
-            n = hi - lo
-            kc[lo:hi, hi_idx, :] = np.transpose(k_tile[:, :n, :], (1, 0, 2)).reshape(n, D)
-            vc[lo:hi, hi_idx, :] = v_tile[:, :n].T
+    # physical block of each logical block j < nblk, and its tiles for the
+    # listed heads: K [nblk, heads, D/x, bs, x], V [nblk, heads, D, bs]
+    phys = np.asarray(table_row[:nblk], dtype=np.int64)
+    k_tiles = k_pool[phys[:, None], heads[None, :]]
+    v_tiles = v_pool[phys[:, None], heads[None, :]]
+    # token t of logical block j is logical position j * bs + t; its K row
+    # is the chunks at offset t, its V row the column t of the tile
+    kc = np.transpose(k_tiles, (0, 3, 1, 2, 4)).reshape(nblk * bs, len(heads), D)[:context_len]
+    vc = np.transpose(v_tiles, (0, 3, 1, 2)).reshape(nblk * bs, len(heads), D)[:context_len]
     return kc, vc
 
 
@@ -195,10 +192,13 @@ def ref_decode_sequence(q_s: np.ndarray, kc: np.ndarray, vc: np.ndarray, scale: 
         q_heads = range(Hq)
     present = list(range(num_kv_heads)) if kv_heads_present is None else list(kv_heads_present)
     out = np.empty((len(list(q_heads)), q_s.shape[1]), dtype=np.float64)
+    rows = {}  # KV head -> its K and V rows as contiguous [L, D] arrays
     for i, h in enumerate(q_heads):
         kvh = kv_head_of(h, Hq, num_kv_heads)
-        j = present.index(kvh)
-        out[i] = softmax_attention(q_s[h], kc[:, j, :], vc[:, j, :], scale)
+        if kvh not in rows:
+            j = present.index(kvh)
+            rows[kvh] = (np.ascontiguousarray(kc[:, j, :]), np.ascontiguousarray(vc[:, j, :]))
+        out[i] = softmax_attention(q_s[h], rows[kvh][0], rows[kvh][1], scale)
     return out
 
 
