@@ -90,6 +90,24 @@ def compare(got: np.ndarray, ref: np.ndarray, dtype: str, what: str):
     return err, rel
 
 
+def oracle_decode_all(q, k_pool, v_pool, block_tables, context_lens, scale, dtype, **scales):
+    """The oracle's decode of every sequence and query head, ``[B, Hq, D]``.
+
+    Called one (sequence, KV head) at a time, so a long context widens one
+    KV head's rows to float64 at once instead of all of them."""
+    B, Hq, D = q.shape
+    Hkv = k_pool.shape[1]
+    G = Hq // Hkv
+    out = np.empty((B, Hq, D), dtype=np.float64)
+    for s in range(B):
+        for g in range(Hkv):
+            heads = list(range(g * G, (g + 1) * G))
+            out[s, g * G:(g + 1) * G] = oracle.ref_paged_attention_decode(q, k_pool, v_pool, block_tables,
+                                                                          context_lens, scale, dtype, seqs=[s],
+                                                                          q_heads=heads, **scales)[0]
+    return out
+
+
 def sampled_seqs(context_lens: np.ndarray, n: int, seed: int):
     """n sequences: the shortest, the longest and a seeded random rest."""
     B = len(context_lens)

@@ -83,10 +83,7 @@ def test_prefill_small(mix, heads, D):
 @pytest.mark.parametrize("seed", [W.PREFILL_SEED, 31])
 def test_chunked_prefill_full_size(seed):
     b = W.chunked_prefill(seed)
-    # the oracle is slow at this size: the request with the longest context
-    # and one more, all their rows
-    longest = int(np.argmax(b.context_lens))
-    check(b, seqs=sorted({longest, (longest + 5) % b.num_seqs}), what="full size, sampled requests")
+    check(b, what="full size, every request")
 
 
 def test_mixed_prefill_and_decode_rows():
@@ -164,4 +161,4 @@ def test_more_than_4096_requests():
     new = [1] * n
     new[5], new[4097], new[4099] = 20, 17, 3
     b = W.build_prefill("prefill_many", 19, 8, 2, 64, cached, new)
-    check(b, seqs=[0, 5, 4095, 4096, 4097, 4099], what="4100 requests")
+    check(b, what="4100 requests, every one")
