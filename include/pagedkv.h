@@ -386,6 +386,49 @@ pkv_status pkv_paged_attention_prefill_fp8(const void* q, const void* k_cache, c
                                            int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
                                            pkv_dtype out_dtype, void* stream);
 
+/*
+ * Measurement aid: the plain-read ceiling.  Decode is bound by memory
+ * bandwidth (runbyai section 1) and reads its KV as fixed-size blocks
+ * scattered through one pool (architvora "Paged Attention"); this call reads
+ * bytes with 16-byte loads and nothing else, so its rate is the ceiling of
+ * that access pattern on the device, reported beside the decode's.
+ *   src        [device] buffer of `bytes` bytes (a positive multiple of 16),
+ *              16-byte aligned
+ *   tiles      NULL: read src front to back once.  Otherwise [device] int32
+ *              [num_tiles]: read tile_bytes bytes at byte offset
+ *              tiles[i] * tile_bytes for each i (entries outside the buffer
+ *              are skipped)
+ *   tile_bytes a power of two in [16, 2^24] (ignored when tiles is NULL)
+ *   streaming  nonzero: non-temporal loads (as the decode's default);
+ *              zero: ordinary loads
+ *   sink       [device] uint32 [1024]; the kernel may write to it (it keeps
+ *              the loads from being dropped); its contents mean nothing
+ * One launch; asynchronous on `stream`.
+ */
+pkv_status pkv_hbm_read_bench(const void* src, int64_t bytes, const int32_t* tiles, int64_t num_tiles,
+                              int32_t tile_bytes, int32_t streaming, uint32_t* sink, void* stream);
+
+/*
+ * Measurement aid: decode over a bf16 cache with every product on the vector
+ * ALU instead of the matrix cores, to weigh the two for this bandwidth-bound
+ * step (runbyai section 1).  Same result as pkv_paged_attention_decode within
+ * the bf16 bar, not bit for bit: every product is an fp32 FMA of the widened
+ * bf16 values.  It runs the fp32 path's kernel on bf16 elements (one wave
+ * per partition x sequence x up to 8 query heads x KV head, query rows and
+ * weights through LDS) and its split-K reduce; the work split differs from
+ * the balanced matrix-core decode, so a comparison weighs the two designs.
+ *   Arguments as pkv_paged_attention_decode with bf16 q and pools; the
+ *   workspace is pkv_decode_workspace_bytes(..., PKV_F32) bytes (the fp32
+ *   path's partials; 0 when every context fits in one partition).
+ */
+pkv_status pkv_paged_attention_decode_vector_alu(const void* q, const void* k_cache, const void* v_cache,
+                                                 const int32_t* block_tables, const int32_t* context_lens,
+                                                 float scale, void* out, int32_t num_seqs, int32_t num_q_heads,
+                                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                                 int64_t num_blocks, int32_t max_blocks_per_seq,
+                                                 int32_t max_context_len, int32_t partition_size, void* workspace,
+                                                 size_t workspace_bytes, pkv_dtype out_dtype, void* stream);
+
 /* Static description of a status code.  Never NULL. */
 const char* pkv_status_string(pkv_status status);
 

@@ -1,5 +1,6 @@
-// Paged decode attention on the vector ALUs: the fp32-KV path (and a bf16
-// variant used as a second, independent GPU path).
+// Paged decode attention on the vector ALUs: the fp32-KV path, and, on bf16
+// elements, the measurement aid pkv_paged_attention_decode_vector_alu that
+// weighs vector-ALU products against the matrix-core decode.
 //
 // Same problem, unit decomposition and split-K partials as decode_mfma.hip
 // (one wave64 per partition x sequence x head group x KV head), but every

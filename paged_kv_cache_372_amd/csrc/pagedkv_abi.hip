@@ -151,6 +151,21 @@ struct Call {
     char* workspace;
 };
 
+// Point a checked call at its workspace (the balanced path carves it per
+// launch in chunk_params; the partitioned path keeps its partials here).
+void bind_workspace(Call* c, void* workspace) {
+    const Plan& pl = c->plan;
+    pkv::DecodeParams& p = c->base;
+    c->workspace = static_cast<char*>(workspace);
+    if (!pl.balanced) {
+        float* ws = static_cast<float*>(workspace);
+        const size_t rows = (size_t)p.num_seqs * p.num_q_heads * pl.num_parts;
+        p.o_part = pl.workspace ? ws : nullptr;
+        p.m_part = pl.workspace ? ws + rows * p.head_dim : nullptr;
+        p.l_part = pl.workspace ? ws + rows * (p.head_dim + 1) : nullptr;
+    }
+}
+
 pkv_status prepare(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
                    const int32_t* context_lens, float scale, void* out, int32_t num_seqs, int32_t num_q_heads,
                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
@@ -198,27 +213,33 @@ pkv_status prepare(const void* q, const void* k_cache, const void* v_cache, cons
     p.kv_fp8 = kv_dtype == PKV_FP8_E4M3;
     p.k_scale = k_scale;
     p.v_scale = v_scale;
-    float* ws = static_cast<float*>(workspace);
     if (pl.balanced) {
         p.walkers = pl.walkers;
         p.range_cap = pl.range_cap;
         p.waves_per_group = pl.waves_per_group;
         p.head_units = pl.head_units;
         p.head_unit_groups = pl.head_unit_groups;
+        if (p.cached_kv) {
+            // Blocks shared by several sequences: one wave per workgroup, so
+            // that workgroup i serves head unit i mod head_units.  Workgroups
+            // go to the 8 XCDs in turn (i mod 8), so with 8 KV heads each
+            // XCD reads one head's tiles and its L2 keeps that head's shared
+            // blocks (a 2048-token prefix: 1 MiB of K and V per head) for
+            // every sequence that reads them.  The ranges, and so the
+            // partials and the reduce, stay those of the plan.
+            p.waves_per_group = 1;
+            p.head_unit_groups = pl.head_units;
+        }
         p.part_bytes = (int64_t)(2 * pl.max_ranges) * num_q_heads * head_dim * (int64_t)sizeof(float);
     } else {
         p.part_blocks = pl.part_tokens / block_size;
         p.num_parts = pl.num_parts;
-        const size_t rows = (size_t)num_seqs * num_q_heads * pl.num_parts;
-        p.o_part = pl.workspace ? ws : nullptr;
-        p.m_part = pl.workspace ? ws + rows * head_dim : nullptr;
-        p.l_part = pl.workspace ? ws + rows * (head_dim + 1) : nullptr;
     }
     c->kv_dtype = kv_dtype;
     c->q_row_bytes = (size_t)num_q_heads * head_dim * (kv_dtype == PKV_F32 ? 4 : 2);  // q is bf16 for fp8 caches
     c->out_row_bytes = (size_t)num_q_heads * head_dim * (out_dtype == PKV_BF16 ? 2 : 4);
     c->new_row_bytes = 0;
-    c->workspace = static_cast<char*>(workspace);
+    bind_workspace(c, workspace);
     return PKV_OK;
 }
 
@@ -663,4 +684,44 @@ pkv_status pkv_paged_attention_prefill_fp8(const void* q, const void* k_cache, c
                         max_context_len, true, k_scale, v_scale, out_dtype, stream);
 }
 
+pkv_status pkv_hbm_read_bench(const void* src, int64_t bytes, const int32_t* tiles, int64_t num_tiles,
+                              int32_t tile_bytes, int32_t streaming, uint32_t* sink, void* stream) {
+    g_last_error[0] = 0;
+    if (bytes <= 0 || bytes % 16) return fail(PKV_ERR_INVALID_ARG, "bytes must be a positive multiple of 16");
+    if (num_tiles < 0) return fail(PKV_ERR_INVALID_ARG, "num_tiles must be >= 0");
+    if (!src || !sink) return fail(PKV_ERR_INVALID_ARG, "null pointer");
+    if ((uintptr_t)src % 16) return fail(PKV_ERR_INVALID_ARG, "src must be 16-byte aligned");
+    if (tiles) {
+        if (tile_bytes < 16 || tile_bytes > (1 << 24) || (tile_bytes & (tile_bytes - 1)))
+            return fail(PKV_ERR_INVALID_ARG, "tile_bytes must be a power of two in [16, 2^24]");
+        if (num_tiles > ((int64_t)1 << 40) / tile_bytes) return fail(PKV_ERR_INVALID_ARG, "too many tiles");
+    }
+    return from_hip(pkv::launch_hbm_read(src, bytes, tiles, num_tiles, tile_bytes, streaming != 0, sink,
+                                         static_cast<hipStream_t>(stream)),
+                    "hbm_read launch");
+}
+
+pkv_status pkv_paged_attention_decode_vector_alu(const void* q, const void* k_cache, const void* v_cache,
+                                                 const int32_t* block_tables, const int32_t* context_lens,
+                                                 float scale, void* out, int32_t num_seqs, int32_t num_q_heads,
+                                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                                 int64_t num_blocks, int32_t max_blocks_per_seq,
+                                                 int32_t max_context_len, int32_t partition_size, void* workspace,
+                                                 size_t workspace_bytes, pkv_dtype out_dtype, void* stream) {
+    g_last_error[0] = 0;
+    // the fp32 path's plan (fixed partitions, its workspace rule); the
+    // kernel reads bf16 elements
+    Call c;
+    pkv_status st = prepare(q, k_cache, v_cache, block_tables, context_lens, scale, out, num_seqs, num_q_heads,
+                            num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len,
+                            partition_size, workspace, workspace_bytes, PKV_F32, out_dtype, 0, nullptr, nullptr, &c);
+    if (st != PKV_OK) return st;
+    if (num_seqs == 0) return PKV_OK;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    st = from_hip(pkv::launch_decode_valu(c.base, true, s), "vector-ALU decode launch");
+    if (st != PKV_OK) return st;
+    return from_hip(pkv::launch_splitk_reduce(c.base, false, s), "split-K reduce launch");
+}
+
 }  // extern "C"
+

@@ -59,6 +59,9 @@ _SIGNATURES = {
                                            _i64, _i32, _i32, _i32, _i32, _vp]),
     "pkv_paged_attention_prefill_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _i32, _i32, _i32,
                                                _i32, _i32, _i32, _i64, _i32, _i32, _i32, _vp]),
+    "pkv_paged_attention_decode_vector_alu": (_i32, [_vp, _vp, _vp, _vp, _vp, _f32, _vp, _i32, _i32, _i32, _i32,
+                                                     _i32, _i64, _i32, _i32, _i32, _vp, _sz, _i32, _vp]),
+    "pkv_hbm_read_bench": (_i32, [_vp, _i64, _vp, _i64, _i32, _i32, _vp, _vp]),
     "pkv_status_string": (ctypes.c_char_p, [_i32]),
     "pkv_last_error": (ctypes.c_char_p, []),
 }
@@ -160,12 +163,21 @@ def decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, h
 
 
 class _DecodeArgs:
-    """Validated decode arguments, reused by the one-call and two-phase entry points."""
+    """Validated decode arguments, reused by the one-call and two-phase entry points.
+
+    A plan holds references to every tensor it points at, so none of them is
+    freed (and its memory handed to another tensor) while the plan lives.
+    Fixed when the plan is built: the stream (the device's current stream at
+    that moment) and ``max_context_len``, which bounds the context lengths
+    the kernels read (longer ones are clamped to it).  Build a new plan when
+    either changes, e.g. when contexts grow past the bound.
+    """
 
     def __init__(self, q, k_cache, v_cache, block_tables, context_lens, scale, out, partition_size,
                  max_context_len, workspace, shared_blocks=False, k_scale=None, v_scale=None, k_new=None,
                  v_new=None):
         dev = q.device
+        self._keep = (q, k_cache, v_cache, block_tables, context_lens, out, k_scale, v_scale, k_new, v_new)
         self.fp8 = k_cache.dtype in FP8_POOL_DTYPES
         self.append = k_new is not None or v_new is not None
         for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (block_tables, "block_tables"),
@@ -261,9 +273,12 @@ def paged_attention_decode_append(q: torch.Tensor, k_new: torch.Tensor, v_new: t
 def prepare_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out, *, partition_size=0,
                    max_context_len=None, workspace=None, shared_blocks=False, k_scale=None,
                    v_scale=None, k_new=None, v_new=None) -> _DecodeArgs:
-    """Validate once; the returned object drives ``run_partitions`` / ``run_reduce`` repeatedly.
-    fp8 pools (uint8 / float8_e4m3fn) take ``k_scale`` / ``v_scale``; ``k_new`` / ``v_new`` select the
-    fused append (``paged_attention_decode_append``)."""
+    """Validate once; the returned plan drives ``run_decode`` / ``run_partitions`` / ``run_reduce``
+    repeatedly on the same tensors (their contents may change between runs).  The plan keeps those
+    tensors alive, and fixes the stream (the current one now) and ``max_context_len`` (contexts longer
+    than it are clamped): build a new plan when either must change.  fp8 pools (uint8 /
+    float8_e4m3fn) take ``k_scale`` / ``v_scale``; ``k_new`` / ``v_new`` select the fused append
+    (``paged_attention_decode_append``)."""
     return _DecodeArgs(q, k_cache, v_cache, block_tables, context_lens, scale, out, partition_size, max_context_len,
                        workspace, shared_blocks, k_scale, v_scale, k_new, v_new)
 
@@ -446,3 +461,58 @@ def swap_blocks(src_k: torch.Tensor, src_v: torch.Tensor, dst_k: torch.Tensor, d
 def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, pairs: torch.Tensor) -> None:
     """Copy-on-write inside one pool: block ``src`` to block ``dst`` for every pair of ``pairs`` (int64 ``[n, 2]``)."""
     swap_blocks(k_cache, v_cache, k_cache, v_cache, pairs)
+
+
+def hbm_read_bench(src: torch.Tensor, sink: torch.Tensor, tiles: Optional[torch.Tensor] = None,
+                   tile_bytes: int = 4096, streaming: bool = True) -> None:
+    """Measurement aid: read ``src`` (contiguous, device) front to back, or the tiles ``tiles`` (int32,
+    device) of ``tile_bytes`` each, with nothing else done; ``sink`` is a device uint32 ``[1024]``."""
+    lib = load_library()
+    dev = src.device
+    _check_tensor(src, "src", dev)
+    _check_tensor(sink, "sink", dev)
+    _require(sink.dtype in (torch.int32, torch.uint32) and sink.numel() >= 1024, "sink must be 32-bit [1024]")
+    if tiles is not None:
+        _check_tensor(tiles, "tiles", dev)
+        _require(tiles.dtype == torch.int32 and tiles.dim() == 1, "tiles must be int32 [n]")
+    nbytes = src.numel() * src.element_size()
+    st = lib.pkv_hbm_read_bench(_ptr(src), nbytes, _ptr(tiles) if tiles is not None else None,
+                                tiles.numel() if tiles is not None else 0, int(tile_bytes), 1 if streaming else 0,
+                                _ptr(sink), _stream(dev))
+    _check(st, "hbm_read_bench")
+
+
+def paged_attention_decode_vector_alu(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                      block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                                      out: torch.Tensor, *, partition_size: int = 0,
+                                      max_context_len: Optional[int] = None,
+                                      workspace: Optional[torch.Tensor] = None) -> None:
+    """Measurement aid: bf16 decode with every product an fp32 FMA on the vector ALU (the fp32 path's
+    kernel); agrees with ``paged_attention_decode`` within the bf16 bar."""
+    lib = load_library()
+    dev = q.device
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (block_tables, "block_tables"),
+                 (context_lens, "context_lens"), (out, "out")):
+        _check_tensor(t, n, dev)
+    nb, hkv, D = _pool_dims(k_cache, v_cache)
+    _require(k_cache.dtype == torch.bfloat16 and q.dtype == torch.bfloat16, "bf16 q and pools")
+    _require(q.dim() == 3 and q.shape[2] == D, f"q must be [B, Hq, {D}]")
+    B, hq = q.shape[0], q.shape[1]
+    _require(tuple(out.shape) == tuple(q.shape), "out must have q's shape")
+    _require(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and block_tables.shape[0] == B,
+             "block_tables must be int32 [B, max_blocks_per_seq]")
+    _require(context_lens.dtype == torch.int32 and tuple(context_lens.shape) == (B,), "context_lens must be int32 [B]")
+    if max_context_len is None:
+        max_context_len = int(context_lens.max().item()) if B else 0
+    need = decode_workspace_bytes(B, hq, hkv, D, int(max_context_len), int(partition_size), torch.float32)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_ptr = _ptr(workspace) if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.pkv_paged_attention_decode_vector_alu(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                                   _ptr(context_lens), float(scale), _ptr(out), B, hq, hkv, D,
+                                                   BLOCK_SIZE, nb, block_tables.shape[1], int(max_context_len),
+                                                   int(partition_size), ws_ptr, ws_bytes, _dtype_code(out),
+                                                   _stream(dev))
+    _check(st, "paged_attention_decode_vector_alu")
+

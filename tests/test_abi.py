@@ -152,6 +152,16 @@ def test_decode_validation(lib):
     assert red == WORKSPACE
 
 
+def test_hbm_read_bench_validation(lib):
+    sink = FAKE
+    assert lib.pkv_hbm_read_bench(FAKE, 0, None, 0, 4096, 1, sink, None) == INVALID
+    assert lib.pkv_hbm_read_bench(FAKE, 40, None, 0, 4096, 1, sink, None) == INVALID      # not a multiple of 16
+    assert lib.pkv_hbm_read_bench(FAKE + 8, 4096, None, 0, 4096, 1, sink, None) == INVALID
+    assert lib.pkv_hbm_read_bench(FAKE, 1 << 20, FAKE, 16, 3000, 1, sink, None) == INVALID  # not a power of two
+    assert lib.pkv_hbm_read_bench(FAKE, 1 << 20, FAKE, 16, 8, 1, sink, None) == INVALID
+    assert lib.pkv_hbm_read_bench(None, 1 << 20, None, 0, 4096, 1, sink, None) == INVALID
+
+
 def pre(lib, **kw):
     a = dict(q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, lens=FAKE, qsl=FAKE, scale=0.1, out=FAKE, B=4, T=64, hq=32, hkv=8,
              D=128, bs=16, nb=100, maxblk=128, maxctx=2000, kvd=BF16, outd=BF16)

@@ -347,6 +347,24 @@ def test_two_phase_calls_equal_one_call():
     assert torch.equal(one.view(torch.int16), db.out.view(torch.int16))
 
 
+@pytest.mark.parametrize("make,ps", [(lambda: W.llama3_8b_decode(num_seqs=8), 0),
+                                     (lambda: W.long_context(num_seqs=2, context_len=8192), 512),
+                                     (lambda: W.build_static("valu_edge", 29, "bf16", 12, 3, 64, [1, 16, 17, 900], 80), 64)],
+                         ids=["gqa4", "gqa8_partition512", "gqa4_d64_edges"])
+def test_vector_alu_decode_bf16(make, ps):
+    """The measurement aid that runs bf16 decode on the vector ALU meets the bf16 bar too."""
+    b = make()
+    say(f"[{b.name} B={b.num_seqs} vector ALU, ps={ps}]")
+    db = DeviceBatch(b)
+    db.write()
+    ops.paged_attention_decode_vector_alu(db.q, db.k_cache, db.v_cache, db.bt, db.lens, b.scale, db.out,
+                                          partition_size=ps, max_context_len=b.max_context_len)
+    torch.cuda.synchronize()
+    kp, vp = oracle_pools(b)
+    ref = oracle_decode_all(b.q, kp, vp, b.block_tables, b.context_lens, b.scale, b.dtype)
+    compare(out_f64(db.out), ref, b.dtype, f"{b.name} vector-ALU decode")
+
+
 def test_fp32_output_from_bf16_kv():
     b = W.llama3_8b_decode(num_seqs=4)
     db = DeviceBatch(b, out_dtype=torch.float32)
