@@ -58,8 +58,11 @@ def traffic_file(workload: str, fused: bool = False) -> str:
 
 
 def kernel_sources(workload: str):
+    """Sources whose code decides the kernel's traffic: the kernel, the
+    internal header, and (decode) the launch planning in the ABI layer."""
     main = {"prefill": "prefill_mfma.hip", "copy": "copy_blocks.hip"}.get(family(workload), "decode_mfma.hip")
-    return [os.path.join(ROOT, "paged_kv_cache_372_amd", "csrc", f) for f in (main, "kernels.h")]
+    files = (main, "kernels.h", "pagedkv_abi.hip") if family(workload) == "decode" else (main, "kernels.h")
+    return [os.path.join(ROOT, "paged_kv_cache_372_amd", "csrc", f) for f in files]
 
 
 def _code_only(text: str) -> str:
@@ -147,8 +150,10 @@ def build_workload(name: str, ps: int):
 
 
 def cpu_baseline(b, budget_s: float = 12.0):
-    """The oracle, as it stands, over the sequences of the same workload, pass
-    after pass, until about ``budget_s`` seconds of CPU work are done."""
+    """The oracle, as it stands, over the same workload, one (sequence, KV
+    head) at a time -- each call covers the query heads of that KV head's
+    group -- pass after pass, until about ``budget_s`` seconds of CPU work
+    are done."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -163,23 +168,27 @@ def cpu_baseline(b, budget_s: float = 12.0):
     else:
         ks = vs = None
         kp, vp = oracle.ref_reshape_and_cache(b.k_new, b.v_new, b.slot_mapping, b.k_pool, b.v_pool)
+    G = b.num_q_heads // b.num_kv_heads
+    units = [(s, g) for s in range(b.num_seqs) for g in range(b.num_kv_heads)]
     t0 = time.perf_counter()
     done, kv_bytes, passes = 0, 0, 0
     es = {"bf16": 2, "f32": 4, "fp8": 1}[b.dtype]
     while time.perf_counter() - t0 < budget_s:
-        for s in range(b.num_seqs):
+        for s, g in units:
             oracle.ref_paged_attention_decode(b.q, kp, vp, b.block_tables, b.context_lens, b.scale, b.dtype, seqs=[s],
-                                              k_scale=ks, v_scale=vs)
+                                              q_heads=list(range(g * G, (g + 1) * G)), k_scale=ks, v_scale=vs)
             done += 1
-            kv_bytes += int(b.context_lens[s]) * 2 * b.num_kv_heads * b.head_dim * es
+            kv_bytes += int(b.context_lens[s]) * 2 * b.head_dim * es
             if time.perf_counter() - t0 >= budget_s:
                 break
         passes += 1
     dt = time.perf_counter() - t0
     return {"value": round(kv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} sequence decodes ({passes} pass(es) over the {b.num_seqs} sequences of the {b.name} "
-                      f"workload; float64, all {b.num_q_heads} q heads, after the oracle's cache write), {dt:.1f} s",
-            "tokens_per_s": round(done / dt, 3), "cpu_model": _cpu_model(), "os_cpu_count": os.cpu_count()}
+            "sample": f"{done} (sequence, KV head) decodes of the {b.name} workload ({len(units)} per pass, "
+                      f"{passes} pass(es) begun; each over its {G} query heads, float64, after the oracle's cache "
+                      f"write), {dt:.1f} s",
+            "tokens_per_s": round(done / b.num_kv_heads / dt, 3), "cpu_model": _cpu_model(),
+            "os_cpu_count": os.cpu_count()}
 
 
 def _cpu_model():
@@ -538,6 +547,155 @@ def run_copy(args):
     print(json.dumps(rec), flush=True)
 
 
+def identity_table_comparison(b, kcs, vcs, g, ps, steps, warmup, permuted_ms):
+    """Cost of the indirection: the same tokens laid out with identity block
+    tables (each sequence's blocks consecutive and in order), decode launch
+    timed by events against the permuted layout's."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_372_amd import ops
+    block_map, tables, slots = identity_layout(b)
+    bm = torch.from_numpy(block_map).cuda()
+    kid = [k.index_select(0, bm) for k in kcs]
+    vid = [v.index_select(0, bm) for v in vcs]
+    bt = torch.from_numpy(tables).cuda()
+    sl = torch.from_numpy(slots).cuda()
+    out = torch.empty_like(g["out"])
+    R = len(kid)
+    ws = torch.empty(max(1, ops.decode_workspace_bytes(b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim,
+                                                       g["max_ctx"], ps)), dtype=torch.uint8, device="cuda")
+    plans = [ops.prepare_decode(g["q"], kid[r], vid[r], bt, g["lens"], b.scale, out, partition_size=ps,
+                                max_context_len=g["max_ctx"], workspace=ws) for r in range(R)]
+
+    def step(i, ev=None):
+        r = i % R
+        ops.reshape_and_cache(g["k_new"], g["v_new"], sl, kid[r], vid[r])
+        if ev is not None:
+            ev[0].record()
+        ops.run_partitions(plans[r])
+        if ev is not None:
+            ev[1].record()
+        ops.run_reduce(plans[r])
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(out.view(torch.int16), g["out"].view(torch.int16)))
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for i in range(steps):
+        step(warmup + i, events[i])
+    torch.cuda.synchronize()
+    t = [e[0].elapsed_time(e[1]) for e in events]
+    ident = sum(t) / steps
+    return {"identity_decode_kernel_ms": round(ident, 5), "permuted_decode_kernel_ms": round(permuted_ms, 5),
+            "identity_over_permuted": round(ident / permuted_ms, 4), "identity_decode_kernel_ms_median":
+            round(float(np.median(t)), 5), "outputs_bit_identical": same,
+            "layout": "each sequence's blocks consecutive, in table order, same pool replicas"}
+
+
+def vector_alu_comparison(b, kcs, vcs, g, ps, plans, steps, warmup):
+    """The same decode (the two launches: decode and split-K reduce) on the
+    vector ALU and on the matrix cores, each timed by events over K calls,
+    alternating pool replicas as the main loop does."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_372_amd import ops
+    R = len(kcs)
+    need = ops.decode_workspace_bytes(b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim, g["max_ctx"], ps,
+                                      torch.float32)
+    ws = torch.empty(max(1, need), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(g["out"])
+
+    def valu(i):
+        r = i % R
+        ops.paged_attention_decode_vector_alu(g["q"], kcs[r], vcs[r], g["bt"], g["lens"], b.scale, out,
+                                              partition_size=ps, max_context_len=g["max_ctx"], workspace=ws)
+
+    def mfma(i):
+        ops.run_partitions(plans[0, i % R])
+        ops.run_reduce(plans[0, i % R])
+
+    res = {}
+    for name, fn in (("vector_alu", valu), ("matrix_core", mfma)):
+        for i in range(warmup):
+            fn(i)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        for i in range(steps):
+            ev[i][0].record()
+            fn(i)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        t = [e[0].elapsed_time(e[1]) for e in ev]
+        res[name + "_ms"] = round(sum(t) / steps, 5)
+        res[name + "_ms_median"] = round(float(np.median(t)), 5)
+    torch.cuda.synchronize()
+    res["vector_alu_over_matrix_core"] = round(res["vector_alu_ms"] / res["matrix_core_ms"], 4)
+    res["max_abs_diff"] = float((out.float() - g["out"].float()).abs().max().item())
+    res["what"] = "decode + split-K reduce launches, HIP events, same inputs and pool replicas"
+    return res
+
+
+HBM_READ_METRIC = "plain HBM read ceiling: GB/s of 16-byte loads (contiguous, and random tiles)"
+
+
+def run_hbm_read(args):
+    """Read-only microbenchmark: a 4 GiB buffer (16x the Infinity Cache) read
+    front to back, and as random whole tiles of 4, 16 and 32 KiB (every tile
+    once, in a seeded random order), with streaming and with ordinary loads.
+    Each launch is timed by HIP events; the headline is the contiguous
+    streaming read."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_372_amd import ops
+    nbytes = 4 << 30
+    src = torch.full((nbytes // 4,), 0x01010101, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    rng = np.random.default_rng(3729)
+    cases = [("contiguous", None, 0)]
+    for tb in (4096, 16384, 32768):
+        perm = torch.from_numpy(rng.permutation(nbytes // tb).astype(np.int32)).cuda()
+        cases.append((f"tiles_{tb // 1024}k", perm, tb))
+    # the KV bytes of one Llama-3-8B-shaped decode step (seed 3722: 578.3 MB)
+    # as random 32 KiB tiles, one K or V block of 8 heads each: a plain read
+    # of the same size, launch and drain included
+    c2_tiles = 578277376 // 32768
+    perm = torch.from_numpy(rng.permutation(nbytes // 32768)[:c2_tiles].astype(np.int32)).cuda()
+    cases.append(("tiles_32k_c2_bytes", perm, 32768))
+    out = {}
+    for name, tiles, tb in cases:
+        for streaming in (True, False):
+            def launch():
+                ops.hbm_read_bench(src, sink, tiles, tb, streaming)
+            for _ in range(args.warmup):
+                launch()
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+            torch.cuda.synchronize()
+            for i in range(args.steps):
+                ev[i][0].record()
+                launch()
+                ev[i][1].record()
+            torch.cuda.synchronize()
+            t = [e[0].elapsed_time(e[1]) for e in ev]
+            key = f"{name}_{'streaming' if streaming else 'ordinary'}"
+            nb = nbytes if tiles is None else tiles.numel() * tb
+            out[key] = {"gbs": round(nb / (sum(t) / len(t) / 1e3) / 1e9, 1),
+                        "gbs_median": round(nb / (float(np.median(t)) / 1e3) / 1e9, 1),
+                        "ms_mean": round(sum(t) / len(t), 5), "bytes": nb}
+            print(json.dumps({"case": key, **out[key]}), flush=True)
+    head = out["contiguous_streaming"]
+    rec = {"metric": HBM_READ_METRIC, "value": head["gbs"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": head["ms_mean"], "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+           "config": {"workload": "hbm_read", "buffer_bytes": nbytes, "tile_bytes": [4096, 16384, 32768],
+                      "loads": "16-byte, 8 in flight per thread, 8 workgroups of 256 threads per CU"},
+           "frac_of_peak": round(head["gbs"] / PEAK_HBM_GBS, 4),
+           "roofline": {"bound": "hbm", "achieved": head["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(head["gbs"] / PEAK_HBM_GBS, 4), "traffic": None, "kernel": "hbm_read_kernel",
+                        "bytes_per_launch": nbytes},
+           "cases": out}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -556,6 +714,14 @@ def main():
     ap.add_argument("--profile-commands", default="")
     ap.add_argument("--no-compare", action="store_true",
                     help="run only the measured form of the step (for profiles: the kernel counts one form)")
+    ap.add_argument("--no-long-context", action="store_true",
+                    help="skip the long_context record the default Llama-3-8B run carries beside its own")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time each decode launch after a 512 MiB write that flushes L2 and the Infinity Cache")
+    ap.add_argument("--vector-alu", action="store_true",
+                    help="also time the bf16 decode with every product on the vector ALU (a measurement aid)")
+    ap.add_argument("--identity-table", action="store_true",
+                    help="also time the decode on the same tokens laid out with identity block tables")
     ap.add_argument("--fused", action="store_true",
                     help="measure the fused step (paged_attention_decode_append: the cache write inside the decode "
                          "launch) where it applies")
@@ -594,6 +760,9 @@ def main():
         calibrate_copy(args.calibrate_copy, max(1, args.steps))
         return
 
+    if args.config == "hbm_read":
+        run_hbm_read(args)
+        return
     if family(args.config) == "prefill":
         run_prefill(args)
         return
@@ -601,8 +770,60 @@ def main():
         run_copy(args)
         return
 
+    rec = run_decode(args, args.config, args.partition_size, args.steps, args.warmup, args.fused,
+                     not args.no_compare, args.identity_table, args.cpu_budget, args.vector_alu)
+    if args.config == "llama3_8b_decode" and args.partition_size < 0 and not args.no_long_context:
+        # the second configuration with a bandwidth target: 8 x 128k tokens,
+        # 64 q / 8 KV heads, split-K at partition 512, on the same clock
+        import gc
+        import torch
+        gc.collect()
+        torch.cuda.empty_cache()
+        lc = run_decode(args, "long_context", 512, args.steps, args.warmup, False, False, False, args.cpu_budget)
+        keep = ("value", "unit", "ms_per_step", "step_ms_median", "step_ms_p10", "step_ms_p90", "frac_of_peak",
+                "host_enqueue_ms_per_step",
+                "tokens_per_s", "decode_kernel_ms", "decode_kernel_ms_median", "roofline", "step", "config",
+                "cpu_baseline", "input_generation_s")
+        rec["long_context"] = {k: lc[k] for k in keep if k in lc}
+    print(json.dumps(rec), flush=True)
+
+
+def identity_layout(b):
+    """The same cached tokens re-laid so that each sequence's blocks are
+    consecutive physical blocks in table order (an identity block table per
+    sequence, offset by the blocks of the sequences before it), plus one NaN
+    block at the end for table padding.  Returns (block_map, tables, slots):
+    new pool block i holds old block block_map[i]."""
+    import numpy as np
+    lens = np.asarray(b.context_lens, dtype=np.int64)
+    nblk = -(-lens // b.block_size)
+    off = np.concatenate([[0], np.cumsum(nblk)])
+    T = int(off[-1])
+    block_map = np.empty(T + 1, dtype=np.int64)
+    tables = np.full(b.block_tables.shape, T, dtype=np.int32)
+    for s in range(b.num_seqs):
+        n = int(nblk[s])
+        block_map[off[s]:off[s] + n] = b.block_tables[s, :n]
+        tables[s, :n] = np.arange(off[s], off[s] + n, dtype=np.int32)
+    block_map[T] = b.pad_block if b.pad_block >= 0 else int(b.block_tables[0, 0])
+    pos = lens - 1
+    slots = (tables[np.arange(b.num_seqs), pos // b.block_size].astype(np.int64) * b.block_size
+             + pos % b.block_size)
+    return block_map, tables, slots
+
+
+def run_decode(args, config, partition_arg, steps, warmup, fused_flag, compare_forms, identity, cpu_budget,
+               vector_alu=False):
+    """One decode workload: K timed steps of the whole hot path, then the
+    decode launch by events, a per-step event pass for the median and spread,
+    and the CPU oracle on a bounded sample.  Returns the bench record."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_372_amd import ops
+    from paged_kv_cache_372_amd.blocks import tables_share_blocks
+
     t_gen = time.perf_counter()
-    b, batching_steps = build_workload(args.config, args.partition_size)
+    b, batching_steps = build_workload(config, partition_arg)
     gen_s = time.perf_counter() - t_gen
     fp8 = b.dtype == "fp8"
     dtype = torch.float32 if b.dtype == "f32" else torch.bfloat16   # q / out (bf16 over an fp8 cache)
@@ -634,7 +855,7 @@ def main():
     k0, v0 = dev(b.k_pool), dev(b.v_pool)
     kcs = [k0] + [k0.clone() for _ in range(R - 1)]
     vcs = [v0] + [v0.clone() for _ in range(R - 1)]
-    ps = b.partition_size if args.partition_size < 0 else args.partition_size
+    ps = b.partition_size if partition_arg < 0 else partition_arg
     gpu_steps = []
     for (kw, vw, sm, qh, bth, lh) in host_steps:
         q = dev(qh)
@@ -668,8 +889,8 @@ def main():
     fusable = (b.dtype == "bf16" and b.num_q_heads // b.num_kv_heads <= 16 and
                all(len(h[2]) == len(h[5]) and int(np.min(h[5])) >= 1 and
                    np.array_equal(np.asarray(h[2], dtype=np.int64), append_slots(h[4], h[5])) for h in host_steps))
-    fused = fusable and args.fused
-    compare = fusable and not args.no_compare
+    fused = fusable and fused_flag
+    compare = fusable and compare_forms
     fplans = {}
     if fusable:
         for j, g in enumerate(gpu_steps):
@@ -703,7 +924,7 @@ def main():
 
     step = step_fused if fused else step_two_call
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
         if compare:
             (step_two_call if fused else step_fused)(i)
@@ -711,11 +932,12 @@ def main():
 
     # timed region 1: K whole steps, nothing but the kernels on the stream
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i)
+    for i in range(steps):
+        step(warmup + i)
+    t_enq = time.perf_counter() - t0   # host time to enqueue the K steps
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    timed_kv = sum(step_kv[(args.warmup + i) % n_in] for i in range(args.steps))
+    timed_kv = sum(step_kv[(warmup + i) % n_in] for i in range(steps))
 
     # the other form of the same steps, for comparison: wall time, then the
     # decode launch by events
@@ -724,27 +946,27 @@ def main():
         other = step_two_call if fused else step_fused
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        for i in range(args.steps):
-            other(args.warmup + i)
+        for i in range(steps):
+            other(warmup + i)
         torch.cuda.synchronize()
         other_wall = time.perf_counter() - t1
-        oev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-        for i in range(args.steps):
-            other(args.warmup + i, oev[i])
+        oev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        for i in range(steps):
+            other(warmup + i, oev[i])
         torch.cuda.synchronize()
-        other_dec = sum(e[0].elapsed_time(e[1]) for e in oev) / args.steps
+        other_dec = sum(e[0].elapsed_time(e[1]) for e in oev) / steps
 
     # timed region 2: the same K steps with HIP events around each decode
     # launch (on the launch stream), for the decode kernel's own duration
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     torch.cuda.synchronize()
-    for i in range(args.steps):
-        step(args.warmup + args.steps + i, events[i])
+    for i in range(steps):
+        step(warmup + steps + i, events[i])
     torch.cuda.synchronize()
     dec_times = [e[0].elapsed_time(e[1]) for e in events]
-    dec = sum(dec_times) / args.steps
-    dec_kv = sum(step_kv[(args.warmup + args.steps + i) % n_in] for i in range(args.steps))
-    ms_per_step = wall / args.steps * 1e3
+    dec = sum(dec_times) / steps
+    dec_kv = sum(step_kv[(warmup + steps + i) % n_in] for i in range(steps))
+    ms_per_step = wall / steps * 1e3
     value = timed_kv / wall / 1e9
     achieved = dec_kv / (sum(dec_times) / 1e3) / 1e9
     traffic = measured_traffic(b.name, resolved_ps, fused)
@@ -754,8 +976,8 @@ def main():
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -773,6 +995,7 @@ def main():
         "frac_of_peak": round(value / PEAK_HBM_GBS, 4),
         "tokens_per_s": round(b.num_seqs / (ms_per_step / 1e3), 1),
         "decode_kernel_ms": round(dec, 5),
+        "host_enqueue_ms_per_step": round(t_enq / steps * 1e3, 5),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "kernel": "decode_valu_kernel" if b.dtype == "f32" else "decode_bf16_balanced_kernel",
@@ -781,16 +1004,50 @@ def main():
     }
     if other_wall is not None:
         key = "two_call" if fused else "fused"
-        rec[key] = {"ms_per_step": round(other_wall / args.steps * 1e3, 5),
+        rec[key] = {"ms_per_step": round(other_wall / steps * 1e3, 5),
                     "value": round(timed_kv / other_wall / 1e9, 2),
                     "decode_kernel_ms": round(other_dec, 5)}
+    # per-step spread: each whole step bracketed by events (the timed region
+    # above has no events in it)
+    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        sev[i][0].record()
+        step(warmup + 2 * steps + i)
+        sev[i][1].record()
+    torch.cuda.synchronize()
+    step_times = sorted(e[0].elapsed_time(e[1]) for e in sev)
+    rec["step_ms_median"] = round(float(np.median(step_times)), 5)
+    rec["step_ms_p10"] = round(float(np.percentile(step_times, 10)), 5)
+    rec["step_ms_p90"] = round(float(np.percentile(step_times, 90)), 5)
+    rec["decode_kernel_ms_median"] = round(float(np.median(dec_times)), 5)
+    if args.cold:
+        # each decode launch after a 512 MiB write that evicts L2 and the
+        # Infinity Cache: cold caches, against the warm rotation above
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        for i in range(steps):
+            flush.fill_(i & 0xFF)
+            step(warmup + 3 * steps + i, cev[i])
+        torch.cuda.synchronize()
+        ct = [e[0].elapsed_time(e[1]) for e in cev]
+        rec["cold"] = {"decode_kernel_ms": round(sum(ct) / steps, 5),
+                       "decode_kernel_ms_median": round(float(np.median(ct)), 5),
+                       "flush_bytes": 512 << 20,
+                       "kv_gbs": round(kv_bytes / (sum(ct) / steps / 1e3) / 1e9, 2)}
+        del flush
+    if vector_alu and b.dtype == "bf16" and batching_steps is None:
+        rec["vector_alu"] = vector_alu_comparison(b, kcs, vcs, gpu_steps[0], ps, plans, steps, warmup)
+    if identity and batching_steps is None:
+        rec["identity_table"] = identity_table_comparison(b, kcs, vcs, gpu_steps[0], ps, steps, warmup, dec)
     try:
         rec["host_pack_h2d_ms"] = round(host_pack_ms(b), 4)
     except Exception as e:  # aux figure only
         rec["host_pack_h2d_ms"] = f"unavailable: {e}"
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(b, args.cpu_budget)
-    print(json.dumps(rec), flush=True)
+        rec["cpu_baseline"] = cpu_baseline(b, cpu_budget)
+    return rec
 
 
 if __name__ == "__main__":
