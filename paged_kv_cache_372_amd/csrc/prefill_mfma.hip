@@ -90,7 +90,17 @@ __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
     // codes of bytes 2*kHigh, 2*kHigh + 1; scale 1.0: the exact value of each code
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHigh));
 }
+template <bool kHigh>
+__device__ __forceinline__ uint32_t e4m3x2_to_f16x2(uint32_t w) {
+    // the same codes as fp16: every E4M3 value (at most 448, at least 2^-9
+    // apart from zero, 4 significant bits) is exact in fp16 too
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, kHigh));
+}
 
+// K becomes bf16 operands (q is bf16); V becomes fp16 operands, for a PV
+// product in fp16: the weights then enter it with 11 significant bits
+// instead of bf16's 8 (weights lie in [0, 2^8], inside fp16's range; those
+// below 2^-24 flush to zero, next to a largest weight of at least 1).
 // K: the QK contraction takes dims in the order that makes step kk read half
 // (kk & 1) of chunk load kk / 2 (q is loaded in the same order).  V: word c
 // of lane (d, g) must hold tokens 4g..4g+3 of dim 16c + d, while lane
@@ -125,8 +135,8 @@ __device__ __forceinline__ PairRegs<D> widen_pair(const PairRegs8<D>& r) {
         }
 #pragma unroll
     for (int c = 0; c < D / 16; ++c)
-        o.v[c] = u32x4_t{e4m3x2_to_bf16x2<false>(w[0][c]), e4m3x2_to_bf16x2<true>(w[0][c]),
-                         e4m3x2_to_bf16x2<false>(w[1][c]), e4m3x2_to_bf16x2<true>(w[1][c])};
+        o.v[c] = u32x4_t{e4m3x2_to_f16x2<false>(w[0][c]), e4m3x2_to_f16x2<true>(w[0][c]),
+                         e4m3x2_to_f16x2<false>(w[1][c]), e4m3x2_to_f16x2<true>(w[1][c])};
     return o;
 }
 
@@ -153,6 +163,12 @@ typedef float float2_t __attribute__((ext_vector_type(2)));
 // two fp32 -> packed bf16 (round to nearest even), one instruction
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{a, b}, bf16x2_t));
+}
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+// two fp32 -> packed fp16 (round to nearest even)
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{a, b}, f16x2_t));
 }
 
 __device__ __forceinline__ uint32_t tail_mask(int nv, int first) {
@@ -447,13 +463,24 @@ __global__ __launch_bounds__(64 * PrefillShape<kFp8>::kWaves) void prefill_bf16_
                     for (int i = 0; i < 8; ++i) pr[i] = exp2_fast(fmaf(sv[j][i], c_scale, -m_use));
                 }
                 st[j].l += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
-                const bf16x8_t pj = __builtin_bit_cast(
-                    bf16x8_t, make_uint4(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
-                                         pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])));
+                if constexpr (kFp8) {
+                    // fp16 weights against the fp16 V operands (see widen_pair)
+                    const f16x8_t pj = __builtin_bit_cast(
+                        f16x8_t, make_uint4(pack_f16x2(pr[0], pr[1]), pack_f16x2(pr[2], pr[3]),
+                                            pack_f16x2(pr[4], pr[5]), pack_f16x2(pr[6], pr[7])));
 #pragma unroll
-                for (int c = 0; c < D / 16; ++c)
-                    acc[j][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.v[c]), pj,
-                                                                        acc[j][c], 0, 0, 0);
+                    for (int c = 0; c < D / 16; ++c)
+                        acc[j][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, r.v[c]), pj,
+                                                                           acc[j][c], 0, 0, 0);
+                } else {
+                    const bf16x8_t pj = __builtin_bit_cast(
+                        bf16x8_t, make_uint4(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
+                                             pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])));
+#pragma unroll
+                    for (int c = 0; c < D / 16; ++c)
+                        acc[j][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.v[c]), pj,
+                                                                            acc[j][c], 0, 0, 0);
+                }
             }
             if constexpr (!kMasked) {
                 // Interleave: the weights of tile j + 1 (VALU) are computed
