@@ -18,7 +18,9 @@
  *   - Pointers marked [device] are device addresses (e.g. from a torch CUDA
  *     tensor); the caller owns all memory.  The library never allocates,
  *     frees or synchronises, and keeps no state between calls (it reads
- *     the current device's compute-unit count to plan a launch).
+ *     the current device's compute-unit count to plan a launch).  The one
+ *     exception is the fixed device scratch of
+ *     pkv_paged_attention_decode_noalloc (see there).
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
  *     stream).  A returned PKV_OK means the work was enqueued.
  *   - Problems visible on the host (null pointer, bad size, unsupported
@@ -247,6 +249,36 @@ pkv_status pkv_paged_attention_decode_append_partitions(const void* q, const voi
                                                         int32_t partition_size, void* workspace,
                                                         size_t workspace_bytes, pkv_dtype kv_dtype,
                                                         pkv_dtype out_dtype, uint32_t flags, void* stream);
+
+/*
+ * Decode with no allocation and no workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments, result and
+ * launches as pkv_paged_attention_decode (bit-identical output), with the
+ * workspace taken from a fixed device array of PKV_NOALLOC_SCRATCH_BYTES
+ * inside the library instead of from the caller.
+ *   - Each device holds its own copy of that array from the first use of
+ *     the library on it until the process ends; its address is looked up on
+ *     the first call on each device.  The call allocates and frees nothing.
+ *   - Sizes whose workspace (pkv_decode_workspace_bytes) exceeds
+ *     PKV_NOALLOC_SCRATCH_BYTES return PKV_ERR_WORKSPACE before any launch
+ *     (e.g. 64 query heads of 8 x 128k-token contexts fit with
+ *     partition_size 0, not with partition_size 512).
+ *   - All calls on one device share the array, which keeps the last call's
+ *     contents (the kernels need no initialised contents).  Calls that
+ *     overlap on one device -- on different streams, or from several host
+ *     threads without ordering -- race on it: order them on one stream.
+ *   - fp8 pools are refused (PKV_ERR_UNSUPPORTED), as for the plain call.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+pkv_status pkv_paged_attention_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                              const int32_t* block_tables, const int32_t* context_lens, float scale,
+                                              void* out, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                              int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                              int32_t max_blocks_per_seq, int32_t max_context_len,
+                                              int32_t partition_size, pkv_dtype kv_dtype, pkv_dtype out_dtype,
+                                              uint32_t flags, void* stream);
 
 /*
  * fp8 KV cache.  The pages name quantisation of the KV cache as the lever for

@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/pagedkv.h"
 #include "kernels.h"
 
@@ -460,6 +462,87 @@ pkv_status pkv_paged_attention_decode_append_partitions(const void* q, const voi
                                    flags, &c);
     if (st != PKV_OK) return st;
     return run_decode_kernels(c, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of pkv_paged_attention_decode_noalloc: a fixed device array that
+// takes the place of the caller's workspace (the flattened block offsets
+// and the split-K partials).  Every device the library runs on holds its
+// own copy, from the first use of this code object until the process ends.
+// In host code `scratch` is only a host-side stand-in for the symbol; its
+// device address is looked up once per device (scratch_address) and only
+// that address is ever passed to a kernel.
+static __device__ __align__(256) unsigned char scratch[PKV_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device
+
+// Address of `scratch` on the current device (looked up on the first call
+// on that device, with that device current).
+pkv_status scratch_address(void** out) {
+    int dev = -1;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return from_hip(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(PKV_ERR_UNSUPPORTED, "device %d: the fixed scratch serves devices 0..%d", dev, kMaxDevices - 1);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        const hipError_t r = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (r != hipSuccess || !p) return from_hip(r != hipSuccess ? r : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_paged_attention_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                              const int32_t* block_tables, const int32_t* context_lens, float scale,
+                                              void* out, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                              int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                              int32_t max_blocks_per_seq, int32_t max_context_len,
+                                              int32_t partition_size, pkv_dtype kv_dtype, pkv_dtype out_dtype,
+                                              uint32_t flags, void* stream) {
+    g_last_error[0] = 0;
+    if (kv_dtype == PKV_FP8_E4M3)
+        return fail(PKV_ERR_UNSUPPORTED, "an fp8 cache needs its scales: use pkv_paged_attention_decode_fp8");
+    Plan pl;
+    pkv_status st = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                              max_context_len, partition_size, kv_dtype, &pl);
+    if (st != PKV_OK) return st;
+    if (pl.workspace > (size_t)PKV_NOALLOC_SCRATCH_BYTES)
+        return fail(PKV_ERR_WORKSPACE,
+                    "these sizes need %zu bytes of scratch; the fixed scratch holds %zu (pass a workspace to "
+                    "pkv_paged_attention_decode instead)",
+                    pl.workspace, (size_t)PKV_NOALLOC_SCRATCH_BYTES);
+    // every host-side check first, against a stand-in address (256-byte
+    // aligned, never dereferenced), then the scratch's device address
+    void* const stand_in = reinterpret_cast<void*>((uintptr_t)256);
+    Call c;
+    st = prepare(q, k_cache, v_cache, block_tables, context_lens, scale, out, num_seqs, num_q_heads, num_kv_heads,
+                 head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len, partition_size,
+                 pl.workspace ? stand_in : nullptr, pl.workspace ? (size_t)PKV_NOALLOC_SCRATCH_BYTES : 0, kv_dtype,
+                 out_dtype, flags, nullptr, nullptr, &c);
+    if (st != PKV_OK) return st;
+    if (num_seqs == 0) return PKV_OK;
+    void* ws = nullptr;
+    if (pl.workspace > 0) {
+        st = scratch_address(&ws);
+        if (st != PKV_OK) return st;
+    }
+    bind_workspace(&c, ws);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    st = run_decode_kernels(c, s);
+    if (st != PKV_OK) return st;
+    return run_reduce_kernels(c, s);
 }
 
 pkv_status pkv_reshape_and_cache_fp8(const void* k_new, const void* v_new, const int64_t* slot_mapping,

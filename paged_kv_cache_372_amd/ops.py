@@ -48,6 +48,8 @@ _SIGNATURES = {
     "pkv_paged_attention_decode_append_partitions": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _i32, _i32,
                                                             _i32, _i32, _i32, _i64, _i32, _i32, _i32, _vp, _sz, _i32,
                                                             _i32, _u32, _vp]),
+    "pkv_paged_attention_decode_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _f32, _vp, _i32, _i32, _i32, _i32, _i32,
+                                                  _i64, _i32, _i32, _i32, _i32, _i32, _u32, _vp]),
     "pkv_reshape_and_cache_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _i32, _vp]),
     "pkv_paged_attention_decode_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _i32, _i32, _i32, _i32, _i32,
                                               _i64, _i32, _i32, _i32, _vp, _sz, _i32, _u32, _vp]),
@@ -268,6 +270,40 @@ def paged_attention_decode_append(q: torch.Tensor, k_new: torch.Tensor, v_new: t
     a = _DecodeArgs(q, k_cache, v_cache, block_tables, context_lens, scale, out, partition_size, max_context_len,
                     workspace, shared_blocks, k_new=k_new, v_new=v_new)
     _check(load_library().pkv_paged_attention_decode_append(*a.args), "paged_attention_decode_append")
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # the library's fixed decode scratch (PKV_NOALLOC_SCRATCH_BYTES)
+
+
+def paged_attention_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                   block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                                   out: torch.Tensor, *, max_context_len: int, partition_size: int = 0,
+                                   shared_blocks: bool = False) -> None:
+    """``paged_attention_decode`` with no workspace and no allocation, for callers that cannot allocate
+    (graph capture, tight serving loops).  The library's fixed per-device scratch
+    (``NOALLOC_SCRATCH_BYTES``) stands in for the workspace; sizes that need more raise.  Calls that
+    overlap on one device (other streams, other threads) race on that scratch.  ``max_context_len`` is
+    required: finding it on the device would need a synchronisation and an allocation.  bf16 or f32 pools.
+    """
+    lib = load_library()
+    dev = q.device
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (block_tables, "block_tables"),
+                 (context_lens, "context_lens"), (out, "out")):
+        _check_tensor(t, n, dev)
+    nb, hkv, D = _pool_dims(k_cache, v_cache)
+    _require(q.dim() == 3 and q.shape[2] == D and q.dtype == k_cache.dtype, f"q must be [B, Hq, {D}] of the pools' dtype")
+    B, hq = q.shape[0], q.shape[1]
+    _require(tuple(out.shape) == tuple(q.shape), "out must have q's shape")
+    _require(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and block_tables.shape[0] == B,
+             "block_tables must be int32 [B, max_blocks_per_seq]")
+    _require(context_lens.dtype == torch.int32 and tuple(context_lens.shape) == (B,), "context_lens must be int32 [B]")
+    _require(max_context_len is not None, "max_context_len is required")
+    st = lib.pkv_paged_attention_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                                _ptr(context_lens), float(scale), _ptr(out), B, hq, hkv, D,
+                                                BLOCK_SIZE, nb, block_tables.shape[1], int(max_context_len),
+                                                int(partition_size), _dtype_code(k_cache), _dtype_code(out),
+                                                DECODE_SHARED_BLOCKS if shared_blocks else 0, _stream(dev))
+    _check(st, "paged_attention_decode_noalloc")
 
 
 def prepare_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out, *, partition_size=0,

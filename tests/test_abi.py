@@ -152,6 +152,36 @@ def test_decode_validation(lib):
     assert red == WORKSPACE
 
 
+def dec_noalloc(lib, **kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, lens=FAKE, scale=0.1, out=FAKE, B=4, hq=32, hkv=8, D=128, bs=16,
+             nb=100, maxblk=128, maxctx=2000, ps=0, kvd=BF16, outd=BF16, flags=0)
+    a.update(kw)
+    return lib.pkv_paged_attention_decode_noalloc(a["q"], a["kc"], a["vc"], a["bt"], a["lens"], a["scale"], a["out"],
+                                                  a["B"], a["hq"], a["hkv"], a["D"], a["bs"], a["nb"], a["maxblk"],
+                                                  a["maxctx"], a["ps"], a["kvd"], a["outd"], a["flags"], None)
+
+
+def test_decode_noalloc_validation(lib):
+    """The no-allocation decode checks its arguments like the plain one, before touching the device."""
+    assert dec_noalloc(lib, hq=30) == INVALID
+    assert dec_noalloc(lib, D=96) == UNSUPPORTED
+    assert dec_noalloc(lib, kvd=FP8) == UNSUPPORTED
+    assert dec_noalloc(lib, q=None) == INVALID
+    assert dec_noalloc(lib, flags=2) == INVALID
+    assert dec_noalloc(lib, scale=math.nan) == INVALID
+    assert dec_noalloc(lib, kc=FAKE + 8) == INVALID
+    # sizes whose workspace exceeds the fixed scratch are refused before any launch
+    big = dict(B=8, hq=64, hkv=8, maxblk=8192, maxctx=131072, ps=512)
+    need = lib.pkv_decode_workspace_bytes(8, 64, 8, 128, 131072, 512, BF16)
+    assert need > ops.NOALLOC_SCRATCH_BYTES
+    assert dec_noalloc(lib, **big) == WORKSPACE
+    assert b"scratch" in lib.pkv_last_error()
+    # ... while the balanced split of the same batch fits
+    assert lib.pkv_decode_workspace_bytes(8, 64, 8, 128, 131072, 0, BF16) <= ops.NOALLOC_SCRATCH_BYTES
+    # nothing to do: no launch, no device access
+    assert dec_noalloc(lib, B=0, q=None, kc=None, vc=None, bt=None, lens=None, out=None) == OK
+
+
 def test_hbm_read_bench_validation(lib):
     sink = FAKE
     assert lib.pkv_hbm_read_bench(FAKE, 0, None, 0, 4096, 1, sink, None) == INVALID
