@@ -749,8 +749,23 @@ __global__ __launch_bounds__(64 * kMaxWavesPerGroup) void decode_bf16_balanced_k
     // with the block kDepth positions further on.  In the last rounds the
     // refills past the walk's end are skipped (kFinal); before that every
     // refill is issued, which keeps the loop's waits exact.
+    //
+    // The waves of a workgroup run in lockstep: a barrier at the top of
+    // every round (no memory wait; every wave of the workgroup walks the
+    // same ranges, so all run the same rounds).  Two waves share each SIMD,
+    // and left alone one of them ran ahead: wave timestamps (s_memrealtime)
+    // on 8 x 128k tokens showed the waves of one compute unit finishing up
+    // to ~240 us apart around a 700 us launch, every compute unit alike,
+    // and the unit slowing once its fast waves were done (the last 10 % of
+    // the blocks took a fifth of the launch).  Whatever the cause (wave
+    // priorities, KV-head order and four-wave workgroups were tried), in
+    // lockstep the unit keeps all eight waves' loads in flight to the end.
+    // Measured (rocprof, same session): 8 x 128k decode 672 us against 693
+    // (eight waves, no barrier) and 691-695 (two four-wave workgroups per
+    // unit); the Llama-shaped batch 94.1-94.7 us against 94.6.
     auto round = [&](int i, auto final_tag) {
         constexpr bool kFinal = decltype(final_tag)::value;
+        __builtin_amdgcn_s_barrier();
         // entries of positions i + kDepth + d, fetched one round ago
 #pragma unroll
         for (int d = 0; d < kDepth; ++d) accept(pend[d], next_pb[d], next_info[d]);

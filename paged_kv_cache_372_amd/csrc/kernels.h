@@ -11,8 +11,7 @@ namespace pkv {
 constexpr int kBlockSize = 16;           // tokens per KV block
 constexpr int kMfmaHeadsPerUnit = 16;    // query heads one MFMA decode wave serves (tile width)
 constexpr int kValuHeadsPerUnit = 8;     // query heads one VALU decode wave serves (register budget)
-constexpr int kMaxWavesPerGroup = 8;     // KV-head waves a balanced-decode workgroup can hold
-constexpr int kPlanWavesPerGroup = 4;    // KV-head waves per workgroup the plan launches (see make_plan)
+constexpr int kMaxWavesPerGroup = 8;     // KV-head waves in one balanced-decode workgroup
 constexpr int kMaxSeqsPerLaunch = 4096;  // sequences one balanced-decode launch takes (LDS tables)
 constexpr int kMinRangeBlocks = 4;       // shortest range of blocks one workgroup walks
 

@@ -119,14 +119,9 @@ pkv_status make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads
     pl->num_chunks = num_seqs > 0 ? (int32_t)ceil_div(num_seqs, pl->chunk_seqs) : 0;
     pl->head_units = num_kv_heads * pl->n_head_groups;
 
-    // Four KV-head waves per workgroup, two workgroups per compute unit.
-    // Against eight waves per workgroup (one per CU), same sessions: the
-    // Llama-shaped step 103.7-104.3 us against 105.9-106.9, the 8 x 128k
-    // decode 698-699 us against 705-709, fp8 8 x 128k 417 against 421.
-    // With eight, waves 4-7 of every workgroup finished about a third
-    // later than waves 0-3 (wave timestamps), whatever their KV head and
-    // wave priorities.
-    pl->waves_per_group = pl->head_units < pkv::kPlanWavesPerGroup ? pl->head_units : pkv::kPlanWavesPerGroup;
+    // Up to eight KV-head waves per workgroup, one workgroup per compute
+    // unit, kept in lockstep by the kernel (a barrier per round of blocks).
+    pl->waves_per_group = pl->head_units < pkv::kMaxWavesPerGroup ? pl->head_units : pkv::kMaxWavesPerGroup;
     pl->head_unit_groups = (int32_t)ceil_div(pl->head_units, pl->waves_per_group);
     const int64_t slots = resident_groups(head_dim, pl->waves_per_group, pl->chunk_seqs > 0 ? pl->chunk_seqs : 1);
     const int64_t w = slots / pl->head_unit_groups;
