@@ -304,8 +304,9 @@ pkv_status pkv_reshape_and_cache_fp8(const void* k_new, const void* v_new, const
 /*
  * Decode over an fp8 cache: pkv_paged_attention_decode with K = decode(code) *
  * k_scale[g] and V = decode(code) * v_scale[g] for KV head g.  q is bf16; out
- * is out_dtype.  The codes are converted to bf16 exactly and the products
- * run as for a bf16 cache (the scales enter the score scale and the output).
+ * is out_dtype.  The codes are converted exactly: K to bf16 for the products
+ * with q, V to fp16 for the products with the softmax weights, which enter
+ * them rounded to fp16 (the scales enter the score scale and the output).
  * Workspace: pkv_decode_workspace_bytes(..., PKV_FP8_E4M3).  The other decode
  * entry points reject PKV_FP8_E4M3.
  */

@@ -39,6 +39,8 @@
 // mantissa bits of the fp32 weights.  With bf16 pools and at most 8 heads in
 // the group, the lo terms ride in the otherwise unused head columns 8..15 and
 // one MFMA per 16 dims carries both; otherwise a second MFMA takes them.
+// Over an fp8 cache the V codes are widened to fp16 (exactly) and P is
+// rounded to fp16 once (11 significant bits): one fp16 MFMA per 16 dims.
 //
 // Why the pool layout is what it is: the MFMA A operand wants, in lane l,
 // 8 consecutive K values of token (l % 16); with K stored as 16-byte chunks
@@ -101,6 +103,19 @@ template <bool kHigh>
 __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
     // codes of bytes 2*kHigh, 2*kHigh + 1; scale 1.0: the exact value of each code
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHigh));
+}
+template <bool kHigh>
+__device__ __forceinline__ uint32_t e4m3x2_to_f16x2(uint32_t w) {
+    // the same codes as fp16, also exact (E4M3: at most 448, 4 significant
+    // bits, nothing below 2^-9 but zero)
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, kHigh));
+}
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+// two fp32 -> packed fp16, round to nearest even (one v_cvt_pk_f16_f32)
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{a, b}, f16x2_t));
 }
 
 template <int D>
@@ -168,12 +183,12 @@ struct SoftmaxState {
 // moves less often.
 constexpr float kRescaleSlack = 8.f;
 
-// An fp8 V word (fp8_v_words) as a bf16 operand with the tokens past
+// An fp8 V word (fp8_v_words) as an fp16 operand with the tokens past
 // valid_n zeroed: one byte per token (tokens 4g..4g+3), so one mask serves
 // all words.
 __device__ __forceinline__ uint2 v_operand_fp8(uint32_t w, uint32_t vm) {
     w &= vm;
-    return make_uint2(e4m3x2_to_bf16x2<false>(w), e4m3x2_to_bf16x2<true>(w));
+    return make_uint2(e4m3x2_to_f16x2<false>(w), e4m3x2_to_f16x2<true>(w));
 }
 template <int D>
 __device__ __forceinline__ uint2 v_operand_masked(const SlotRegs<D>& r, int c, uint2 vm) {
@@ -225,43 +240,46 @@ __device__ __forceinline__ void compute_block(const Slot& r, float4_t* acc, Soft
     for (int i = 0; i < 4; ++i) pr[i] = exp2_fast(sv[i] - m_use);
     st.l += (pr[0] + pr[1]) + (pr[2] + pr[3]);
 
-    // P^T as the B operand: x = p - (p & lo_mask) is p itself in the hi
-    // columns and p minus its bf16 truncation in the lo columns; the upper
-    // 16 bits of x are the term the column feeds.
-    uint32_t xw[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t pb = __float_as_uint(pr[i]);
-        xw[i] = kPackLo ? __float_as_uint(pr[i] - __uint_as_float(pb & lo_mask)) : pb;
-    }
-    const short4_t p_hi = __builtin_bit_cast(short4_t, make_uint2(__builtin_amdgcn_perm(xw[1], xw[0], 0x07060302u),
-                                                                  __builtin_amdgcn_perm(xw[3], xw[2], 0x07060302u)));
-    short4_t p_lo;
-    if constexpr (!kPackLo) {
-        uint32_t lw[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) lw[i] = __float_as_uint(pr[i] - __uint_as_float(xw[i] & 0xFFFF0000u));
-        p_lo = __builtin_bit_cast(short4_t, make_uint2(__builtin_amdgcn_perm(lw[1], lw[0], 0x07060302u),
-                                                       __builtin_amdgcn_perm(lw[3], lw[2], 0x07060302u)));
-    }
-
-    auto pv = [&](int c, uint2 vw) __attribute__((always_inline)) {
-        const short4_t a = __builtin_bit_cast(short4_t, vw);
-        acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, p_hi, acc[c], 0, 0, 0);
-        if constexpr (!kPackLo) acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, p_lo, acc[c], 0, 0, 0);
-    };
-    // tokens past the end hold stale or NaN data: zero them (0 * NaN = NaN);
-    // only the last block of a sequence has such tokens
     if constexpr (std::is_same_v<Slot, SlotRegs<D>>) {
+        // P^T as the B operand: x = p - (p & lo_mask) is p itself in the hi
+        // columns and p minus its bf16 truncation in the lo columns; the upper
+        // 16 bits of x are the term the column feeds.
+        uint32_t xw[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t pb = __float_as_uint(pr[i]);
+            xw[i] = kPackLo ? __float_as_uint(pr[i] - __uint_as_float(pb & lo_mask)) : pb;
+        }
+        const short4_t p_hi = __builtin_bit_cast(short4_t, make_uint2(__builtin_amdgcn_perm(xw[1], xw[0], 0x07060302u),
+                                                                      __builtin_amdgcn_perm(xw[3], xw[2], 0x07060302u)));
+        short4_t p_lo;
+        if constexpr (!kPackLo) {
+            uint32_t lw[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) lw[i] = __float_as_uint(pr[i] - __uint_as_float(xw[i] & 0xFFFF0000u));
+            p_lo = __builtin_bit_cast(short4_t, make_uint2(__builtin_amdgcn_perm(lw[1], lw[0], 0x07060302u),
+                                                           __builtin_amdgcn_perm(lw[3], lw[2], 0x07060302u)));
+        }
+        // tokens past the end hold stale or NaN data: zero them (0 * NaN =
+        // NaN); only the last block of a sequence has such tokens
         const uint2 vm = valid_n < 16 ? v_mask_bf16(valid_n, g) : make_uint2(0xFFFFFFFFu, 0xFFFFFFFFu);
 #pragma unroll
-        for (int c = 0; c < D / 16; ++c) pv(c, v_operand_masked<D>(r, c, vm));
+        for (int c = 0; c < D / 16; ++c) {
+            const short4_t a = __builtin_bit_cast(short4_t, v_operand_masked<D>(r, c, vm));
+            acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, p_hi, acc[c], 0, 0, 0);
+            if constexpr (!kPackLo) acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, p_lo, acc[c], 0, 0, 0);
+        }
     } else {
+        // fp8 pools: V widened to fp16 (exact) and the weights rounded to
+        // fp16 once (11 significant bits), one fp16 MFMA per 16 dims.
+        const f16x4_t p16 = __builtin_bit_cast(f16x4_t, make_uint2(pack_f16x2(pr[0], pr[1]), pack_f16x2(pr[2], pr[3])));
         const uint32_t vm = valid_n < 16 ? v_mask_fp8(valid_n, g) : 0xFFFFFFFFu;
         uint32_t w[D / 16];
         fp8_v_words<D>(r, w);
 #pragma unroll
-        for (int c = 0; c < D / 16; ++c) pv(c, v_operand_fp8(w[c], vm));
+        for (int c = 0; c < D / 16; ++c)
+            acc[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, v_operand_fp8(w[c], vm)), p16,
+                                                           acc[c], 0, 0, 0);
     }
 }
 
@@ -845,9 +863,8 @@ void launch_balanced(const DecodeParams& p, dim3 grid, dim3 block, size_t lds, h
         hipLaunchKernelGGL((decode_bf16_balanced_kernel<D, kDepth, false, kFp8, kPackLo>), grid, block, lds, stream, p);
 }
 
-// The packed lo terms are used for bf16 pools only: with fp8 pools the
-// variant with two PV MFMAs per 16 dims measured about 10 % faster (456 vs
-// 507 us on 8 x 128k tokens), although it issues more instructions.
+// The packed lo terms are used for bf16 pools only; fp8 pools take fp16
+// weights, one MFMA per 16 dims (compute_block).
 template <int D, bool kFp8>
 void launch_balanced(const DecodeParams& p, dim3 grid, dim3 block, size_t lds, hipStream_t stream) {
     if (!kFp8 && p.group <= kMfmaHeadsPerUnit / 2) launch_balanced<D, false, true>(p, grid, block, lds, stream);
