@@ -4,11 +4,14 @@
 
 One step is one pass of the whole hot path over one batch: the cache write of
 every sequence's new token, the block-table-driven decode partitions, and the
-split-K reduce: reshape_and_cache, then paged_attention_decode.  Where every
-sequence gains one bf16 token at position L - 1 (the static decode
-workloads), the fused form of the same step, whose decode launch stores the
-new tokens itself (paged_attention_decode_append), is timed beside it and
-reported under ``fused``; ``--fused`` makes it the measured step.  The default workload is the
+split-K reduce.  Where every sequence gains one bf16 token at position L - 1
+(the static bf16 decode workloads) the measured step is the fused form,
+paged_attention_decode_append, whose decode launch stores the new tokens
+itself (bit for bit the result of the two calls); the two-call form,
+reshape_and_cache then paged_attention_decode, is timed beside it and
+reported under ``two_call`` (``--two-call`` makes it the measured step).
+Other workloads (fp32, fp8, continuous batching with prompt writes) take the
+two calls.  The default workload is the
 Llama-3-8B-shaped decode layer (64 sequences, 32 q / 8 KV heads, head_dim 128,
 bf16 KV, context lengths uniform on [128, 4096]).  Inputs are resident in HBM
 before timing starts.  To keep the 256 MB Infinity Cache from serving KV
@@ -50,6 +53,10 @@ def family(workload: str) -> str:
     if workload in COPY_CONFIGS:
         return "copy"
     return "decode"
+
+
+# static bf16 decode workloads whose step can take the fused append
+FUSABLE_CONFIGS = ("llama3_8b_decode", "shared_prefix", "long_context")
 
 
 def traffic_file(workload: str, fused: bool = False) -> str:
@@ -311,7 +318,7 @@ def summarize_profile(prefix: str, workload: str, partition_size, copy_mib: int,
     if os.path.exists(bench_log):
         last = [ln for ln in open(bench_log).read().splitlines() if ln.startswith("{")]
         if last:
-            flag = " --fused" if fused else ""
+            flag = "" if fused or workload not in FUSABLE_CONFIGS else " --two-call"
             lines += ["", f"## Bench line of the same build (`python bench.py --config {workload}{flag}`)", "", "```",
                       last[-1], "```"]
     rec = {"source_sha256": kernel_source_hash(workload), "workload": workload, "partition_size": partition_size,
@@ -722,8 +729,12 @@ def main():
                     help="also time the bf16 decode with every product on the vector ALU (a measurement aid)")
     ap.add_argument("--identity-table", action="store_true",
                     help="also time the decode on the same tokens laid out with identity block tables")
+    ap.add_argument("--two-call", action="store_true",
+                    help="measure the two-call step (reshape_and_cache, then paged_attention_decode) where the fused "
+                         "one applies")
     ap.add_argument("--fused", action="store_true",
-                    help="measure the fused step (paged_attention_decode_append: the cache write inside the decode "
+                    help="(default where it applies) measure the fused step (paged_attention_decode_append: the cache "
+                         "write inside the decode "
                          "launch) where it applies")
     args = ap.parse_args()
 
@@ -736,11 +747,12 @@ def main():
         ps = ps if ps > 0 else "balanced"
         if family(args.config) != "decode":
             ps = "none"
-        tag = "_fused" if args.fused else ""
+        fused = args.config in FUSABLE_CONFIGS and not args.two_call
+        tag = "_fused" if fused else ""
         summarize_profile(args.summarize_profile, args.config, ps, args.profile_copy_mib,
                           os.path.join(ROOT, "profiles", f"{family(args.config)}_{args.config}{tag}.md"),
-                          traffic_file(args.config, args.fused),
-                          open(args.profile_commands).read() if args.profile_commands else "", args.fused)
+                          traffic_file(args.config, fused),
+                          open(args.profile_commands).read() if args.profile_commands else "", fused)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -770,7 +782,7 @@ def main():
         run_copy(args)
         return
 
-    rec = run_decode(args, args.config, args.partition_size, args.steps, args.warmup, args.fused,
+    rec = run_decode(args, args.config, args.partition_size, args.steps, args.warmup, not args.two_call,
                      not args.no_compare, args.identity_table, args.cpu_budget, args.vector_alu)
     if args.config == "llama3_8b_decode" and args.partition_size < 0 and not args.no_long_context:
         # the second configuration with a bandwidth target: 8 x 128k tokens,
@@ -779,9 +791,10 @@ def main():
         import torch
         gc.collect()
         torch.cuda.empty_cache()
-        lc = run_decode(args, "long_context", 512, args.steps, args.warmup, False, False, False, args.cpu_budget)
+        lc = run_decode(args, "long_context", 512, args.steps, args.warmup, not args.two_call, True, False,
+                        args.cpu_budget)
         keep = ("value", "unit", "ms_per_step", "step_ms_median", "step_ms_p10", "step_ms_p90", "frac_of_peak",
-                "host_enqueue_ms_per_step",
+                "host_enqueue_ms_per_step", "two_call", "fused",
                 "tokens_per_s", "decode_kernel_ms", "decode_kernel_ms_median", "roofline", "step", "config",
                 "cpu_baseline", "input_generation_s")
         rec["long_context"] = {k: lc[k] for k in keep if k in lc}
