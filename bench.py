@@ -67,8 +67,12 @@ def traffic_file(workload: str, fused: bool = False) -> str:
 def kernel_sources(workload: str):
     """Sources whose code decides the kernel's traffic: the kernel, the
     internal header, and (decode) the launch planning in the ABI layer."""
-    main = {"prefill": "prefill_mfma.hip", "copy": "copy_blocks.hip"}.get(family(workload), "decode_mfma.hip")
-    files = (main, "kernels.h", "pagedkv_abi.hip") if family(workload) == "decode" else (main, "kernels.h")
+    if family(workload) == "prefill":
+        main = "prefill_mfma.hip" if workload.endswith("_fp8") else "prefill_wide.hip"
+        files = (main, "prefill_common.h", "kernels.h")
+    else:
+        main = "copy_blocks.hip" if family(workload) == "copy" else "decode_mfma.hip"
+        files = (main, "kernels.h", "pagedkv_abi.hip") if family(workload) == "decode" else (main, "kernels.h")
     return [os.path.join(ROOT, "paged_kv_cache_372_amd", "csrc", f) for f in files]
 
 
@@ -251,7 +255,8 @@ def calibrate_copy(mib: int, reps: int):
 
 
 DECODE_KERNEL_PREFIX = "void pkv::(anonymous namespace)::decode_bf16_balanced_kernel"
-PREFILL_KERNEL_PREFIX = "void pkv::(anonymous namespace)::prefill_bf16_kernel"
+PREFILL_KERNEL_PREFIX = {False: "void pkv::(anonymous namespace)::prefill_wide_kernel",
+                         True: "void pkv::(anonymous namespace)::prefill_fp8_kernel"}
 COPY_KERNEL_PREFIX = "pkv::(anonymous namespace)::copy_blocks_kernel"
 
 
@@ -291,7 +296,8 @@ def summarize_profile(prefix: str, workload: str, partition_size, copy_mib: int,
     copy_name = "__amd_rocclr_copyBuffer"
     f_factor = copy_kib / cal_f[copy_name]
     w_factor = copy_kib / cal_w[copy_name]
-    prefix_k = {"prefill": PREFILL_KERNEL_PREFIX, "copy": COPY_KERNEL_PREFIX}.get(family(workload), DECODE_KERNEL_PREFIX)
+    prefix_k = {"prefill": PREFILL_KERNEL_PREFIX[workload.endswith("_fp8")],
+                "copy": COPY_KERNEL_PREFIX}.get(family(workload), DECODE_KERNEL_PREFIX)
     short_k = prefix_k.split("::")[-1]
     dec = [k for k in fetch if short_k in k][0]
     form = " (fused append step)" if fused else ""
@@ -449,7 +455,7 @@ def run_prefill(args):
         "prefill_kernel_ms": round(k_ms, 5),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "kernel": "prefill_bf16_kernel", "flops_per_launch": flops},
+                     "kernel": "prefill_fp8_kernel" if fp8 else "prefill_wide_kernel", "flops_per_launch": flops},
         "input_generation_s": round(gen_s, 2),
     }
     if not args.no_cpu_baseline:

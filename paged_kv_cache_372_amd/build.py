@@ -35,6 +35,7 @@ HIPCC_FLAGS = [
 # compiler drops the quieting max(x, x) it puts before every fmaxf.
 FILE_FLAGS = {
     "prefill_mfma.hip": ["-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form", "-Xarch_device", "-fno-honor-nans"],
+    "prefill_wide.hip": ["-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form", "-Xarch_device", "-fno-honor-nans"],
 }
 
 

@@ -1,5 +1,5 @@
-// Multi-token-query paged attention (chunked prefill), bf16 KV, on the gfx950
-// matrix cores.
+// Multi-token-query paged attention (chunked prefill) over an fp8 (E4M3)
+// cache, on the gfx950 matrix cores.  (bf16 pools take prefill_wide.hip.)
 //
 // What is computed.  A request s brings n_s >= 1 new query tokens whose keys
 // and values are already in the paged cache, which then holds L_s tokens, the
@@ -9,64 +9,55 @@
 // long prompts are cut into chunks that share each step with decode requests
 // (architvora "Continuous Batching"), so a chunk attends over everything
 // cached before it plus itself.  The keys are reached through the request's
-// block table (architvora "Paged Attention").
+// block table (architvora "Paged Attention").  K and V are stored as E4M3
+// codes with one scale per KV head: K's scale joins the score scale, V's
+// the output.
 //
 // Work decomposition.  The rows of a request are its (query token, head of
 // the KV group) pairs, token-major: n_s * G rows per KV head.  A workgroup
-// takes 256 consecutive rows of one (request, KV head); each of its 4 waves
-// (8 over an fp8 cache) takes 64 rows (32) and walks, on its own, the key
-// blocks those rows can see.  The waves read the same K/V blocks at about
-// the same time, so the
+// takes 256 consecutive rows of one (request, KV head); each of its 8 waves
+// takes 32 rows and walks, on its own, the key blocks those rows can see.
+// The waves read the same K/V blocks at about the same time, so the
 // workgroup's loads hit in L1/L2 after the first; the KV head is the
 // workgroup index modulo Hkv, which keeps each head on one XCD (with 8 KV
 // heads) and its blocks in that XCD's L2.  Heaviest tiles (the last rows of
 // a request see the most keys) are launched first.
 //
-// Per pair of 16-token blocks (A, B), per wave, for each of its four 16-row
+// Per pair of 16-token blocks (A, B), per wave, for each of its two 16-row
 // column tiles j:
 //   S^T[32 keys x 16 rows] = K . Q_j^T        2 x D/32 x mfma_f32_16x16x32_bf16
 //   online softmax on S (exp2 domain, scale*log2e folded in, causal mask)
-//   O_j^T[D x 16 rows] += V^T . P_j^T         D/16 x mfma_f32_16x16x32_bf16
+//   O_j^T[D x 16 rows] += V^T . P_j^T         D/16 x mfma_f32_16x16x32_f16
 // The K-dimension of the PV product runs over the 32 keys of the pair in the
 // order (A 4g..4g+3, B 4g..4g+3) for lane group g: that is exactly what the
 // QK result leaves in each lane, so P needs no data movement, and the V^T
-// operand is the two 8-byte V loads of A and B side by side.  P is rounded
-// to bf16 once (a flash-attention-style product; decode, which is bound by
-// memory, carries two bf16 terms instead).
+// operand is the two 8-byte V rows of A and B side by side (see widen_pair).
+// P is rounded once, to fp16, against V's codes as fp16.
 //
-// Memory: K/V operands are loaded straight from the pool into a register
-// ring two pairs deep (the pool layout makes each load a contiguous 1 KiB or
-// 512 B run per wave); table entries come through the scalar cache one round
-// ahead, as in the decode kernel.  There is no LDS staging: LDS-DMA loads
-// make the compiler wait for every load in flight before any LDS read.
+// Memory: K/V codes are loaded straight from the pool into a register ring
+// two pairs deep (each load a contiguous 1 KiB run per wave); table entries
+// come through the scalar cache one round ahead, as in the decode kernel.
 #include <type_traits>
 
-#include "kernels.h"
+#include "prefill_common.h"
 
 namespace pkv {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
-typedef const int32_t __attribute__((address_space(4)))* scalar_i32_ptr;
 
-// Shape of a workgroup (256 rows either way).  bf16 pools: 4 waves of 64
-// rows, one wave per SIMD.  fp8 pools: the ring of raw codes is half the
-// registers, so 8 waves of 32 rows fit two waves per SIMD, and one wave's
-// softmax runs under the other's products.  Measured on the chunked-prefill
-// workload over an fp8 cache: 662 against 583 TFLOP/s (one pair in flight:
-// 637).  The 8 x 32 shape for bf16 spills with two pairs in flight and
-// measured 524 against 680 with one.
-template <bool kFp8>
-struct PrefillShape {
-    static constexpr int kWaves = kFp8 ? 8 : 4;
+// Shape of a workgroup: 8 waves of 32 rows.  The ring of raw codes is half
+// the registers bf16 operands would take, so two waves fit per SIMD and one
+// wave's softmax runs under the other's products.  Measured on the
+// chunked-prefill workload over an fp8 cache: 662 against 583 TFLOP/s for 4
+// waves of 64 rows (one pair in flight: 637).
+struct Fp8Shape {
+    static constexpr int kWaves = 8;
     static constexpr int kRowsPerWave = kPrefillRowsPerGroup / kWaves;
-    static constexpr int kNQ = kRowsPerWave / 16;                // 16-row column tiles per wave
-    static constexpr int kPairDepth = 2;                         // block pairs in flight per wave
+    static constexpr int kNQ = kRowsPerWave / 16;  // 16-row column tiles per wave
+    static constexpr int kPairDepth = 2;           // block pairs in flight per wave
 };
-constexpr float kSlack = 8.f;                    // lazy-rescale margin (log2 units)
 constexpr int kExpValu = 28;                     // VALU instructions for one column tile's weights
 
 template <int D>
@@ -157,13 +148,6 @@ struct ColState {
     float l;  // this lane's share of the sum of weights
 };
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float float2_t __attribute__((ext_vector_type(2)));
-
-// two fp32 -> packed bf16 (round to nearest even), one instruction
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{a, b}, bf16x2_t));
-}
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 // two fp32 -> packed fp16 (round to nearest even)
@@ -171,91 +155,21 @@ __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{a, b}, f16x2_t));
 }
 
-__device__ __forceinline__ uint32_t tail_mask(int nv, int first) {
-    // 16-bit lanes [first, first + 1] of a token run, kept when inside nv
-    return nv >= first + 2 ? 0xFFFFFFFFu : (nv == first + 1 ? 0x0000FFFFu : 0u);
-}
-
-template <int D, bool kFp8>
-__global__ __launch_bounds__(64 * PrefillShape<kFp8>::kWaves) void prefill_bf16_kernel(PrefillParams p) {
-    constexpr int kPrefillWaves = PrefillShape<kFp8>::kWaves;
-    constexpr int kPrefillRowsPerWave = PrefillShape<kFp8>::kRowsPerWave;
-    constexpr int kNQ = PrefillShape<kFp8>::kNQ;
-    constexpr int kPairDepth = PrefillShape<kFp8>::kPairDepth;
-    using Elem = std::conditional_t<kFp8, uint8_t, uint16_t>;  // one K/V pool element
-    using Ring = std::conditional_t<kFp8, PairRegs8<D>, PairRegs<D>>;
+template <int D>
+__global__ __launch_bounds__(64 * Fp8Shape::kWaves) void prefill_fp8_kernel(PrefillParams p) {
+    constexpr int kPrefillWaves = Fp8Shape::kWaves;
+    constexpr int kPrefillRowsPerWave = Fp8Shape::kRowsPerWave;
+    constexpr int kNQ = Fp8Shape::kNQ;
+    constexpr int kPairDepth = Fp8Shape::kPairDepth;
+    using Ring = PairRegs8<D>;
     extern __shared__ int32_t t_off[];  // [B + 1] first workgroup tile of each request
     __shared__ int32_t wave_total[kPrefillWaves];
-    const int B = p.num_seqs;
-    const int T = p.num_tokens;
     const int G = p.group;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-
-    // rows [r0, r1) of q/out belong to request i (clamped to the call's T)
-    auto rows_of = [&](int i, int& r0, int& r1) {
-        r0 = min(max(p.query_start_loc[i], 0), T);
-        r1 = min(max(p.query_start_loc[i + 1], r0), T);
-    };
-
-    // ---- workgroup tiles of every request (exclusive prefix sums)
-    {
-        const int nthr = 64 * kPrefillWaves;
-        const int per = (B + nthr - 1) / nthr;
-        const int i0 = min(B, tid * per);
-        const int i1 = min(B, i0 + per);
-        int sum = 0;
-        for (int i = i0; i < i1; ++i) {
-            int a, b;
-            rows_of(i, a, b);
-            sum += ((b - a) * G + kPrefillRowsPerGroup - 1) / kPrefillRowsPerGroup;
-        }
-        int x = sum;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const int y = __shfl_up(x, d);
-            if (lane >= d) x += y;
-        }
-        if (lane == 63) wave_total[wave] = x;
-        __syncthreads();
-        int run = x - sum;
-        for (int w = 0; w < wave; ++w) run += wave_total[w];
-        for (int i = i0; i < i1; ++i) {
-            t_off[i] = run;
-            int a, b;
-            rows_of(i, a, b);
-            run += ((b - a) * G + kPrefillRowsPerGroup - 1) / kPrefillRowsPerGroup;
-        }
-        if (tid == nthr - 1) t_off[B] = run;
-        __syncthreads();
-    }
-    // values read from LDS or memory below are the same in every lane; say
-    // so, so that table entries are fetched through the scalar cache
-    const int total = __builtin_amdgcn_readfirstlane(t_off[B]);
-    const int idx = blockIdx.x / p.num_kv_heads;
-    const int kvh = blockIdx.x - idx * p.num_kv_heads;
-    if (idx >= total) return;
-    const int tile = total - 1 - idx;  // heaviest tiles first
-    int s = 0;
-    {
-        int lo = 0, hi = B - 1;  // last request whose first tile is <= tile
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (t_off[mid] <= tile) lo = mid;
-            else hi = mid - 1;
-        }
-        s = __builtin_amdgcn_readfirstlane(lo);
-    }
-    int r0, r1;
-    rows_of(s, r0, r1);
-    r0 = __builtin_amdgcn_readfirstlane(r0);
-    r1 = __builtin_amdgcn_readfirstlane(r1);
-    const int n = r1 - r0;
-    const int rows = n * G;
-    const int R0 = (tile - __builtin_amdgcn_readfirstlane(t_off[s])) * kPrefillRowsPerGroup + wave * kPrefillRowsPerWave;
+    const int lane = threadIdx.x & 63;
+    WaveRows wr;
+    if (!locate_rows<kPrefillWaves, kPrefillRowsPerWave>(p, t_off, wave_total, wr)) return;
+    const int s = wr.s, r0 = wr.r0, n = wr.n, rows = wr.rows, R0 = wr.R0, L = wr.L, kvh = wr.kvh;
     if (R0 >= rows) return;  // no barrier follows
-    const int L = __builtin_amdgcn_readfirstlane(clamp_ctx(p.context_lens[s], p.ctx_cap));
     const int Rl = min(R0 + kPrefillRowsPerWave - 1, rows - 1);
     const int kend = min(L, L - n + Rl / G + 1);  // keys [0, kend) are visible to some row
 
@@ -279,11 +193,11 @@ __global__ __launch_bounds__(64 * PrefillShape<kFp8>::kWaves) void prefill_bf16_
         }
     }
 
-    // Q^T operands: column tile j, k-group g holds dims 32kk + 8g .. +7.
-    // A negative scale is carried by q (negating bf16 is exact), so the
-    // softmax below works with c = |scale * log2 e| >= 0.
-    // (an fp8 cache: K's scale joins the score scale, V's the output)
-    const float eff_scale = kFp8 ? p.scale_log2 * p.k_scale[kvh] : p.scale_log2;
+    // Q^T operands: step kk, k-group g holds dims 64(kk/2) + 16g + 8(kk&1)
+    // .. +7, the order widen_pair gives K.  A negative scale is carried by q
+    // (negating bf16 is exact), so the softmax below works with
+    // c = |scale * log2 e * k_scale| >= 0.
+    const float eff_scale = p.scale_log2 * p.k_scale[kvh];
     const float c_scale = fabsf(eff_scale);
     const uint32_t qsign = eff_scale < 0.f ? 0x80008000u : 0u;
     bf16x8_t qv[kNQ][D / 32];
@@ -293,8 +207,7 @@ __global__ __launch_bounds__(64 * PrefillShape<kFp8>::kWaves) void prefill_bf16_
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk) {
             uint4 w = make_uint4(0, 0, 0, 0);
-            // fp8: step kk, group g takes dims 64(kk/2) + 16g + 8(kk&1) .. +7
-            const int dq = kFp8 ? 64 * (kk >> 1) + 16 * g + 8 * (kk & 1) : 32 * kk + 8 * g;
+            const int dq = 64 * (kk >> 1) + 16 * g + 8 * (kk & 1);
             if (orow[j] >= 0) w = *reinterpret_cast<const uint4*>(qb + orow[j] + dq);
             w.x ^= qsign;
             w.y ^= qsign;
@@ -320,10 +233,9 @@ __global__ __launch_bounds__(64 * PrefillShape<kFp8>::kWaves) void prefill_bf16_
 
     if (NP > 0) {
         const int64_t block_stride = (int64_t)p.num_kv_heads * D * kBlockSize;
-        const Elem* k_head = reinterpret_cast<const Elem*>(p.k_cache) + (int64_t)kvh * D * kBlockSize;
-        const Elem* v_head = reinterpret_cast<const Elem*>(p.v_cache) + (int64_t)kvh * D * kBlockSize;
+        const uint8_t* k_head = reinterpret_cast<const uint8_t*>(p.k_cache) + (int64_t)kvh * D * kBlockSize;
+        const uint8_t* v_head = reinterpret_cast<const uint8_t*>(p.v_cache) + (int64_t)kvh * D * kBlockSize;
         const scalar_i32_ptr bt = (scalar_i32_ptr)(p.block_tables + (int64_t)s * p.max_blocks_per_seq);
-        const int vo = (lane & 15) * 4 + (lane >> 4);
 
         Ring ring[kPairDepth];
         PairInfo info[kPairDepth];
@@ -354,29 +266,16 @@ __global__ __launch_bounds__(64 * PrefillShape<kFp8>::kWaves) void prefill_bf16_
             // read the same blocks
             const u32x4_t* ka = reinterpret_cast<const u32x4_t*>(k_head + (int64_t)pa * block_stride);
             const u32x4_t* kb = reinterpret_cast<const u32x4_t*>(k_head + (int64_t)pb * block_stride);
-            if constexpr (kFp8) {
-                const u32x4_t* va = reinterpret_cast<const u32x4_t*>(v_head + (int64_t)pa * block_stride);
-                const u32x4_t* vb = reinterpret_cast<const u32x4_t*>(v_head + (int64_t)pb * block_stride);
+            const u32x4_t* va = reinterpret_cast<const u32x4_t*>(v_head + (int64_t)pa * block_stride);
+            const u32x4_t* vb = reinterpret_cast<const u32x4_t*>(v_head + (int64_t)pb * block_stride);
 #pragma unroll
-                for (int i = 0; i < D / 64; ++i) ring[d].k[0][i] = __builtin_bit_cast(uint4, ka[i * 64 + lane]);
+            for (int i = 0; i < D / 64; ++i) ring[d].k[0][i] = __builtin_bit_cast(uint4, ka[i * 64 + lane]);
 #pragma unroll
-                for (int i = 0; i < D / 64; ++i) ring[d].k[1][i] = __builtin_bit_cast(uint4, kb[i * 64 + lane]);
+            for (int i = 0; i < D / 64; ++i) ring[d].k[1][i] = __builtin_bit_cast(uint4, kb[i * 64 + lane]);
 #pragma unroll
-                for (int i = 0; i < D / 64; ++i) ring[d].v[0][i] = __builtin_bit_cast(uint4, va[i * 64 + lane]);
+            for (int i = 0; i < D / 64; ++i) ring[d].v[0][i] = __builtin_bit_cast(uint4, va[i * 64 + lane]);
 #pragma unroll
-                for (int i = 0; i < D / 64; ++i) ring[d].v[1][i] = __builtin_bit_cast(uint4, vb[i * 64 + lane]);
-            } else {
-                const u32x2_t* va = reinterpret_cast<const u32x2_t*>(v_head + (int64_t)pa * block_stride);
-                const u32x2_t* vb = reinterpret_cast<const u32x2_t*>(v_head + (int64_t)pb * block_stride);
-#pragma unroll
-                for (int kk = 0; kk < D / 32; ++kk) ring[d].k[0][kk] = __builtin_bit_cast(uint4, ka[kk * 64 + lane]);
-#pragma unroll
-                for (int kk = 0; kk < D / 32; ++kk) ring[d].k[1][kk] = __builtin_bit_cast(uint4, kb[kk * 64 + lane]);
-#pragma unroll
-                for (int c = 0; c < D / 16; ++c) ring[d].v[c].xy = va[c * 64 + vo];
-#pragma unroll
-                for (int c = 0; c < D / 16; ++c) ring[d].v[c].zw = vb[c * 64 + vo];
-            }
+            for (int i = 0; i < D / 64; ++i) ring[d].v[1][i] = __builtin_bit_cast(uint4, vb[i * 64 + lane]);
         };
 
         // One pair.  kMasked: the pair holds tokens past the context end or
@@ -384,12 +283,7 @@ __global__ __launch_bounds__(64 * PrefillShape<kFp8>::kWaves) void prefill_bf16_
         // score is live and the mask work is skipped.
         auto compute_pair = [&](Ring& rr, const PairInfo& inf, auto masked_tag) __attribute__((always_inline)) {
             constexpr bool kMasked = decltype(masked_tag)::value;
-            PairRegs<D> rw;
-            if constexpr (kFp8) rw = widen_pair<D>(rr);
-            PairRegs<D>& r = [&]() -> PairRegs<D>& {
-                if constexpr (kFp8) return rw;
-                else return rr;
-            }();
+            PairRegs<D> r = widen_pair<D>(rr);
             if constexpr (kMasked) {
                 // tokens past a block's valid count are zeroed in place (they
                 // may hold NaN, and 0 * NaN = NaN)
@@ -463,24 +357,14 @@ __global__ __launch_bounds__(64 * PrefillShape<kFp8>::kWaves) void prefill_bf16_
                     for (int i = 0; i < 8; ++i) pr[i] = exp2_fast(fmaf(sv[j][i], c_scale, -m_use));
                 }
                 st[j].l += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
-                if constexpr (kFp8) {
-                    // fp16 weights against the fp16 V operands (see widen_pair)
-                    const f16x8_t pj = __builtin_bit_cast(
-                        f16x8_t, make_uint4(pack_f16x2(pr[0], pr[1]), pack_f16x2(pr[2], pr[3]),
-                                            pack_f16x2(pr[4], pr[5]), pack_f16x2(pr[6], pr[7])));
+                // fp16 weights against the fp16 V operands (see widen_pair)
+                const f16x8_t pj = __builtin_bit_cast(
+                    f16x8_t, make_uint4(pack_f16x2(pr[0], pr[1]), pack_f16x2(pr[2], pr[3]),
+                                        pack_f16x2(pr[4], pr[5]), pack_f16x2(pr[6], pr[7])));
 #pragma unroll
-                    for (int c = 0; c < D / 16; ++c)
-                        acc[j][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, r.v[c]), pj,
-                                                                           acc[j][c], 0, 0, 0);
-                } else {
-                    const bf16x8_t pj = __builtin_bit_cast(
-                        bf16x8_t, make_uint4(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
-                                             pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])));
-#pragma unroll
-                    for (int c = 0; c < D / 16; ++c)
-                        acc[j][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.v[c]), pj,
-                                                                            acc[j][c], 0, 0, 0);
-                }
+                for (int c = 0; c < D / 16; ++c)
+                    acc[j][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, r.v[c]), pj,
+                                                                       acc[j][c], 0, 0, 0);
             }
             if constexpr (!kMasked) {
                 // Interleave: the weights of tile j + 1 (VALU) are computed
@@ -512,117 +396,6 @@ __global__ __launch_bounds__(64 * PrefillShape<kFp8>::kWaves) void prefill_bf16_
             load_pair(d, next_pa[d], next_pb[d], next_info[d]);
             __builtin_amdgcn_sched_barrier(0);
         }
-        // bf16, mask-free pairs: the pieces of compute_pair, so that one
-        // pair's QK products can run under the previous pair's softmax
-        auto qk_free = [&](const PairRegs<D>& r, float (*sv)[8], float* mx) __attribute__((always_inline)) {
-#pragma unroll
-            for (int j = 0; j < kNQ; ++j) {
-                float4_t sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kk = 0; kk < D / 32; ++kk) {
-                    sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.k[0][kk]), qv[j][kk],
-                                                                 sa, 0, 0, 0);
-                    sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.k[1][kk]), qv[j][kk],
-                                                                 sb, 0, 0, 0);
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    sv[j][i] = sa[i];
-                    sv[j][4 + i] = sb[i];
-                }
-            }
-        };
-        auto max_free = [&](float (*sv)[8], float* mx) __attribute__((always_inline)) {
-#pragma unroll
-            for (int j = 0; j < kNQ; ++j) {
-                const float m8 = fmaxf(fmaxf(fmaxf(sv[j][0], sv[j][1]), fmaxf(sv[j][2], sv[j][3])),
-                                       fmaxf(fmaxf(sv[j][4], sv[j][5]), fmaxf(sv[j][6], sv[j][7])));
-                mx[j] = max_over_groups(m8) * c_scale;  // all scores live and c >= 0: scale the max only
-            }
-        };
-        auto rescale = [&](const float* mx) __attribute__((always_inline)) {
-            bool raise[kNQ];
-            bool any = false;
-#pragma unroll
-            for (int j = 0; j < kNQ; ++j) {
-                raise[j] = mx[j] > st[j].m + kSlack;
-                any = any || raise[j];
-            }
-            if (__any(any)) {
-#pragma unroll
-                for (int j = 0; j < kNQ; ++j) {
-                    const float alpha = raise[j] ? exp2_fast(st[j].m - mx[j]) : 1.f;
-                    st[j].l *= alpha;
-#pragma unroll
-                    for (int c = 0; c < D / 16; ++c) acc[j][c] *= alpha;
-                    st[j].m = raise[j] ? mx[j] : st[j].m;
-                }
-            }
-        };
-        auto pv_free = [&](const PairRegs<D>& r, float (*sv)[8]) __attribute__((always_inline)) {
-#pragma unroll
-            for (int j = 0; j < kNQ; ++j) {
-                const float m_use = st[j].m == -INFINITY ? 0.f : st[j].m;
-                float pr[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) pr[i] = exp2_fast(fmaf(sv[j][i], c_scale, -m_use));
-                st[j].l += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
-                const bf16x8_t pj = __builtin_bit_cast(
-                    bf16x8_t, make_uint4(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
-                                         pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])));
-#pragma unroll
-                for (int c = 0; c < D / 16; ++c)
-                    acc[j][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.v[c]), pj,
-                                                                        acc[j][c], 0, 0, 0);
-            }
-        };
-        // A mask-free round of two pairs, pipelined: QK(0), its rescale
-        // check, then one scheduling region with the weights and PV products
-        // of pair 0 and the QK products and maxima of pair 1, then pair 1's
-        // check and PV products.
-        auto round_pipe = [&](int i) __attribute__((always_inline)) {
-#pragma unroll
-            for (int d = 0; d < kPairDepth; ++d) accept(pend[d], next_pa[d], next_pb[d], next_info[d]);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int d = 0; d < kPairDepth; ++d) fetch(i + 2 * kPairDepth + d, pend[d]);
-            if constexpr (!kFp8) {
-                float sv0[kNQ][8], mx0[kNQ], sv1[kNQ][8], mx1[kNQ];
-                qk_free(ring[0], sv0, mx0);
-                max_free(sv0, mx0);
-                rescale(mx0);
-                __builtin_amdgcn_sched_barrier(0);
-                qk_free(ring[1], sv1, mx1);
-                pv_free(ring[0], sv0);
-                max_free(sv1, mx1);
-                // interleave: one MFMA, then three VALU, over the region.
-                // Measured on the chunked-prefill workload (TFLOP/s, same
-                // session): 3 VALU per MFMA 690, 2 685, 4 675, 4 then 2
-                // 673, 5 then 1 668; without the pipelined round 681.
-#pragma unroll
-                for (int t = 0; t < 2 * kNQ * (D / 16); ++t) {
-                    __builtin_amdgcn_sched_group_barrier(0x8, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x2, 3, 0);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-                load_pair(0, next_pa[0], next_pb[0], next_info[0]);
-                __builtin_amdgcn_sched_barrier(0);
-                rescale(mx1);
-                __builtin_amdgcn_sched_barrier(0);
-                pv_free(ring[1], sv1);
-                __builtin_amdgcn_sched_group_barrier(0x2, kExpValu, 0);
-#pragma unroll
-                for (int t = 0; t < (kNQ - 1) * (D / 16); ++t) {
-                    __builtin_amdgcn_sched_group_barrier(0x8, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x2, kExpValu / (D / 16), 0);
-                }
-                __builtin_amdgcn_sched_group_barrier(0x8, D / 16, 0);
-                __builtin_amdgcn_sched_barrier(0);
-                load_pair(1, next_pa[1], next_pb[1], next_info[1]);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        };
-
         auto round = [&](int i, auto final_tag, auto masked_tag) __attribute__((always_inline)) {
             constexpr bool kFinal = decltype(final_tag)::value;
 #pragma unroll
@@ -646,10 +419,8 @@ __global__ __launch_bounds__(64 * PrefillShape<kFp8>::kWaves) void prefill_bf16_
         // included, take the masked form.
         const int NPf = min(NP, (qmin + 1) / (2 * kBlockSize));
         int i = 0;
-        for (; i + 2 * kPairDepth <= NP && i + kPairDepth <= NPf; i += kPairDepth) {
-            if constexpr (!kFp8 && kPairDepth == 2) round_pipe(i);
-            else round(i, std::false_type{}, std::false_type{});
-        }
+        for (; i + 2 * kPairDepth <= NP && i + kPairDepth <= NPf; i += kPairDepth)
+            round(i, std::false_type{}, std::false_type{});
         for (; i + 2 * kPairDepth <= NP; i += kPairDepth) round(i, std::false_type{}, std::true_type{});
         for (; i < NP; i += kPairDepth) round(i, std::true_type{}, std::true_type{});
     }
@@ -659,7 +430,7 @@ __global__ __launch_bounds__(64 * PrefillShape<kFp8>::kWaves) void prefill_bf16_
 #pragma unroll
     for (int j = 0; j < kNQ; ++j) {
         const float lt = sum_over_groups(st[j].l);
-        const float inv = lt > 0.f ? (kFp8 ? p.v_scale[kvh] : 1.f) / lt : 0.f;
+        const float inv = lt > 0.f ? p.v_scale[kvh] / lt : 0.f;
         if (orow[j] < 0) continue;
         if (obf) {
             uint16_t* ob = reinterpret_cast<uint16_t*>(p.out) + orow[j] + 4 * g;
@@ -685,15 +456,11 @@ size_t prefill_lds_bytes(int32_t num_seqs) { return (size_t)(num_seqs + 1) * siz
 hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream) {
     if (p.num_seqs == 0 || p.tile_bound == 0) return hipSuccess;
     const dim3 grid((unsigned)((int64_t)p.tile_bound * p.num_kv_heads));
-    const dim3 block(64 * (p.kv_fp8 ? PrefillShape<true>::kWaves : PrefillShape<false>::kWaves));
+    if (!p.kv_fp8) return launch_prefill_wide(p, stream);
+    const dim3 block(64 * Fp8Shape::kWaves);
     const size_t lds = prefill_lds_bytes(p.num_seqs);
-    if (p.kv_fp8) {
-        if (p.head_dim == 128) hipLaunchKernelGGL((prefill_bf16_kernel<128, true>), grid, block, lds, stream, p);
-        else hipLaunchKernelGGL((prefill_bf16_kernel<64, true>), grid, block, lds, stream, p);
-    } else {
-        if (p.head_dim == 128) hipLaunchKernelGGL((prefill_bf16_kernel<128, false>), grid, block, lds, stream, p);
-        else hipLaunchKernelGGL((prefill_bf16_kernel<64, false>), grid, block, lds, stream, p);
-    }
+    if (p.head_dim == 128) hipLaunchKernelGGL((prefill_fp8_kernel<128>), grid, block, lds, stream, p);
+    else hipLaunchKernelGGL((prefill_fp8_kernel<64>), grid, block, lds, stream, p);
     return hipGetLastError();
 }
 
