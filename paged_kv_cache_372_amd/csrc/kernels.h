@@ -111,12 +111,16 @@ struct PrefillParams {
     int32_t kv_fp8;                 // 1: pools hold E4M3 codes ([NB][Hkv][D/16][16][16] and [NB][Hkv][D][16])
     const float* k_scale;           // fp8: [Hkv] K dequantisation scale
     const float* v_scale;           // fp8: [Hkv] V dequantisation scale
+    int32_t lpt_buckets;            // tile weight classes (tiles are taken heaviest first)
+    int32_t lpt_shift;              // a weight class is 2^lpt_shift keys
 };
 
 // Rows (query token x head of a KV group) one prefill workgroup covers.
 constexpr int kPrefillRowsPerGroup = 256;
+// LDS for a prefill workgroup's tile order: num_seqs + 3 + lpt_buckets ints
+constexpr int kPrefillPlanLdsBytes = 48 * 1024;
 
-size_t prefill_lds_bytes(int32_t num_seqs);
+size_t prefill_lds_bytes(int32_t num_seqs, int32_t lpt_buckets);
 hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream);
 
 // Balanced bf16 decode: dynamic LDS bytes and launch shape.

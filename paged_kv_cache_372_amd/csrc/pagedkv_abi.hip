@@ -733,6 +733,11 @@ pkv_status prefill_impl(const void* q, const void* k_cache, const void* v_cache,
             return fail(PKV_ERR_UNSUPPORTED, "%d tokens x %d query heads: too many workgroups for one launch",
                         num_tokens, num_q_heads);
         p.tile_bound = (int32_t)bound;
+        // weight classes for the heaviest-first tile order: 64-key classes,
+        // coarser when the LDS for them would not fit
+        p.lpt_shift = 6;
+        while ((int64_t)(n + 3 + (p.ctx_cap >> p.lpt_shift) + 2) * 4 > pkv::kPrefillPlanLdsBytes) ++p.lpt_shift;
+        p.lpt_buckets = (p.ctx_cap >> p.lpt_shift) + 2;
         pkv_status rc = from_hip(pkv::launch_prefill_bf16(p, st), "prefill kernel launch");
         if (rc != PKV_OK) return rc;
     }

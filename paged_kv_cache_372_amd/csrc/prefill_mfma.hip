@@ -162,12 +162,12 @@ __global__ __launch_bounds__(64 * Fp8Shape::kWaves) void prefill_fp8_kernel(Pref
     constexpr int kNQ = Fp8Shape::kNQ;
     constexpr int kPairDepth = Fp8Shape::kPairDepth;
     using Ring = PairRegs8<D>;
-    extern __shared__ int32_t t_off[];  // [B + 1] first workgroup tile of each request
+    extern __shared__ int32_t plan[];  // tile order (see locate_rows)
     __shared__ int32_t wave_total[kPrefillWaves];
     const int G = p.group;
     const int lane = threadIdx.x & 63;
     WaveRows wr;
-    if (!locate_rows<kPrefillWaves, kPrefillRowsPerWave>(p, t_off, wave_total, wr)) return;
+    if (!locate_rows<kPrefillWaves, kPrefillRowsPerWave>(p, plan, wave_total, wr)) return;
     const int s = wr.s, r0 = wr.r0, n = wr.n, rows = wr.rows, R0 = wr.R0, L = wr.L, kvh = wr.kvh;
     if (R0 >= rows) return;  // no barrier follows
     const int Rl = min(R0 + kPrefillRowsPerWave - 1, rows - 1);
@@ -451,14 +451,16 @@ __global__ __launch_bounds__(64 * Fp8Shape::kWaves) void prefill_fp8_kernel(Pref
 
 }  // namespace
 
-size_t prefill_lds_bytes(int32_t num_seqs) { return (size_t)(num_seqs + 1) * sizeof(int32_t); }
+size_t prefill_lds_bytes(int32_t num_seqs, int32_t lpt_buckets) {
+    return (size_t)(num_seqs + 3 + lpt_buckets) * sizeof(int32_t);
+}
 
 hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream) {
     if (p.num_seqs == 0 || p.tile_bound == 0) return hipSuccess;
     const dim3 grid((unsigned)((int64_t)p.tile_bound * p.num_kv_heads));
     if (!p.kv_fp8) return launch_prefill_wide(p, stream);
     const dim3 block(64 * Fp8Shape::kWaves);
-    const size_t lds = prefill_lds_bytes(p.num_seqs);
+    const size_t lds = prefill_lds_bytes(p.num_seqs, p.lpt_buckets);
     if (p.head_dim == 128) hipLaunchKernelGGL((prefill_fp8_kernel<128>), grid, block, lds, stream, p);
     else hipLaunchKernelGGL((prefill_fp8_kernel<64>), grid, block, lds, stream, p);
     return hipGetLastError();

@@ -108,7 +108,7 @@ __global__ __launch_bounds__(512) void prefill_wide_kernel(PrefillParams p) {
     constexpr int kP = WS::kPairs;
     constexpr int kKC = WS::kKC, kDT = WS::kDT, kStepLoads = WS::kStepLoads;
     constexpr int kKeysPerStep = 2 * kP * kBlockSize;  // 64
-    extern __shared__ int32_t t_off[];  // [B + 1] first workgroup tile of each request
+    extern __shared__ int32_t plan[];  // tile order (see locate_rows)
     __shared__ int32_t wave_total[kWaves];
     // slot layout: K chunks of pair 0, of pair 1, then V chunks of pair 0, of pair 1
     __shared__ uint4 slot0[WS::kSlotChunks], slot1[WS::kSlotChunks], slot2[WS::kSlotChunks];
@@ -118,7 +118,7 @@ __global__ __launch_bounds__(512) void prefill_wide_kernel(PrefillParams p) {
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     WaveRows wr;
-    if (!locate_rows<kWaves, kRowsPerWave>(p, t_off, wave_total, wr)) return;  // the whole workgroup
+    if (!locate_rows<kWaves, kRowsPerWave>(p, plan, wave_total, wr)) return;  // the whole workgroup
     const int s = wr.s, r0 = wr.r0, nq = wr.n, rows = wr.rows, R0 = wr.R0, L = wr.L, kvh = wr.kvh;
     const int G = p.group;
     const bool has_rows = R0 < rows;
@@ -193,42 +193,48 @@ __global__ __launch_bounds__(512) void prefill_wide_kernel(PrefillParams p) {
         }
         // the step's blocks -> one ring slot
         auto dma_step = [&](uint4* dst, const int (&pb)[2 * kP]) __attribute__((always_inline)) {
+            static_assert(kP == 2, "four blocks per step");
+            int64_t off[2 * kP];  // element offset of each block
+#pragma unroll
+            for (int b = 0; b < 2 * kP; ++b) off[b] = (int64_t)pb[b] * block_stride;
 #pragma unroll
             for (int j = 0; j < kStepLoads; ++j) {
-                // the block by a uniform two-level choice (an indexed pb, which
-                // a chain of selects becomes, would go to scratch memory)
-                static_assert(kP == 2, "four blocks per step");
+                // the block by a uniform two-level choice (an indexed array,
+                // which a chain of selects becomes, would go to scratch memory)
                 const int sel = ld_blk[j];
-                const int lo = (sel & 1) ? pb[1] : pb[0];
-                const int hi = (sel & 1) ? pb[3] : pb[2];
-                const int blk = __builtin_amdgcn_readfirstlane((sel & 2) ? hi : lo);
-                const uint16_t* base = (ld_v[j] ? v_head : k_head) + (int64_t)blk * block_stride;
+                const int64_t lo = (sel & 1) ? off[1] : off[0];
+                const int64_t hi = (sel & 1) ? off[3] : off[2];
+                const uint16_t* base = (ld_v[j] ? v_head : k_head) + ((sel & 2) ? hi : lo);
                 const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
                     const_cast<uint16_t*>(base), (short)0, WS::kBlockChunks * 16, 0x00020000);
                 buffer_load_lds16(rs, (lds_void_ptr)(dst + WS::kThreads * j + 64 * wave), ld_off[j]);
             }
         };
 
+        const uint32_t nb_u32 = (uint32_t)min(p.num_blocks, (int64_t)0x7fffffff);  // entries are int32
         uint32_t okm = 0;  // bit 4(u mod 4) + b: block b of step u lies inside the pool (and the walk)
-        int pend[2 * kP];
-        int pend_u = 0;
-        auto fetch = [&](int u) __attribute__((always_inline)) {
-            pend_u = min(u, NU - 1);  // past the end: the last step's blocks again (loaded, never used)
+        struct Pending {
+            int e[2 * kP];  // table entries as read (checked when accepted)
+            int u;          // their step
+        };
+        auto fetch = [&](Pending& pd, int u) __attribute__((always_inline)) {
+            pd.u = min(u, NU - 1);  // past the end: the last step's blocks again (loaded, never used)
 #pragma unroll
-            for (int b = 0; b < 2 * kP; ++b) pend[b] = bt[min(2 * kP * pend_u + b, nblk - 1)];
+            for (int b = 0; b < 2 * kP; ++b) pd.e[b] = bt[min(2 * kP * pd.u + b, nblk - 1)];
         };
         // checked entries -> physical blocks (an id outside the pool loads
         // block 0); the empty asm pins the wait for the scalar loads here
-        auto accept = [&](int (&pb)[2 * kP]) __attribute__((always_inline)) {
+        auto accept = [&](const Pending& pd, int (&pb)[2 * kP]) __attribute__((always_inline)) {
             uint32_t bits = 0;
 #pragma unroll
             for (int b = 0; b < 2 * kP; ++b) {
-                const bool ok = (pend[b] >= 0) & ((int64_t)pend[b] < p.num_blocks) & (2 * kP * pend_u + b < nblk);
-                pb[b] = ok ? pend[b] : 0;
+                // 0 <= entry < pool size, as one unsigned compare
+                const bool ok = ((uint32_t)pd.e[b] < nb_u32) & (2 * kP * pd.u + b < nblk);
+                pb[b] = ok ? pd.e[b] : 0;
                 bits |= (uint32_t)ok << b;
                 asm volatile("" : "+s"(pb[b]));
             }
-            const int sh = 2 * kP * (pend_u & 3);
+            const int sh = 2 * kP * (pd.u & 3);
             okm = (okm & ~(((1u << (2 * kP)) - 1) << sh)) | (bits << sh);
         };
         // valid tokens of block b (0 .. 2 kP - 1) of step u
@@ -236,20 +242,25 @@ __global__ __launch_bounds__(512) void prefill_wide_kernel(PrefillParams p) {
             return ((okm >> (2 * kP * (u & 3) + b)) & 1u) ? min(kBlockSize, L - (2 * kP * u + b) * kBlockSize) : 0;
         };
 
-        // prologue: steps 0 and 1
+        // prologue: the entries of steps 0, 1 and 2 read together, the
+        // loads of steps 0 and 1.  Later steps read the entries of step
+        // u + 3 after their last LDS read, so the scalar reads land during
+        // the next barrier (see below).
+        Pending pend;
         {
+            Pending p0, p1;
+            fetch(p0, 0);
+            fetch(p1, 1);
+            fetch(pend, 2);
             int pb[2 * kP];
-            fetch(0);
-            accept(pb);
+            accept(p0, pb);
             __builtin_amdgcn_sched_barrier(0);
             dma_step(slot0, pb);
             __builtin_amdgcn_sched_barrier(0);
-            fetch(1);
-            accept(pb);
+            accept(p1, pb);
             __builtin_amdgcn_sched_barrier(0);
             dma_step(slot1, pb);
             __builtin_amdgcn_sched_barrier(0);
-            fetch(2);
         }
 
         if (has_rows) {
@@ -273,14 +284,14 @@ __global__ __launch_bounds__(512) void prefill_wide_kernel(PrefillParams p) {
                 __builtin_amdgcn_sched_barrier(0);
                 {
                     int pb[2 * kP];
-                    accept(pb);  // step u + 2
-                    fetch(u + 3);
+                    accept(pend, pb);  // step u + 2
                     dma_step(dst, pb);
                 }
-                // The table reads land before the operand reads start: scalar
+                // No scalar read may be out during the operand reads: scalar
                 // and LDS reads share one counter, and while a scalar read is
                 // out (they may return out of order) every LDS wait is a wait
-                // for all of them.
+                // for all of them.  (The entries of step u + 3 are read after
+                // this step's last LDS read.)
                 __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
                 __builtin_amdgcn_sched_barrier(0);
 
@@ -392,6 +403,8 @@ __global__ __launch_bounds__(512) void prefill_wide_kernel(PrefillParams p) {
                         __builtin_amdgcn_sched_group_barrier(0x8, kDT, 0);
                     }
                 }
+                __builtin_amdgcn_sched_barrier(0);
+                fetch(pend, u + 3);
             };
 
             // Steps [0, NUf) see only keys visible to every row of the wave,
@@ -419,10 +432,10 @@ __global__ __launch_bounds__(512) void prefill_wide_kernel(PrefillParams p) {
                 __builtin_amdgcn_s_barrier();
                 __builtin_amdgcn_sched_barrier(0);
                 int pb[2 * kP];
-                accept(pb);  // step u + 2
-                fetch(u + 3);
+                accept(pend, pb);  // step u + 2
                 dma_step(slot_dyn((u + 2) % 3), pb);
                 __builtin_amdgcn_sched_barrier(0);
+                fetch(pend, u + 3);
             }
         }
         wait_vmcnt<0>();  // no load into LDS outlives the workgroup
@@ -456,7 +469,7 @@ __global__ __launch_bounds__(512) void prefill_wide_kernel(PrefillParams p) {
 hipError_t launch_prefill_wide(const PrefillParams& p, hipStream_t stream) {
     if (p.num_seqs == 0 || p.tile_bound == 0) return hipSuccess;
     const dim3 grid((unsigned)((int64_t)p.tile_bound * p.num_kv_heads));
-    const size_t lds = prefill_lds_bytes(p.num_seqs);
+    const size_t lds = prefill_lds_bytes(p.num_seqs, p.lpt_buckets);
     if (p.head_dim == 128) hipLaunchKernelGGL((prefill_wide_kernel<128>), grid, dim3(512), lds, stream, p);
     else hipLaunchKernelGGL((prefill_wide_kernel<64>), grid, dim3(512), lds, stream, p);
     return hipGetLastError();
