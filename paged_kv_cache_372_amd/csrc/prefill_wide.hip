@@ -94,9 +94,10 @@ struct WideShape {
     static constexpr int kVChunks = 2 * kDT * 64;    // 16-byte V operand chunks per pair
     static constexpr int kBlockChunks = D * kBlockSize * 2 / 16;        // 16-byte chunks of one K or V block
     static constexpr int kSlotChunks = kPairs * (kKChunks + kVChunks);  // one ring slot: K of both pairs, then V
-    static constexpr int kStepLoads = kSlotChunks / kThreads;            // direct-to-LDS loads per thread per step
-    static_assert(kSlotChunks % kThreads == 0 && kBlockChunks % 64 == 0 && kKChunks == 2 * kBlockChunks,
-                  "whole loads per thread; each wave's load within one block");
+    static constexpr int kStepLoads = kBlockChunks / 64;                 // direct-to-LDS loads per thread per step
+    // each wave loads one block of K or of V per step
+    static_assert(kThreads / 64 == 2 * 2 * kPairs && kKChunks == 2 * kBlockChunks && kVChunks == 2 * kBlockChunks,
+                  "one wave per block and kind");
 };
 
 template <int D>
@@ -112,7 +113,6 @@ __global__ __launch_bounds__(512) void prefill_wide_kernel(PrefillParams p) {
     __shared__ int32_t wave_total[kWaves];
     // slot layout: K chunks of pair 0, of pair 1, then V chunks of pair 0, of pair 1
     __shared__ uint4 slot0[WS::kSlotChunks], slot1[WS::kSlotChunks], slot2[WS::kSlotChunks];
-    auto slot_dyn = [&](int q) -> uint4* { return q == 0 ? slot0 : q == 1 ? slot1 : slot2; };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -172,43 +172,37 @@ __global__ __launch_bounds__(512) void prefill_wide_kernel(PrefillParams p) {
         const uint16_t* k_head = reinterpret_cast<const uint16_t*>(p.k_cache) + (int64_t)kvh * D * kBlockSize;
         const uint16_t* v_head = reinterpret_cast<const uint16_t*>(p.v_cache) + (int64_t)kvh * D * kBlockSize;
         const scalar_i32_ptr bt = (scalar_i32_ptr)(p.block_tables + (int64_t)s * p.max_blocks_per_seq);
-        // This thread's loads: chunk q = 512j + tid of a slot; each wave's 64
-        // chunks of one load lie in one block (kBlockChunks is a multiple of
-        // 64).  K chunk q of a pair: block q / kBlockChunks, copied in place.
-        // V chunk q: block q / (64 D/32), tile (q / 64) mod D/32, lane
-        // (n', h'): dim 32t + n', tokens 8h' .. +7.
-        int ld_off[kStepLoads];  // this lane's byte offset within its block
-        int ld_blk[kStepLoads];  // block of the step, 0 .. 2 kP - 1 (uniform in the wave)
-        bool ld_v[kStepLoads];   // a V chunk (uniform in the wave)
+        // This wave's loads: wave w copies block (w mod 4) of the step (pair
+        // (w mod 4) / 2, block A or B of it), K for w < 4, V otherwise, in
+        // kStepLoads loads of 64 chunks.  K is copied as the pool lays it
+        // out; V chunk 64t + lane' (lane' = 32h' + n') is dim 32t + n',
+        // tokens 8h' .. +7.
+        const bool ld_v = wave >= 4;
+        const int ld_blk = wave & 3;
+        const uint16_t* const ld_head = ld_v ? v_head : k_head;
+        const int ld_at = (ld_v ? kP * WS::kKChunks : 0) + ld_blk * WS::kBlockChunks;  // its chunks in a slot
+        int ld_off[kStepLoads];  // this lane's byte offset within the block, per load
 #pragma unroll
-        for (int j = 0; j < kStepLoads; ++j) {
-            const int q = WS::kThreads * j + tid;
-            ld_v[j] = __builtin_amdgcn_readfirstlane(q >= kP * WS::kKChunks);  // uniform: a wave's 64 chunks
-            const int qv_ = ld_v[j] ? q - kP * WS::kKChunks : q;
-            const int per = ld_v[j] ? WS::kVChunks : WS::kKChunks;
-            const int a = qv_ / per, qq = qv_ - a * per, ln = qq & 63;
-            const int b = qq / WS::kBlockChunks;
-            ld_blk[j] = __builtin_amdgcn_readfirstlane(2 * a + b);
-            ld_off[j] = 16 * (ld_v[j] ? (32 * ((qq >> 6) % kDT) + (ln & 31)) * 2 + (ln >> 5) : qq - b * WS::kBlockChunks);
-        }
-        // the step's blocks -> one ring slot
-        auto dma_step = [&](uint4* dst, const int (&pb)[2 * kP]) __attribute__((always_inline)) {
+        for (int j = 0; j < kStepLoads; ++j)
+            ld_off[j] = 16 * (ld_v ? (32 * j + (lane & 31)) * 2 + (lane >> 5) : 64 * j + lane);
+        // the step's blocks -> the descriptor of this wave's block (scalar
+        // work), then its loads into one ring slot
+        auto dma_prepare = [&](const int (&pb)[2 * kP]) __attribute__((always_inline)) {
             static_assert(kP == 2, "four blocks per step");
-            int64_t off[2 * kP];  // element offset of each block
+            // this wave's block by a uniform two-level choice (an indexed
+            // array, which a chain of selects becomes, would go to scratch)
+            const int lo = (ld_blk & 1) ? pb[1] : pb[0];
+            const int hi = (ld_blk & 1) ? pb[3] : pb[2];
+            const int blk = (ld_blk & 2) ? hi : lo;
+            return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(ld_head + (int64_t)blk * block_stride),
+                                                     (short)0, WS::kBlockChunks * 16, 0x00020000);
+        };
+        // slot q is a constant: each slot is an LDS array of its own
+        auto dma_issue = [&](auto q_tag, __amdgpu_buffer_rsrc_t rs) __attribute__((always_inline)) {
+            constexpr int q = decltype(q_tag)::value;
+            uint4* const dst = (q == 0 ? slot0 : q == 1 ? slot1 : slot2) + ld_at;
 #pragma unroll
-            for (int b = 0; b < 2 * kP; ++b) off[b] = (int64_t)pb[b] * block_stride;
-#pragma unroll
-            for (int j = 0; j < kStepLoads; ++j) {
-                // the block by a uniform two-level choice (an indexed array,
-                // which a chain of selects becomes, would go to scratch memory)
-                const int sel = ld_blk[j];
-                const int64_t lo = (sel & 1) ? off[1] : off[0];
-                const int64_t hi = (sel & 1) ? off[3] : off[2];
-                const uint16_t* base = (ld_v[j] ? v_head : k_head) + ((sel & 2) ? hi : lo);
-                const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-                    const_cast<uint16_t*>(base), (short)0, WS::kBlockChunks * 16, 0x00020000);
-                buffer_load_lds16(rs, (lds_void_ptr)(dst + WS::kThreads * j + 64 * wave), ld_off[j]);
-            }
+            for (int j = 0; j < kStepLoads; ++j) buffer_load_lds16(rs, (lds_void_ptr)(dst + 64 * j), ld_off[j]);
         };
 
         const uint32_t nb_u32 = (uint32_t)min(p.num_blocks, (int64_t)0x7fffffff);  // entries are int32
@@ -255,11 +249,11 @@ __global__ __launch_bounds__(512) void prefill_wide_kernel(PrefillParams p) {
             int pb[2 * kP];
             accept(p0, pb);
             __builtin_amdgcn_sched_barrier(0);
-            dma_step(slot0, pb);
+            dma_issue(std::integral_constant<int, 0>{}, dma_prepare(pb));
             __builtin_amdgcn_sched_barrier(0);
             accept(p1, pb);
             __builtin_amdgcn_sched_barrier(0);
-            dma_step(slot1, pb);
+            dma_issue(std::integral_constant<int, 1>{}, dma_prepare(pb));
             __builtin_amdgcn_sched_barrier(0);
         }
 
@@ -276,16 +270,18 @@ __global__ __launch_bounds__(512) void prefill_wide_kernel(PrefillParams p) {
             auto step = [&](int u, auto masked_tag, auto q_tag) __attribute__((always_inline)) {
                 constexpr bool kMasked = decltype(masked_tag)::value;
                 constexpr int kQ = decltype(q_tag)::value;  // u mod 3
-                uint4* const dst = kQ == 0 ? slot2 : kQ == 1 ? slot0 : slot1;        // step u + 2
                 const uint4* const src = kQ == 0 ? slot0 : kQ == 1 ? slot1 : slot2;  // step u
                 // every load but those of step u - 1 has landed, in every wave
                 wait_vmcnt<kStepLoads>();
                 __builtin_amdgcn_s_barrier();
                 __builtin_amdgcn_sched_barrier(0);
+                // the loads of step u + 2 (into the slot step u - 1 read) go out
+                // under the QK products below
+                __amdgpu_buffer_rsrc_t rs;
                 {
                     int pb[2 * kP];
                     accept(pend, pb);  // step u + 2
-                    dma_step(dst, pb);
+                    rs = dma_prepare(pb);
                 }
                 // No scalar read may be out during the operand reads: scalar
                 // and LDS reads share one counter, and while a scalar read is
@@ -296,6 +292,7 @@ __global__ __launch_bounds__(512) void prefill_wide_kernel(PrefillParams p) {
                 __builtin_amdgcn_sched_barrier(0);
 
                 // ---- QK: one chain of D/16 products per pair, interleaved
+                dma_issue(std::integral_constant<int, (kQ + 2) % 3>{}, rs);
                 float16v_t x[kP];
 #pragma unroll
                 for (int a = 0; a < kP; ++a)
@@ -307,12 +304,14 @@ __global__ __launch_bounds__(512) void prefill_wide_kernel(PrefillParams p) {
                     for (int a = 0; a < kP; ++a)
                         x[a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                             __builtin_bit_cast(bf16x8_t, src[a * WS::kKChunks + 32 * c + k_lane]), qv[c], x[a], 0, 0, 0);
-                // K reads run two products ahead (LDS latency is some 100 cycles)
+                // K reads run two products ahead (LDS latency is some 100
+                // cycles); the step's loads go out one per product pair
                 __builtin_amdgcn_sched_group_barrier(0x100, 2 * kP, 0);
 #pragma unroll
                 for (int c = 0; c < kKC; ++c) {
                     __builtin_amdgcn_sched_group_barrier(0x8, kP, 0);
                     if (c + 2 < kKC) __builtin_amdgcn_sched_group_barrier(0x100, kP, 0);
+                    if (c < kStepLoads) __builtin_amdgcn_sched_group_barrier(0x20, 1, 0);
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 // V operands of the first block: read now, used after the softmax
@@ -433,7 +432,11 @@ __global__ __launch_bounds__(512) void prefill_wide_kernel(PrefillParams p) {
                 __builtin_amdgcn_sched_barrier(0);
                 int pb[2 * kP];
                 accept(pend, pb);  // step u + 2
-                dma_step(slot_dyn((u + 2) % 3), pb);
+                const __amdgpu_buffer_rsrc_t rs = dma_prepare(pb);
+                const int q = (u + 2) % 3;
+                if (q == 0) dma_issue(std::integral_constant<int, 0>{}, rs);
+                else if (q == 1) dma_issue(std::integral_constant<int, 1>{}, rs);
+                else dma_issue(std::integral_constant<int, 2>{}, rs);
                 __builtin_amdgcn_sched_barrier(0);
                 fetch(pend, u + 3);
             }
