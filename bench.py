@@ -709,6 +709,64 @@ def run_hbm_read(args):
     print(json.dumps(rec), flush=True)
 
 
+ISSUE_RATE_METRIC = "instruction issue rates: matrix-core TFLOP/s, vector ALU cycles per instruction, LDS bytes per cycle"
+
+
+def run_issue_rates(args):
+    """Issue-rate microbenchmark (library aid pkv_issue_rate_bench): each
+    pattern with one and with two waves per SIMD, one workgroup per compute
+    unit, timed by HIP events on the launching stream.  Cycles are at the
+    nominal 2.4 GHz.  The headline is mfma_f32_32x32x16_bf16 into four
+    accumulators, one wave per SIMD."""
+    import torch
+    from paged_kv_cache_372_amd import ops
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.zeros(512, dtype=torch.int32, device="cuda")
+    iters = {0: 4000, 1: 4000, 2: 2000, 3: 2000, 4: 20000, 5: 10000, 6: 10000}
+    flops = {0: 16384, 1: 16384, 2: 32768, 3: 32768}
+    clk = 2.4e9
+    cases = {}
+    for wps in (1, 2):
+        for pat, name in enumerate(ops.ISSUE_RATE_PATTERNS):
+            n = iters[pat]
+            for _ in range(max(1, args.warmup // 10)):
+                ops.issue_rate_bench(pat, wps, max(1, n // 10), sink)
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(3)]
+            for e in ev:
+                e[0].record()
+                ops.issue_rate_bench(pat, wps, n, sink)
+                e[1].record()
+            torch.cuda.synchronize()
+            ms = min(e[0].elapsed_time(e[1]) for e in ev)
+            waves = cus * 4 * wps
+            insts = waves * n * 16  # per pattern instruction (EXP: each v_exp_f32 with its v_add_f32)
+            key = f"{name}_wps{wps}"
+            rec = {"case": key, "ms": round(ms, 4), "instructions": insts}
+            if pat in flops:
+                rec["tflops"] = round(insts * flops[pat] / (ms / 1e3) / 1e12, 1)
+                rec["frac_of_bf16_peak"] = round(rec["tflops"] / PEAK_BF16_TFLOPS, 4)
+            elif pat in (4, 5):
+                # one SIMD's instructions per cycle, all its waves together
+                per_simd = insts / (cus * 4)
+                rec["cycles_per_instruction_per_simd"] = round((ms / 1e3) * clk / per_simd, 2)
+            else:
+                nbytes = insts * 64 * 16
+                rec["lds_bytes_per_cycle_per_cu"] = round(nbytes / (ms / 1e3) / clk / cus, 1)
+            cases[key] = rec
+            print(json.dumps(rec), flush=True)
+    head = cases["mfma_32x32x16_bf16_4acc_wps1"]
+    out = {"metric": ISSUE_RATE_METRIC, "value": head["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": 3,
+           "warmup": args.warmup, "ms_per_step": head["ms"], "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "issue_rates", "compute_units": cus, "grid": "one workgroup per CU",
+                      "instructions_per_wave_and_iteration": 16},
+           "frac_of_peak": head["frac_of_bf16_peak"],
+           "roofline": {"bound": "mfma", "achieved": head["tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": head["frac_of_bf16_peak"], "traffic": None, "kernel": "rate_mfma32"},
+           "cases": cases}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -780,6 +838,9 @@ def main():
 
     if args.config == "hbm_read":
         run_hbm_read(args)
+        return
+    if args.config == "issue_rates":
+        run_issue_rates(args)
         return
     if family(args.config) == "prefill":
         run_prefill(args)

@@ -442,6 +442,31 @@ pkv_status pkv_hbm_read_bench(const void* src, int64_t bytes, const int32_t* til
                               int32_t tile_bytes, int32_t streaming, uint32_t* sink, void* stream);
 
 /*
+ * Measurement aid: issue rates of the instructions the chunked-prefill
+ * kernels are built from (prefill is the compute-heavy stage, runbyai
+ * section 1).  One launch, one workgroup per compute unit of
+ * 256 x waves_per_simd threads (one or two waves per SIMD); each wave runs
+ * `iters` iterations of 16 instructions of one pattern:
+ *   0, 1  mfma_f32_16x16x32_bf16 into 1 accumulator (one dependent chain) or 4
+ *   2, 3  mfma_f32_32x32x16_bf16, likewise
+ *   4     v_fma_f32, 16 independent chains
+ *   5     v_exp_f32 each followed by a v_add_f32, 16 chains
+ *   6     16-byte LDS reads, consecutive lanes on consecutive 16 bytes of a
+ *         64 KiB array, one XOR each
+ * Time it with events around the call on `stream`; the instruction counts
+ * follow from the pattern, the number of compute units and the arguments.
+ *   pattern          0 .. 6
+ *   waves_per_simd   1 or 2
+ *   iters            1 .. 10^7
+ *   sink             device memory, at least 512 uint32 (written only in a
+ *                    branch that is never taken)
+ * Errors: PKV_ERR_INVALID_ARG for any argument out of range or a null sink.
+ * Asynchronous on `stream`.
+ */
+pkv_status pkv_issue_rate_bench(int32_t pattern, int32_t waves_per_simd, int32_t iters, uint32_t* sink,
+                                void* stream);
+
+/*
  * Measurement aid: decode over a bf16 cache with every product on the vector
  * ALU instead of the matrix cores, to weigh the two for this bandwidth-bound
  * step (runbyai section 1).  Same result as pkv_paged_attention_decode within

@@ -137,6 +137,11 @@ hipError_t launch_cache_write_fp8(const void* k_new, const void* v_new, const in
                                   void* v_cache, const float* k_scale, const float* v_scale, int64_t num_tokens,
                                   int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks, bool src_bf16,
                                   hipStream_t stream);
+// Issue-rate microbenchmark (issue_rates.hip): pattern 0..6 as
+// pkv_issue_rate_bench; one workgroup of 256 x waves_per_simd threads per CU.
+hipError_t launch_issue_rate(int32_t pattern, int32_t waves_per_simd, int32_t iters, uint32_t* sink,
+                             hipStream_t stream);
+
 hipError_t launch_hbm_read(const void* src, int64_t bytes, const int32_t* tiles, int64_t num_tiles,
                            int32_t tile_bytes, bool streaming, uint32_t* sink, hipStream_t stream);
 hipError_t launch_cache_write(const void* k_new, const void* v_new, const int64_t* slot_mapping,

@@ -791,6 +791,17 @@ pkv_status pkv_hbm_read_bench(const void* src, int64_t bytes, const int32_t* til
                     "hbm_read launch");
 }
 
+pkv_status pkv_issue_rate_bench(int32_t pattern, int32_t waves_per_simd, int32_t iters, uint32_t* sink,
+                                void* stream) {
+    g_last_error[0] = 0;
+    if (pattern < 0 || pattern > 6) return fail(PKV_ERR_INVALID_ARG, "pattern must be 0 .. 6");
+    if (waves_per_simd < 1 || waves_per_simd > 2) return fail(PKV_ERR_INVALID_ARG, "waves_per_simd must be 1 or 2");
+    if (iters < 1 || iters > 10000000) return fail(PKV_ERR_INVALID_ARG, "iters must be 1 .. 10^7");
+    if (!sink) return fail(PKV_ERR_INVALID_ARG, "null sink");
+    return from_hip(pkv::launch_issue_rate(pattern, waves_per_simd, iters, sink, static_cast<hipStream_t>(stream)),
+                    "issue_rate launch");
+}
+
 pkv_status pkv_paged_attention_decode_vector_alu(const void* q, const void* k_cache, const void* v_cache,
                                                  const int32_t* block_tables, const int32_t* context_lens,
                                                  float scale, void* out, int32_t num_seqs, int32_t num_q_heads,

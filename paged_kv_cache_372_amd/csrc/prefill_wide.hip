@@ -4,11 +4,12 @@
 // attention of each request's n_s new query tokens over its L_s cached
 // tokens, aligned at the end of the context, the keys reached through the
 // request's block table (architvora "Paged Attention"; runbyai section 1).
+// Workgroups take their tiles heaviest first (locate_rows).
 //
-// Matrix shape.  mfma_f32_32x32x16_bf16 issued back to back runs near the
-// matrix cores' peak, where mfma_f32_16x16x32_bf16 from one wave per SIMD
-// reaches about a third of it.  A wave owns one 32-row tile.  Per pair of
-// blocks (A, B) = 32 keys:
+// Matrix shape.  A wave owns one 32-row tile and uses mfma_f32_32x32x16_bf16,
+// whose operands carry twice the products per byte of the 16 x 16 shape (both
+// shapes issue at close to the matrix cores' peak: pkv_issue_rate_bench).
+// Per pair of blocks (A, B) = 32 keys:
 //   S^T[32 keys x 32 rows] = K . Q^T            D/16 x mfma_f32_32x32x16_bf16
 //   O^T[32 dims x 32 rows] += V^T . P^T          per 32-dim tile: 2 (blocks)
 // Operands of mfma_f32_32x32x16_bf16, lane l = 32h + n: A holds row n,
@@ -21,28 +22,28 @@
 // is one 16-byte run of the pool's [dim][16 tokens] V block.
 //
 // Two waves per SIMD.  Eight waves of 32 rows (256 per workgroup) fit the
-// register file twice over, and a SIMD's second wave hides the first one's
-// softmax: one wave issues a VALU instruction about every eighth cycle, two
-// waves every fourth (measured), and one wave's products run while the
-// other computes its weights.  A step takes two pairs (64 keys): the wave
-// runs their QK products as two independent chains, the mask, maxima and
-// weights over 64 keys, then their PV products.
+// register file twice over.  One wave alone issues a VALU instruction about
+// every seventh cycle, two waves every fourth (pkv_issue_rate_bench), and
+// the softmax is some 140 VALU instructions per wave and step: the second
+// wave of a SIMD keeps its VALU and matrix cores fed while the first waits.
+// A step takes two pairs (64 keys): the wave runs their QK products as two
+// independent chains, the mask, maxima and weights over 64 keys, then their
+// PV products.
 //
-// Staging.  The workgroup loads each pair once, with direct-to-LDS buffer
-// loads, each of which reads one KV block (its descriptor is that block).
-// A K block is copied as it lies in the pool ([D/8][16 tokens][8 dims]): a
-// QK operand then reads, per 16 lanes, 256 consecutive bytes, in the token
-// order the product wants.  V is loaded in operand order (lane l of load
-// (b, t) fetches dim 32t + l % 32, tokens 8(l / 32) .. +7 of block b): a PV
-// operand is 1 KiB of consecutive LDS.  Both are read without bank
-// conflicts.  (The buffer form, unlike the flat one, leaves the compiler
-// counting LDS reads precisely: a flat load into LDS makes it wait for all
-// of them.)  K and V
-// share a ring of three slots of two pairs each, one LDS array per slot
-// (distinct objects, so the compiler knows which slot a read touches and
-// adds no waits of its own).  Step u, one barrier: every load but those of
-// step u - 1 has landed; the workgroup loads the pairs of step u + 2 into
-// the slot step u - 1 read, while its waves work on step u's.  The waits
+// Staging.  The workgroup loads each block once, with direct-to-LDS buffer
+// loads: wave w copies block w mod 4 of the step, K for w < 4 and V for the
+// others, from one descriptor (the block).  A K block is copied as it lies
+// in the pool ([D/8][16 tokens][8 dims]): a QK operand then reads, per 16
+// lanes, 256 consecutive bytes, in the token order the product wants.  V is
+// loaded in operand order (lane l of load t fetches dim 32t + l % 32, tokens
+// 8(l / 32) .. +7): a PV operand is 1 KiB of consecutive LDS.  Both are read
+// without bank conflicts.  (The buffer form, unlike the flat one, leaves the
+// compiler counting LDS reads precisely: a flat load into LDS makes it wait
+// for all of them.)  K and V share a ring of three slots of two pairs each,
+// one LDS array per slot (distinct objects, so the compiler knows which slot
+// a read touches and adds no waits of its own).  Step u, one barrier: every
+// load but those of step u - 1 has landed; the loads of step u + 2 go into
+// the slot step u - 1 read, issued between step u's QK products.  The waits
 // are explicit vmcnt counts: loads return in issue order, and every thread
 // issues the same number of loads in every step.
 #include <type_traits>

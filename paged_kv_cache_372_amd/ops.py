@@ -64,6 +64,7 @@ _SIGNATURES = {
     "pkv_paged_attention_decode_vector_alu": (_i32, [_vp, _vp, _vp, _vp, _vp, _f32, _vp, _i32, _i32, _i32, _i32,
                                                      _i32, _i64, _i32, _i32, _i32, _vp, _sz, _i32, _vp]),
     "pkv_hbm_read_bench": (_i32, [_vp, _i64, _vp, _i64, _i32, _i32, _vp, _vp]),
+    "pkv_issue_rate_bench": (_i32, [_i32, _i32, _i32, _vp, _vp]),
     "pkv_status_string": (ctypes.c_char_p, [_i32]),
     "pkv_last_error": (ctypes.c_char_p, []),
 }
@@ -516,6 +517,22 @@ def hbm_read_bench(src: torch.Tensor, sink: torch.Tensor, tiles: Optional[torch.
                                 tiles.numel() if tiles is not None else 0, int(tile_bytes), 1 if streaming else 0,
                                 _ptr(sink), _stream(dev))
     _check(st, "hbm_read_bench")
+
+
+ISSUE_RATE_PATTERNS = ("mfma_16x16x32_bf16_1acc", "mfma_16x16x32_bf16_4acc", "mfma_32x32x16_bf16_1acc",
+                       "mfma_32x32x16_bf16_4acc", "v_fma_f32", "v_exp_f32+v_add_f32", "ds_read_b128")
+
+
+def issue_rate_bench(pattern: int, waves_per_simd: int, iters: int, sink: torch.Tensor) -> None:
+    """Measurement aid: one launch of ``iters`` x 16 instructions of pattern ``pattern``
+    (``ISSUE_RATE_PATTERNS``) per wave, one workgroup of 256 x ``waves_per_simd`` threads per
+    compute unit; ``sink`` is a device 32-bit tensor of at least 512 elements."""
+    lib = load_library()
+    dev = sink.device
+    _check_tensor(sink, "sink", dev)
+    _require(sink.dtype in (torch.int32, torch.uint32) and sink.numel() >= 512, "sink must be 32-bit [>= 512]")
+    _check(lib.pkv_issue_rate_bench(int(pattern), int(waves_per_simd), int(iters), _ptr(sink), _stream(dev)),
+           "issue_rate_bench")
 
 
 def paged_attention_decode_vector_alu(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

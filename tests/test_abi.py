@@ -182,6 +182,15 @@ def test_decode_noalloc_validation(lib):
     assert dec_noalloc(lib, B=0, q=None, kc=None, vc=None, bt=None, lens=None, out=None) == OK
 
 
+def test_issue_rate_bench_validation(lib):
+    sink = ctypes.c_void_p(FAKE)
+    assert lib.pkv_issue_rate_bench(7, 1, 10, sink, None) == INVALID      # no such pattern
+    assert lib.pkv_issue_rate_bench(-1, 1, 10, sink, None) == INVALID
+    assert lib.pkv_issue_rate_bench(0, 3, 10, sink, None) == INVALID      # one or two waves per SIMD
+    assert lib.pkv_issue_rate_bench(0, 1, 0, sink, None) == INVALID
+    assert lib.pkv_issue_rate_bench(0, 1, 10, None, None) == INVALID
+
+
 def test_hbm_read_bench_validation(lib):
     sink = FAKE
     assert lib.pkv_hbm_read_bench(FAKE, 0, None, 0, 4096, 1, sink, None) == INVALID
