@@ -68,8 +68,7 @@ def kernel_sources(workload: str):
     """Sources whose code decides the kernel's traffic: the kernel, the
     internal header, and (decode) the launch planning in the ABI layer."""
     if family(workload) == "prefill":
-        main = "prefill_mfma.hip" if workload.endswith("_fp8") else "prefill_wide.hip"
-        files = (main, "prefill_common.h", "kernels.h")
+        files = ("prefill_wide.hip", "prefill_common.h", "prefill.h", "kernels.h")
     else:
         main = "copy_blocks.hip" if family(workload) == "copy" else "decode_mfma.hip"
         files = (main, "kernels.h", "pagedkv_abi.hip") if family(workload) == "decode" else (main, "kernels.h")
@@ -255,8 +254,7 @@ def calibrate_copy(mib: int, reps: int):
 
 
 DECODE_KERNEL_PREFIX = "void pkv::(anonymous namespace)::decode_bf16_balanced_kernel"
-PREFILL_KERNEL_PREFIX = {False: "void pkv::(anonymous namespace)::prefill_wide_kernel",
-                         True: "void pkv::(anonymous namespace)::prefill_fp8_kernel"}
+PREFILL_KERNEL_PREFIX = "void pkv::(anonymous namespace)::prefill_wide_kernel"
 COPY_KERNEL_PREFIX = "pkv::(anonymous namespace)::copy_blocks_kernel"
 
 
@@ -296,7 +294,7 @@ def summarize_profile(prefix: str, workload: str, partition_size, copy_mib: int,
     copy_name = "__amd_rocclr_copyBuffer"
     f_factor = copy_kib / cal_f[copy_name]
     w_factor = copy_kib / cal_w[copy_name]
-    prefix_k = {"prefill": PREFILL_KERNEL_PREFIX[workload.endswith("_fp8")],
+    prefix_k = {"prefill": PREFILL_KERNEL_PREFIX,
                 "copy": COPY_KERNEL_PREFIX}.get(family(workload), DECODE_KERNEL_PREFIX)
     short_k = prefix_k.split("::")[-1]
     dec = [k for k in fetch if short_k in k][0]
@@ -455,7 +453,7 @@ def run_prefill(args):
         "prefill_kernel_ms": round(k_ms, 5),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "kernel": "prefill_fp8_kernel" if fp8 else "prefill_wide_kernel", "flops_per_launch": flops},
+                     "kernel": "prefill_wide_kernel", "flops_per_launch": flops},
         "input_generation_s": round(gen_s, 2),
     }
     if not args.no_cpu_baseline:

@@ -28,13 +28,12 @@ HIPCC_FLAGS = [
 ]
 
 
-# Extra flags per source.  The prefill kernel keeps four column tiles of
-# accumulators live; by default the compiler puts MFMA results in AGPRs and
-# moves them back and forth every iteration, which the first flag avoids.
-# Its scores are finite or -inf, never NaN: without NaN semantics the
-# compiler drops the quieting max(x, x) it puts before every fmaxf.
+# Extra flags per source.  The prefill kernel keeps its score and output
+# tiles in VGPRs (by default the compiler puts MFMA results in AGPRs and
+# copies them back for the softmax every step).  Its scores are finite or
+# -inf, never NaN: without NaN semantics the compiler drops the quieting
+# max(x, x) it puts before every fmaxf.
 FILE_FLAGS = {
-    "prefill_mfma.hip": ["-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form", "-Xarch_device", "-fno-honor-nans"],
     "prefill_wide.hip": ["-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form", "-Xarch_device", "-fno-honor-nans"],
 }
 

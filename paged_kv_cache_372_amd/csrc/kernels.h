@@ -87,42 +87,6 @@ inline int64_t decode_units(const DecodeParams& p) {
     return (int64_t)p.num_parts * p.num_seqs * p.n_head_groups * p.num_kv_heads;
 }
 
-// Everything one multi-token-query (chunked prefill) launch needs.
-struct PrefillParams {
-    const void* q;                  // [T][Hq][D] bf16, requests' rows packed
-    const void* k_cache;            // [NB][Hkv][D/8][16][8]
-    const void* v_cache;            // [NB][Hkv][D][16]
-    const int32_t* block_tables;    // [B][max_blocks_per_seq] (this launch's requests)
-    const int32_t* context_lens;    // [B]
-    const int32_t* query_start_loc; // [B + 1] absolute rows of q / out
-    void* out;                      // [T][Hq][D]
-    float scale_log2;
-    int32_t num_seqs;               // B of this launch
-    int32_t num_tokens;             // T of the whole call: rows are clamped to it
-    int32_t num_q_heads;
-    int32_t num_kv_heads;
-    int32_t group;                  // Hq / Hkv
-    int32_t head_dim;
-    int64_t num_blocks;
-    int32_t max_blocks_per_seq;
-    int32_t ctx_cap;
-    int32_t out_bf16;
-    int32_t tile_bound;             // workgroup tiles launched per KV head (>= the tiles needed)
-    int32_t kv_fp8;                 // 1: pools hold E4M3 codes ([NB][Hkv][D/16][16][16] and [NB][Hkv][D][16])
-    const float* k_scale;           // fp8: [Hkv] K dequantisation scale
-    const float* v_scale;           // fp8: [Hkv] V dequantisation scale
-    int32_t lpt_buckets;            // tile weight classes (tiles are taken heaviest first)
-    int32_t lpt_shift;              // a weight class is 2^lpt_shift keys
-};
-
-// Rows (query token x head of a KV group) one prefill workgroup covers.
-constexpr int kPrefillRowsPerGroup = 256;
-// LDS for a prefill workgroup's tile order: num_seqs + 3 + lpt_buckets ints
-constexpr int kPrefillPlanLdsBytes = 48 * 1024;
-
-size_t prefill_lds_bytes(int32_t num_seqs, int32_t lpt_buckets);
-hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream);
-
 // Balanced bf16 decode: dynamic LDS bytes and launch shape.
 size_t balanced_lds_bytes(int32_t num_seqs);
 const void* balanced_kernel(int32_t head_dim);

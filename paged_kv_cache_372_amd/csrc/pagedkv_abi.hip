@@ -10,6 +10,7 @@
 
 #include "../../include/pagedkv.h"
 #include "kernels.h"
+#include "prefill.h"
 
 namespace {
 
@@ -738,7 +739,7 @@ pkv_status prefill_impl(const void* q, const void* k_cache, const void* v_cache,
         p.lpt_shift = 6;
         while ((int64_t)(n + 3 + (p.ctx_cap >> p.lpt_shift) + 2) * 4 > pkv::kPrefillPlanLdsBytes) ++p.lpt_shift;
         p.lpt_buckets = (p.ctx_cap >> p.lpt_shift) + 2;
-        pkv_status rc = from_hip(pkv::launch_prefill_bf16(p, st), "prefill kernel launch");
+        pkv_status rc = from_hip(pkv::launch_prefill(p, st), "prefill kernel launch");
         if (rc != PKV_OK) return rc;
     }
     return PKV_OK;

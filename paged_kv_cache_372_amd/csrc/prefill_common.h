@@ -1,9 +1,9 @@
-// Pieces shared by the two chunked-prefill kernels (prefill_mfma.hip: 16 x 16
-// tiles, fp8 pools; prefill_wide.hip: 32 x 32 tiles staged in LDS, bf16
-// pools): how a workgroup finds its rows, and small numeric helpers.
+// Pieces of the chunked-prefill kernel (prefill_wide.hip) kept apart: how a
+// workgroup finds its tile and each wave its rows (heaviest tiles first), and
+// small numeric helpers.
 #pragma once
 
-#include "kernels.h"
+#include "prefill.h"
 
 namespace pkv {
 namespace {
@@ -19,6 +19,23 @@ typedef float float2_t __attribute__((ext_vector_type(2)));
 // two fp32 -> packed bf16 (round to nearest even), one instruction
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{a, b}, bf16x2_t));
+}
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+// two fp32 -> packed fp16 (round to nearest even)
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{a, b}, f16x2_t));
+}
+// E4M3 codes (bytes 2 kHigh and 2 kHigh + 1 of w) -> their exact values,
+// packed as two bf16 or two fp16: every E4M3 value (at most 448, at least
+// 2^-9 apart from zero, 4 significant bits) is exact in both
+template <bool kHigh>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHigh));
+}
+template <bool kHigh>
+__device__ __forceinline__ uint32_t e4m3x2_to_f16x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, kHigh));
 }
 __device__ __forceinline__ uint32_t tail_mask(int nv, int first) {
     // 16-bit lanes [first, first + 1] of a token run, kept when inside nv
@@ -211,9 +228,5 @@ __device__ __forceinline__ bool locate_rows(const PrefillParams& p, int32_t* lds
 }
 
 }  // namespace
-
-// The bf16-pool kernel (prefill_wide.hip); same grid and LDS table as
-// launch_prefill_bf16, which calls it.
-hipError_t launch_prefill_wide(const PrefillParams& p, hipStream_t stream);
 
 }  // namespace pkv
