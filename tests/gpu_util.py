@@ -16,6 +16,38 @@ TOL = {"f32": 1e-5, "bf16": 2e-2}
 REL_RMS = {"f32": 1e-6, "bf16": 1e-2}
 
 
+def prompt_run_slots(rng, NB: int) -> np.ndarray:
+    """Slots of a prompt-like cache write into NB blocks: runs of consecutive
+    slots of one block (the 16-byte V store path) mixed with every case that
+    must fall back to element stores, in an order that puts runs across the
+    16-token groups the cache write is cut into."""
+    blocks = [int(b) for b in rng.permutation(NB)]
+
+    def run_from(block_i, offset, n):   # n consecutive positions of a sequence laid over blocks
+        out, b, o = [], block_i, offset
+        for _ in range(n):
+            out.append(blocks[b] * 16 + o)
+            o += 1
+            if o == 16:
+                b, o = b + 1, 0
+        return out
+    segs = []
+    segs += run_from(0, 0, 40)           # block-aligned prompt of 40 tokens (ends mid-block)
+    segs += run_from(3, 3, 37)           # prompt starting at offset 3: runs straddle the aligned boundaries
+    segs += run_from(6, 0, 16)           # exactly one block
+    r = run_from(7, 0, 16)
+    r[5] = -1                            # a skipped slot inside a run
+    segs += r
+    r = run_from(8, 0, 16)
+    r[10] = NB * 16 + 2                  # a slot outside the pool inside a run
+    segs += r
+    segs += run_from(9, 0, 8)[::-1]      # consecutive slots in reverse order
+    segs += [blocks[10] * 16 + 4, blocks[11] * 16 + 9]   # single appended tokens
+    segs += run_from(12, 9, 23)          # a run from offset 9 across a block boundary
+    segs += run_from(15, 0, 13)          # the call ends inside a run
+    return np.asarray(segs, dtype=np.int64)
+
+
 def say(*a):
     print(*a, flush=True)
     sys.stdout.flush()

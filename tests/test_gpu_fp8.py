@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import workloads as W
-from gpu_util import compare, int_dev, oracle_decode_all, out_f64, say, to_dev
+from gpu_util import compare, int_dev, oracle_decode_all, out_f64, prompt_run_slots, say, to_dev
 from paged_kv_cache_372_amd import ops
 from paged_kv_cache_372_amd.blocks import tables_share_blocks
 
@@ -69,6 +69,37 @@ def test_fp8_cache_write_bit_exact(src, D):
     bad = np.argwhere(gk != rk)
     assert bad.size == 0, f"K codes differ at {bad[:5].tolist()}: gpu {gk[tuple(bad[0])]:#x} oracle {rk[tuple(bad[0])]:#x}"
     assert np.array_equal(gv, rv), "V codes differ"
+
+
+@pytest.mark.parametrize("src", ["bf16", "f32"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_fp8_cache_write_prompt_runs(src, D):
+    """Prompt-like writes into fp8 pools: a run that fills a 16-token V row
+    goes out as one 16-byte store of codes, the rest as single codes."""
+    rng = np.random.default_rng(500 + D)
+    NB, Hkv = 64, 2
+    slots = prompt_run_slots(rng, NB)
+    T = len(slots)
+    kp = rng.integers(0, 256, size=(NB, Hkv, D // 16, 16, 16), dtype=np.uint8)
+    vp = rng.integers(0, 256, size=(NB, Hkv, D, 16), dtype=np.uint8)
+    x = rng.standard_normal((2, T, Hkv, D)).astype(np.float32) * rng.choice([0.01, 1.0, 30.0], size=(2, T, 1, 1))
+    if src == "bf16":
+        xb = W.bf16_bits_rne(x)
+        dev_in = [to_dev(xb[i], "bf16") for i in range(2)]
+        host_in = xb
+    else:
+        dev_in = [f32(x[i]) for i in range(2)]
+        host_in = x
+    k_scale = np.array([0.37, 3.1], dtype=np.float32)
+    v_scale = np.array([0.011, 2.0], dtype=np.float32)
+    say(f"[fp8 cache write prompt runs src={src} D={D} T={T}]")
+    dk, dv = u8(kp), u8(vp)
+    ops.reshape_and_cache_fp8(dev_in[0], dev_in[1], int_dev(slots, np.int64), dk, dv, f32(k_scale), f32(v_scale))
+    torch.cuda.synchronize()
+    ref_slots = np.where(slots >= NB * 16, -1, slots)
+    rk, rv = oracle.ref_reshape_and_cache_fp8(host_in[0], host_in[1], ref_slots, kp, vp, k_scale, v_scale, src)
+    assert np.array_equal(dk.cpu().numpy(), rk), "K codes differ"
+    assert np.array_equal(dv.cpu().numpy(), rv), "V codes differ"
 
 
 def test_fp8_decoder_every_code():

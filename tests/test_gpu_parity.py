@@ -18,7 +18,7 @@ import torch
 
 import oracle
 import workloads as W
-from gpu_util import (DeviceBatch, compare, int_dev, oracle_decode_all, oracle_pools, out_f64, say, to_dev,
+from gpu_util import (DeviceBatch, prompt_run_slots, compare, int_dev, oracle_decode_all, oracle_pools, out_f64, say, to_dev,
                       to_host_bits)
 from paged_kv_cache_372_amd import ops
 from paged_kv_cache_372_amd.blocks import tables_share_blocks
@@ -91,29 +91,7 @@ def test_cache_write_prompt_runs(dtype, D):
     path) mixed with every case that must fall back to element stores."""
     rng = np.random.default_rng(300 + D)
     NB, Hkv = 64, 2
-    blocks = [int(b) for b in rng.permutation(NB)]
-    segs = []
-    def run_from(block_i, offset, n):   # n consecutive positions of a sequence laid over blocks
-        out, b, o = [], block_i, offset
-        for _ in range(n):
-            out.append(blocks[b] * 16 + o)
-            o += 1
-            if o == 16:
-                b, o = b + 1, 0
-        return out
-    segs += run_from(0, 0, 40)           # block-aligned prompt of 40 tokens (ends mid-block)
-    segs += run_from(3, 3, 37)           # prompt starting at offset 3: runs straddle the aligned boundaries
-    segs += run_from(6, 0, 16)           # exactly one block
-    r = run_from(7, 0, 16)
-    r[5] = -1                            # a skipped slot inside a run
-    segs += r
-    r = run_from(8, 0, 16)
-    r[10] = NB * 16 + 2                  # a slot outside the pool inside a run
-    segs += r
-    segs += run_from(9, 0, 8)[::-1]      # consecutive slots in reverse order
-    segs += [blocks[10] * 16 + 4, blocks[11] * 16 + 9]   # single appended tokens
-    segs += run_from(12, 0, 13)          # the call ends inside a run
-    slots = np.asarray(segs, dtype=np.int64)
+    slots = prompt_run_slots(rng, NB)
     T = len(slots)
     ks, vs = W.pool_shapes(NB, Hkv, D, 16, dtype)
     bits = np.uint32 if dtype == "f32" else np.uint16
