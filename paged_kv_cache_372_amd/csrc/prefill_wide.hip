@@ -180,9 +180,11 @@ __global__ __launch_bounds__(512) void prefill_wide_kernel(PrefillParams p) {
     }
     // Q^T operands, step c: dims 16c + 8h .. +7 of row n.  A negative scale
     // rides on q (negating bf16 is exact); the softmax uses c = |scale log2 e|
-    // (fp8: times K's scale).
+    // (fp8: times K's scale), kept at least 2^-126 so that c times a masked
+    // score (-inf) stays -inf: a zero scale then still gives weights of
+    // exactly 1 to every visible key.
     const float eff_scale = kFp8 ? p.scale_log2 * p.k_scale[kvh] : p.scale_log2;
-    const float c_scale = fabsf(eff_scale);
+    const float c_scale = fmaxf(fabsf(eff_scale), 0x1p-126f);
     const uint32_t qsign = eff_scale < 0.f ? 0x80008000u : 0u;
     bf16x8_t qv[kKC];
     const uint16_t* qb = reinterpret_cast<const uint16_t*>(p.q);
@@ -434,15 +436,16 @@ __global__ __launch_bounds__(512) void prefill_wide_kernel(PrefillParams p) {
                 __builtin_amdgcn_sched_barrier(0);
                 // ---- mask, maxima, new reference, weights
                 if constexpr (kMasked) {
+                    // block b's keys visible to this lane's row lie below
+                    // min(end of its valid tokens, qpos + 1); the others'
+                    // scores become -inf (unscaled: c > 0 keeps them -inf)
 #pragma unroll
                     for (int b = 0; b < 2 * kP; ++b) {
-                        const int nv = nv_of(u, b);
-                        const int kp0 = (2 * kP * u + b) * kBlockSize + 8 * h;  // key position of its register 0
+                        const int kb = (2 * kP * u + b) * kBlockSize;  // the block's first key position
+                        const int vis = min(kb + nv_of(u, b), qpos + 1) - kb - 8 * h;  // registers r < vis
 #pragma unroll
-                        for (int r = 0; r < 8; ++r) {
-                            const float e = x[b >> 1][8 * (b & 1) + r];
-                            x[b >> 1][8 * (b & 1) + r] = (8 * h + r < nv) && (kp0 + r <= qpos) ? e * c_scale : -INFINITY;
-                        }
+                        for (int r = 0; r < 8; ++r)
+                            x[b >> 1][8 * (b & 1) + r] = r < vis ? x[b >> 1][8 * (b & 1) + r] : -INFINITY;
                     }
                 }
                 float m16 = x[0][0];
@@ -450,8 +453,8 @@ __global__ __launch_bounds__(512) void prefill_wide_kernel(PrefillParams p) {
                 for (int a = 0; a < kP; ++a)
 #pragma unroll
                     for (int r = (a == 0 ? 1 : 0); r < 16; ++r) m16 = fmaxf(m16, x[a][r]);
-                // unmasked: every score is live and c >= 0, so scale the max only
-                const float mx = kMasked ? max_halves(m16) : max_halves(m16) * c_scale;
+                // c > 0: scale the max only
+                const float mx = max_halves(m16) * c_scale;
                 const bool raise = mx > m_ref + kSlack;
                 const float alpha = raise ? exp2_fast(m_ref - mx) : 1.f;  // m_ref = -inf -> 0
                 m_ref = raise ? mx : m_ref;
@@ -467,7 +470,7 @@ __global__ __launch_bounds__(512) void prefill_wide_kernel(PrefillParams p) {
                     float pr[16];
 #pragma unroll
                     for (int r = 0; r < 16; ++r)
-                        pr[r] = kMasked ? exp2_fast(x[a][r] - m_use) : exp2_fast(fmaf(x[a][r], c_scale, -m_use));
+                        pr[r] = exp2_fast(fmaf(x[a][r], c_scale, -m_use));
                     lp += (((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]))) +
                           (((pr[8] + pr[9]) + (pr[10] + pr[11])) + ((pr[12] + pr[13]) + (pr[14] + pr[15])));
                     auto pack = [](float lo, float hi) __attribute__((always_inline)) {
@@ -486,8 +489,9 @@ __global__ __launch_bounds__(512) void prefill_wide_kernel(PrefillParams p) {
                 l_sum = fmaf(l_sum, alpha, lp);
                 __builtin_amdgcn_sched_barrier(0);
 
-                // ---- PV; tokens past a block's valid count are zeroed in
-                // masked steps (they may hold NaN, and 0 * NaN = NaN)
+                // ---- PV; tokens past a block's valid count (the context end,
+                // a block outside the pool) are zeroed: they may hold NaN, and
+                // 0 * NaN = NaN.  The causal diagonal needs no zeroing.
 #pragma unroll
                 for (int a = 0; a < kP; ++a)
 #pragma unroll
@@ -498,15 +502,18 @@ __global__ __launch_bounds__(512) void prefill_wide_kernel(PrefillParams p) {
                             vop[t] = (a == 0 && b == 0) ? v_first[t]
                                                         : src[kP * WS::kKChunks + a * WS::kVChunks + 64 * (b * kDT + t) + lane];
                         if constexpr (kMasked) {
-                            const int nv = nv_of(u, 2 * a + b) - 8 * h;
-                            const uint32_t m0 = tail_mask(nv, 0), m1 = tail_mask(nv, 2), m2 = tail_mask(nv, 4),
-                                           m3 = tail_mask(nv, 6);
+                            const int nvb = nv_of(u, 2 * a + b);
+                            if (nvb < kBlockSize) {
+                                const int nv = nvb - 8 * h;
+                                const uint32_t m0 = tail_mask(nv, 0), m1 = tail_mask(nv, 2), m2 = tail_mask(nv, 4),
+                                               m3 = tail_mask(nv, 6);
 #pragma unroll
-                            for (int t = 0; t < kDT; ++t) {
-                                vop[t].x &= m0;
-                                vop[t].y &= m1;
-                                vop[t].z &= m2;
-                                vop[t].w &= m3;
+                                for (int t = 0; t < kDT; ++t) {
+                                    vop[t].x &= m0;
+                                    vop[t].y &= m1;
+                                    vop[t].z &= m2;
+                                    vop[t].w &= m3;
+                                }
                             }
                         }
 #pragma unroll

@@ -97,6 +97,17 @@ def test_fp32_output():
     check(b, what="fp32 out", out_dtype=torch.float32)
 
 
+@pytest.mark.parametrize("scale_kind", ["negative", "zero"])
+def test_negative_and_zero_scale(scale_kind):
+    """A negative scale (carried by q) and a zero one (every visible key
+    weighs the same: the output is the mean of the visible V rows), on a mix
+    with causal-diagonal and context-end blocks."""
+    cached, new = MIXES["block_edges"]
+    b = W.build_prefill(f"prefill_scale_{scale_kind}", 8, 32, 8, 128, cached, new)
+    b.scale = -b.scale if scale_kind == "negative" else 0.0
+    check(b, what=f"{scale_kind} scale")
+
+
 def test_single_query_rows_match_decode_kernel():
     """n = 1 for every request: the prefill kernel and the decode kernel agree (both vs the oracle too)."""
     b = W.build_prefill("prefill_as_decode", 9, 32, 8, 128, [10, 200, 1500, 4095], [1, 1, 1, 1])
