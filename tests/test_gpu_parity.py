@@ -282,6 +282,28 @@ def test_head_groupings(dtype, hq, hkv, D):
         run_and_check(b, partition_size=ps, what=f"{dtype} {hq}/{hkv} D={D}")
 
 
+@pytest.mark.parametrize("dtype,hq,hkv,D,ps,kind", [
+    ("bf16", 8, 2, 128, 0, "skew"), ("bf16", 8, 2, 64, 0, "skew"), ("bf16", 6, 2, 128, 0, "short"),
+    ("f32", 3, 3, 64, 16, "short"), ("f32", 3, 3, 64, 64, "short")])
+def test_reduce_shapes(dtype, hq, hkv, D, ps, kind):
+    """The split-K merge in each of its forms (for a part with 128 to 1024
+    balanced-decode workgroup columns):
+    * skew: one 20000-token sequence among 63 short ones.  At most 1024
+      ranges for 64 sequences, so one wave merges each row; the long
+      sequence's rows (89 pieces or more) are merged by whole workgroups.
+    * bf16 short: 33 sequences x 6 heads = 198 rows, so the last workgroup of
+      four rows is half empty.
+    * fp32, 16-token partitions: up to 44 pieces, one workgroup per row;
+      64-token partitions: at most 11, one wave per row, 15 rows."""
+    rng = np.random.default_rng([hq, hkv, D, ps, len(kind)])
+    if kind == "skew":
+        lengths = np.concatenate([[20000], rng.integers(16, 200, size=63)])
+    else:
+        lengths = rng.integers(1, 700, size=33 if dtype == "bf16" else 5)
+    b = W.build_static("reduce", 8, dtype, hq, hkv, D, lengths, W.pool_blocks_for(lengths, 16))
+    run_and_check(b, partition_size=ps, what=f"{dtype} {hq}/{hkv} D={D} {kind}")
+
+
 def test_zero_length_and_single_token():
     b = W.build_static("edge", 9, "bf16", 8, 2, 128, [1, 1, 40, 300], 30)
     db, got = run_and_check(b, partition_size=32)
