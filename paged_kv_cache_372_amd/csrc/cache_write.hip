@@ -209,46 +209,53 @@ __global__ __launch_bounds__(kThreads) void cache_write_fp8_kernel(const E* __re
     const float ks = k_scale[h];
     const float vs = v_scale[h];
 
-    if (tid < kTokens) {
-        const int64_t t = t0 + tid;
-        int64_t tile = -1;
-        int off = 0;
-        if (t < num_tokens) {
-            const int64_t slot = slot_mapping[t];
-            if (slot >= 0 && slot < num_slots) {
-                tile = (slot / kBlockSize * num_kv_heads + h) * (int64_t)(D * kBlockSize);
-                off = (int)(slot % kBlockSize);
-            }
-        }
-        tile_of[tid] = tile;
-        off_of[tid] = off;
-    }
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t t_last = num_tokens - 1;  // launched for num_tokens >= 1
+    // ---- every load goes out before any is waited for: the slots (wave 0,
+    // lane t: token t0 + t), then the K and V rows.  Tokens past the last one
+    // read the last one again and are not stored; so are the clamped chunks of
+    // threads with no K chunk of their own.
+    int64_t slot_in = -1;
+    if (wave == 0) slot_in = slot_mapping[t0 + tid < t_last ? t0 + tid : t_last];
     constexpr int X = 16 / (int)sizeof(E);            // input elements per 16-byte load
     // K inputs of this thread (thread (c, t), t fastest: the 16 elements of
-    // output chunk c of token t), loaded before the barrier as for bf16
+    // output chunk c of token t)
     constexpr int K_IT = (kTokens * NCH + kThreads - 1) / kThreads;
     constexpr int KW = 16 / X;                        // 16-byte loads per output chunk
     uint4 kraw[K_IT][KW];
 #pragma unroll
     for (int it = 0; it < K_IT; ++it) {
         const int i = tid + it * kThreads;
-        const int t = i % kTokens;
-        const int c = i / kTokens;
+        const int64_t t = t0 + i % kTokens < t_last ? t0 + i % kTokens : t_last;
+        const int c = i / kTokens < NCH ? i / kTokens : NCH - 1;
+        const uint4* src = reinterpret_cast<const uint4*>(k_new + (t * num_kv_heads + h) * (int64_t)D + 16 * c);
 #pragma unroll
-        for (int u = 0; u < KW; ++u) kraw[it][u] = make_uint4(0, 0, 0, 0);
-        if (i < kTokens * NCH && t0 + t < num_tokens) {
-            const uint4* src = reinterpret_cast<const uint4*>(k_new + ((t0 + t) * num_kv_heads + h) * (int64_t)D + 16 * c);
-#pragma unroll
-            for (int u = 0; u < KW; ++u) kraw[it][u] = src[u];
-        }
+        for (int u = 0; u < KW; ++u) kraw[it][u] = src[u];
     }
-    for (int i = tid; i < kTokens * (D / X); i += kThreads) {
-        const int t = i / (D / X);
-        const int c = i % (D / X);
-        if (t0 + t < num_tokens) {
-            const uint4 w = reinterpret_cast<const uint4*>(v_new + ((t0 + t) * num_kv_heads + h) * (int64_t)D)[c];
-            *reinterpret_cast<uint4*>(&vrow[t][c * X]) = w;
+    // V rows: 16-byte pieces, thread i takes piece i % (D / X) of token i / (D / X)
+    constexpr int V_PIECES = kTokens * (D / X);
+    constexpr int V_IT = (V_PIECES + kThreads - 1) / kThreads;
+    uint4 vraw[V_IT];
+#pragma unroll
+    for (int it = 0; it < V_IT; ++it) {
+        const int i = (tid + it * kThreads) < V_PIECES ? tid + it * kThreads : V_PIECES - 1;
+        const int64_t t = t0 + i / (D / X) < t_last ? t0 + i / (D / X) : t_last;
+        vraw[it] = reinterpret_cast<const uint4*>(v_new + (t * num_kv_heads + h) * (int64_t)D)[i % (D / X)];
+    }
+    if (wave == 0 && tid < kTokens) {
+        int64_t tile = -1;
+        int off = 0;
+        if (t0 + tid < num_tokens && slot_in >= 0 && slot_in < num_slots) {
+            tile = (slot_in / kBlockSize * num_kv_heads + h) * (int64_t)(D * kBlockSize);
+            off = (int)(slot_in % kBlockSize);
         }
+        tile_of[tid] = tile;
+        off_of[tid] = off;
+    }
+#pragma unroll
+    for (int it = 0; it < V_IT; ++it) {
+        const int i = tid + it * kThreads;
+        if (i < V_PIECES) *reinterpret_cast<uint4*>(&vrow[i / (D / X)][(i % (D / X)) * X]) = vraw[it];
     }
     __syncthreads();
 
