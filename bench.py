@@ -4,14 +4,14 @@
 
 One step is one pass of the whole hot path over one batch: the cache write of
 every sequence's new token, the block-table-driven decode partitions, and the
-split-K reduce.  Where every sequence gains one bf16 token at position L - 1
-(the static bf16 decode workloads) the measured step is the fused form,
-paged_attention_decode_append, whose decode launch stores the new tokens
-itself (bit for bit the result of the two calls); the two-call form,
-reshape_and_cache then paged_attention_decode, is timed beside it and
-reported under ``two_call`` (``--two-call`` makes it the measured step).
-Other workloads (fp32, fp8, continuous batching with prompt writes) take the
-two calls.  The default workload is the
+split-K reduce.  Where every sequence gains one token at position L - 1 of
+a bf16 or fp8 cache (the static bf16 and fp8 decode workloads) the measured
+step is the fused form, paged_attention_decode_append(_fp8), whose decode
+launch stores the new tokens itself (bit for bit the result of the two
+calls); the two-call form, reshape_and_cache(_fp8) then
+paged_attention_decode(_fp8), is timed beside it and reported under
+``two_call`` (``--two-call`` makes it the measured step).  Other workloads
+(fp32, continuous batching with prompt writes) take the two calls.  The default workload is the
 Llama-3-8B-shaped decode layer (64 sequences, 32 q / 8 KV heads, head_dim 128,
 bf16 KV, context lengths uniform on [128, 4096]).  Inputs are resident in HBM
 before timing starts.  To keep the 256 MB Infinity Cache from serving KV
@@ -55,8 +55,8 @@ def family(workload: str) -> str:
     return "decode"
 
 
-# static bf16 decode workloads whose step can take the fused append
-FUSABLE_CONFIGS = ("llama3_8b_decode", "shared_prefix", "long_context")
+# static bf16 and fp8 decode workloads whose step can take the fused append
+FUSABLE_CONFIGS = ("llama3_8b_decode", "shared_prefix", "long_context", "llama3_8b_decode_fp8", "long_context_fp8")
 
 
 def traffic_file(workload: str, fused: bool = False) -> str:
@@ -957,14 +957,15 @@ def run_decode(args, config, partition_arg, steps, warmup, fused_flag, compare_f
                                              shared_blocks=g["shared"], k_scale=k_scale, v_scale=v_scale)
     resolved_ps = ps if ps else ("auto" if b.dtype == "f32" else "balanced")
 
-    # The fused step applies when each sequence gains exactly one bf16 token,
-    # stored at position L - 1 of its table (the static decode workloads).
+    # The fused step applies when each sequence gains exactly one token, into
+    # a bf16 or fp8 cache at position L - 1 of its table (the static decode
+    # workloads).
     def append_slots(bt, lens):
         lens = np.asarray(lens, dtype=np.int64)
         pos = lens - 1
         return np.asarray(bt, dtype=np.int64)[np.arange(len(lens)), pos // b.block_size] * b.block_size \
             + pos % b.block_size
-    fusable = (b.dtype == "bf16" and b.num_q_heads // b.num_kv_heads <= 16 and
+    fusable = (b.dtype in ("bf16", "fp8") and b.num_q_heads // b.num_kv_heads <= 16 and
                all(len(h[2]) == len(h[5]) and int(np.min(h[5])) >= 1 and
                    np.array_equal(np.asarray(h[2], dtype=np.int64), append_slots(h[4], h[5])) for h in host_steps))
     fused = fusable and fused_flag
@@ -975,7 +976,8 @@ def run_decode(args, config, partition_arg, steps, warmup, fused_flag, compare_f
             for r in range(R):
                 fplans[j, r] = ops.prepare_decode(g["q"], kcs[r], vcs[r], g["bt"], g["lens"], b.scale, g["out"],
                                                   partition_size=ps, max_context_len=g["max_ctx"], workspace=ws,
-                                                  shared_blocks=g["shared"], k_new=g["k_new"], v_new=g["v_new"])
+                                                  shared_blocks=g["shared"], k_scale=k_scale, v_scale=v_scale,
+                                                  k_new=g["k_new"], v_new=g["v_new"])
 
     def step_two_call(i, ev=None):
         j, r = i % n_in, i % R

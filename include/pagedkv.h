@@ -218,7 +218,8 @@ pkv_status pkv_paged_attention_decode_reduce(const int32_t* context_lens, void* 
  *   k_new, v_new   [device] [num_seqs][num_kv_heads][head_dim], kv_dtype;
  *                  k_new 16-byte aligned
  *   k_cache, v_cache [device] pools, written at the appended slots
- *   kv_dtype       PKV_BF16 only (others: PKV_ERR_UNSUPPORTED)
+ *   kv_dtype       PKV_BF16 only (others: PKV_ERR_UNSUPPORTED; fp8 pools:
+ *                  pkv_paged_attention_decode_append_fp8)
  *   num_q_heads    at most 16 query heads per KV head (else
  *                  PKV_ERR_UNSUPPORTED)
  * All other arguments, the workspace and the flags as for
@@ -330,6 +331,47 @@ pkv_status pkv_paged_attention_decode_partitions_fp8(const void* q, const void* 
                                                      int32_t max_context_len, int32_t partition_size,
                                                      void* workspace, size_t workspace_bytes, pkv_dtype out_dtype,
                                                      uint32_t flags, void* stream);
+
+/*
+ * The fused decode step over an fp8 cache: pkv_paged_attention_decode_append
+ * with E4M3 pools.  The new tokens arrive as bf16 rows and are stored as the
+ * codes pkv_reshape_and_cache_fp8(..., src_dtype = PKV_BF16) would store
+ * (E4M3 of fp32(x / scale) with the KV head's k_scale or v_scale); the
+ * attention is that of pkv_paged_attention_decode_fp8.  Pools and out are
+ * bit for bit those of those two calls in a row with slot_mapping as for
+ * pkv_paged_attention_decode_append.  The decode step appends the token and
+ * attends over the whole cache (runbyai sections 1-2); the codes are the
+ * reading of KV quantisation for long contexts (runbyai section 5) that
+ * pkv_reshape_and_cache_fp8 states.
+ *   k_new, v_new      [device] bf16 [num_seqs][num_kv_heads][head_dim];
+ *                     k_new 16-byte aligned
+ *   k_cache, v_cache  [device] fp8 pools (layout as for
+ *                     pkv_reshape_and_cache_fp8), written at the appended
+ *                     slots
+ *   k_scale, v_scale  [device] fp32 [num_kv_heads], positive
+ * Null scales return PKV_ERR_INVALID_ARG; everything else as for
+ * pkv_paged_attention_decode_append (at most 16 query heads per KV head).
+ * Workspace: pkv_decode_workspace_bytes(..., PKV_FP8_E4M3).
+ */
+pkv_status pkv_paged_attention_decode_append_fp8(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                                                 void* v_cache, const float* k_scale, const float* v_scale,
+                                                 const int32_t* block_tables, const int32_t* context_lens, float scale,
+                                                 void* out, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                                 int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                                 int32_t max_blocks_per_seq, int32_t max_context_len,
+                                                 int32_t partition_size, void* workspace, size_t workspace_bytes,
+                                                 pkv_dtype out_dtype, uint32_t flags, void* stream);
+
+/* The decode launch of pkv_paged_attention_decode_append_fp8 on its own (the
+ * append included); follow it with pkv_paged_attention_decode_reduce(...,
+ * kv_dtype = PKV_FP8_E4M3, ...) on the same stream with the same sizes and
+ * workspace. */
+pkv_status pkv_paged_attention_decode_append_partitions_fp8(
+    const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache, const float* k_scale,
+    const float* v_scale, const int32_t* block_tables, const int32_t* context_lens, float scale, void* out,
+    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len, int32_t partition_size, void* workspace,
+    size_t workspace_bytes, pkv_dtype out_dtype, uint32_t flags, void* stream);
 
 /*
  * Whole-block copies between KV pools: copy-on-write and swapping.

@@ -30,6 +30,7 @@
 // Infinity Cache were measured to slow the following decode (a step with
 // 17k prompt tokens written: decode 241 -> 205 us, step 280 -> 258 us;
 // Llama-shaped decode step 108 -> 104 us).
+#include "e4m3.h"
 #include "kernels.h"
 
 namespace pkv {
@@ -40,23 +41,6 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kTokens = 16;            // run starts per workgroup
 constexpr int kWindow = 2 * kTokens;   // tokens a workgroup may write
 constexpr int kThreads = 256;
-
-// fp32 -> OCP E4M3 code: round to nearest (ties to even mantissa), saturate
-// at +-448; the sign of zero is kept.  Written out from the format (1 sign,
-// 4 exponent bits with bias 7, 3 mantissa bits, subnormals m * 2^-9) with
-// integer operations, so the result is fixed bit for bit.
-__device__ __forceinline__ uint32_t e4m3_rne_sat(float y) {
-    const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
-    const float a = fminf(fabsf(y), 448.f);
-    if (a < 0.015625f)                                   // below 2^-6: multiples of 2^-9
-        return sign | (uint32_t)__builtin_rintf(a * 512.f);  // exact scaling, rint rounds to even
-    const uint32_t ab = __float_as_uint(a);
-    const uint32_t r = (ab >> 20) & 7u;                  // top 3 mantissa bits
-    const uint32_t rem = ab & 0xFFFFFu;                  // the 20 dropped bits
-    const uint32_t up = (rem > 0x80000u || (rem == 0x80000u && (r & 1u))) ? 1u : 0u;
-    const uint32_t code = ((((ab >> 23) - 120u) << 3) | r) + up;  // exponent bias 127 -> 7; a carry bumps it
-    return sign | (code < 0x7Eu ? code : 0x7Eu);
-}
 
 // Copying cache write (bf16 or fp32 pools): one workgroup per (16
 // consecutive tokens, KV head), writing the runs that start among them.
@@ -278,7 +262,7 @@ __global__ __launch_bounds__(kThreads) void cache_write_fp8_kernel(const E* __re
         for (int q4 = 0; q4 < 4; ++q4) {
             uint32_t b = 0;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) b |= e4m3_rne_sat(to_f32(src[4 * q4 + e]) / ks) << (8 * e);
+            for (int e = 0; e < 4; ++e) b |= e4m3_encode(to_f32(src[4 * q4 + e]), ks) << (8 * e);
             w[q4] = b;
         }
         __builtin_nontemporal_store(u32x4_t{w[0], w[1], w[2], w[3]},
@@ -290,7 +274,7 @@ __global__ __launch_bounds__(kThreads) void cache_write_fp8_kernel(const E* __re
         const int d = i / kTokens;
         const int64_t tile = tile_of[t];
         if (tile < 0) continue;
-        __builtin_nontemporal_store((uint8_t)e4m3_rne_sat(to_f32(vrow[t][d]) / vs),
+        __builtin_nontemporal_store((uint8_t)e4m3_encode(to_f32(vrow[t][d]), vs),
                                     v_cache + tile + (int64_t)d * kBlockSize + off_of[t]);
     }
 }

@@ -28,8 +28,8 @@
 // memory only once, at its start.
 //
 // With the fused append (a decode step's cache write in this launch, bf16
-// pools), the wave that walks a sequence's last block also stores the
-// token the sequence gains this step; see the comment at its prologue.
+// or fp8 pools), the wave that walks a sequence's last block also stores
+// the token the sequence gains this step; see the comment at its prologue.
 //
 // Per 16-token block, per wave:
 //   S[16 tok x 16 heads] = K[16 x D] . Q^T[D x 16]  D/32 x mfma_f32_16x16x32_bf16
@@ -55,6 +55,7 @@
 // blocks sit in the pool.
 #include <type_traits>
 
+#include "e4m3.h"
 #include "kernels.h"
 
 namespace pkv {
@@ -304,8 +305,8 @@ typedef const int32_t __attribute__((address_space(4)))* scalar_i32_ptr;
 
 // Dynamic LDS of the balanced kernel: the flattened offsets and lengths of
 // the batch ([B + 1] and [B] int32), then, with the fused append, each
-// wave's kAppendSlots new-token rows (K and V, D bf16 each) from a 16-byte
-// boundary.
+// wave's kAppendSlots new-token rows (K and V, D pool elements each: bf16,
+// or E4M3 codes) from a 16-byte boundary.
 __host__ __device__ inline int append_rows_offset(int num_seqs) { return (2 * num_seqs + 1 + 3) & ~3; }
 
 template <int D, int kDepth, bool kCached, bool kFp8, bool kPackLo>
@@ -394,7 +395,7 @@ __global__ __launch_bounds__(64 * kMaxWavesPerGroup) void decode_bf16_balanced_k
     const int n_ranges = (NR - 1 - walker) / NG + 1;
     const int r_final = walker + NG * (n_ranges - 1);
     const int K = (n_ranges - 1) * CS + min(CS, T - r_final * CS);  // blocks this workgroup walks
-    const bool appending = !kFp8 && p.k_new != nullptr;  // fused append of the new tokens
+    const bool appending = p.k_new != nullptr;  // fused append of the new tokens
 
     // last sequence starting at or before flattened block f (it holds block f)
     auto seq_of_block = [&](int f) {
@@ -480,9 +481,13 @@ __global__ __launch_bounds__(64 * kMaxWavesPerGroup) void decode_bf16_balanced_k
     // lines it has written, and no other wave reads the slot.  Tokens past the
     // first kAppendSlots of a walk (short sequences) are stored into the
     // pool before the walk instead, and read back from it.  A table entry
-    // outside the pool is skipped, as the walk skips it.
-    using Row = uint16_t;  // bf16 pools
-    Row* const ap_rows = reinterpret_cast<Row*>(tables + append_rows_offset(B)) + wave * (kAppendSlots * 2 * D);
+    // outside the pool is skipped, as the walk skips it.  The new rows are
+    // bf16; into an fp8 pool they go as the codes the quantising cache write
+    // stores (e4m3_encode with the KV head's scales), encoded once, when they
+    // enter LDS or the pool, each lane encoding its own dims.
+    // LDS rows: K then V, D pool elements each
+    Elem* const ap_rows = reinterpret_cast<Elem*>(tables + append_rows_offset(B)) + wave * (kAppendSlots * 2 * D);
+    constexpr int kRowChunks = D * (int)sizeof(Elem) / 16;  // 16-byte chunks of a row as the pool holds it
     // next sequence, from cursor (ri, s) on, whose last block lies in range
     // ri of this walk; -1 when none is left
     auto next_append = [&](int& ri, int& s) -> int {
@@ -500,36 +505,51 @@ __global__ __launch_bounds__(64 * kMaxWavesPerGroup) void decode_bf16_balanced_k
         }
         return -1;
     };
+    // A new token's rows as loaded (bf16 bits).  bf16 pools: lanes <
+    // kRowChunks hold the 8 dims of K chunk `lane`.  fp8 pools: every lane
+    // holds K dims lane + 64i (an fp8 K row as the pool holds it is its codes
+    // in dim order, chunk c being dims 16c..16c+15, so each lane encodes its
+    // own dims).  V: dims lane + 64i.
     struct NewRow {
-        uint4 k;                    // lanes < D/8: 16-byte chunk `lane` of the K row
-        uint32_t v[(D + 63) / 64];  // dim lane + 64i of the V row
+        uint4 k;
+        uint32_t kd[(D + 63) / 64];
+        uint32_t v[(D + 63) / 64];
     };
     auto load_new_row = [&](int s, NewRow& a) {
         const int64_t src = ((int64_t)s * p.num_kv_heads + kvh) * D;
-        a.k = lane < D / 8 ? reinterpret_cast<const uint4*>(reinterpret_cast<const Row*>(p.k_new) + src)[lane]
-                           : make_uint4(0, 0, 0, 0);
+        const uint16_t* kn = reinterpret_cast<const uint16_t*>(p.k_new) + src;
+        if constexpr (kFp8) {
+#pragma unroll
+            for (int i = 0; i < (D + 63) / 64; ++i) a.kd[i] = lane + 64 * i < D ? kn[lane + 64 * i] : 0u;
+        } else {
+            a.k = lane < kRowChunks ? reinterpret_cast<const uint4*>(kn)[lane] : make_uint4(0, 0, 0, 0);
+        }
 #pragma unroll
         for (int i = 0; i < (D + 63) / 64; ++i)
-            a.v[i] = lane + 64 * i < D ? reinterpret_cast<const Row*>(p.v_new)[src + lane + 64 * i] : 0u;
+            a.v[i] = lane + 64 * i < D ? reinterpret_cast<const uint16_t*>(p.v_new)[src + lane + 64 * i] : 0u;
     };
-    Row* const kc_base = reinterpret_cast<Row*>(const_cast<void*>(p.k_cache)) + (int64_t)kvh * D * kBlockSize;
-    Row* const vc_base = reinterpret_cast<Row*>(const_cast<void*>(p.v_cache)) + (int64_t)kvh * D * kBlockSize;
+    // fp8 pools: the code of a bf16 value, with the KV head's K or V scale
+    const float ks_new = kFp8 ? p.k_scale[kvh] : 1.f;
+    const float vs_new = kFp8 ? p.v_scale[kvh] : 1.f;
+    auto encode = [&](uint32_t bits, float scale) -> Elem {
+        return (Elem)e4m3_encode(__uint_as_float(bits << 16), scale);
+    };
+    Elem* const kc_base = reinterpret_cast<Elem*>(const_cast<void*>(p.k_cache)) + (int64_t)kvh * D * kBlockSize;
+    Elem* const vc_base = reinterpret_cast<Elem*>(const_cast<void*>(p.v_cache)) + (int64_t)kvh * D * kBlockSize;
     int ap_ri = 0, ap_s = -1;
     int ap_count = 0;  // rows kept in LDS
     int ap_used = 0;   // sequence ends the walk has reached
     NewRow ap_row[kAppendSlots];
-    if constexpr (!kFp8) {
-        if (appending) {
-            // rows of the first kAppendSlots ends, requested before the
-            // walk's first table fetches and written to LDS once its first
-            // KV loads are issued
+    if (appending) {
+        // rows of the first kAppendSlots ends, requested before the walk's
+        // first table fetches and written to LDS once its first KV loads are
+        // issued
 #pragma unroll
-            for (int j = 0; j < kAppendSlots; ++j) {
-                const int s = ap_count == j ? next_append(ap_ri, ap_s) : -1;
-                if (s >= 0) {
-                    load_new_row(s, ap_row[j]);
-                    ++ap_count;
-                }
+        for (int j = 0; j < kAppendSlots; ++j) {
+            const int s = ap_count == j ? next_append(ap_ri, ap_s) : -1;
+            if (s >= 0) {
+                load_new_row(s, ap_row[j]);
+                ++ap_count;
             }
         }
     }
@@ -543,11 +563,20 @@ __global__ __launch_bounds__(64 * kMaxWavesPerGroup) void decode_bf16_balanced_k
 #pragma unroll
         for (int j = 0; j < kAppendSlots; ++j) {
             if (j < ap_count) {
-                Row* r = ap_rows + j * 2 * D;
-                if (lane < D / 8) reinterpret_cast<uint4*>(r)[lane] = ap_row[j].k;
+                Elem* r = ap_rows + j * 2 * D;
+                if constexpr (kFp8) {
 #pragma unroll
-                for (int i = 0; i < (D + 63) / 64; ++i)
-                    if (lane + 64 * i < D) r[D + lane + 64 * i] = (Row)ap_row[j].v[i];
+                    for (int i = 0; i < (D + 63) / 64; ++i)
+                        if (lane + 64 * i < D) {
+                            r[lane + 64 * i] = encode(ap_row[j].kd[i], ks_new);
+                            r[D + lane + 64 * i] = encode(ap_row[j].v[i], vs_new);
+                        }
+                } else {
+                    if (lane < kRowChunks) reinterpret_cast<uint4*>(r)[lane] = ap_row[j].k;
+#pragma unroll
+                    for (int i = 0; i < (D + 63) / 64; ++i)
+                        if (lane + 64 * i < D) r[D + lane + 64 * i] = (Elem)ap_row[j].v[i];
+                }
             }
         }
     };
@@ -562,36 +591,70 @@ __global__ __launch_bounds__(64 * kMaxWavesPerGroup) void decode_bf16_balanced_k
             load_new_row(s, a);
             if (e < 0 || (int64_t)e >= p.num_blocks) continue;
             const int o = pos % kBlockSize;
-            Row* kc = kc_base + (int64_t)e * block_stride;
-            Row* vc = vc_base + (int64_t)e * block_stride;
-            // K tile [D/8][16][8]: chunk c of token o at (16c + o) * 8;
+            Elem* kc = kc_base + (int64_t)e * block_stride;
+            Elem* vc = vc_base + (int64_t)e * block_stride;
+            // K tile [D*sizeof(Elem)/16][16][16 bytes]: chunk c of token o at
+            // 16-byte unit 16c + o (fp8: dim d is byte d % 16 of chunk d / 16);
             // V tile [D][16]: dim d of token o at 16d + o
-            if (lane < D / 8) reinterpret_cast<uint4*>(kc)[lane * kBlockSize + o] = a.k;
+            if constexpr (kFp8) {
 #pragma unroll
-            for (int i = 0; i < (D + 63) / 64; ++i)
-                if (lane + 64 * i < D) vc[(lane + 64 * i) * kBlockSize + o] = (Row)a.v[i];
+                for (int i = 0; i < (D + 63) / 64; ++i) {
+                    const int d = lane + 64 * i;
+                    if (d < D) {
+                        kc[((d >> 4) * kBlockSize + o) * 16 + (d & 15)] = encode(a.kd[i], ks_new);
+                        vc[d * kBlockSize + o] = encode(a.v[i], vs_new);
+                    }
+                }
+            } else {
+                if (lane < kRowChunks) reinterpret_cast<uint4*>(kc)[lane * kBlockSize + o] = a.k;
+#pragma unroll
+                for (int i = 0; i < (D + 63) / 64; ++i)
+                    if (lane + 64 * i < D) vc[(lane + 64 * i) * kBlockSize + o] = (Elem)a.v[i];
+            }
         }
     };
     // The new token (position o of the block in ring slot r, LDS row j) in
-    // the slot's operand registers: K chunk 4kk + g of token lane % 16, and
-    // V dims 16c + lane % 16 of tokens 4g..4g+3 (two per 32-bit word).
-    auto patch_slot = [&](SlotRegs<D>& r, int j, int o) {
-        const Row* row = ap_rows + j * 2 * D;
+    // the slot's operand registers.  bf16: K chunk 4kk + g of token
+    // lane % 16, and V dims 16c + lane % 16 of tokens 4g..4g+3 (two per
+    // 32-bit word).  fp8: K code chunk 4i + g of token lane % 16, and byte o
+    // of the 16 codes of dim 64i + lane.
+    auto patch_slot = [&](Slot& r, int j, int o) {
+        const Elem* row = ap_rows + j * 2 * D;
         const bool kt = (lane & 15) == o;
+        if constexpr (kFp8) {
 #pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk) {
-            const uint4 w = reinterpret_cast<const uint4*>(row)[4 * kk + g];
-            if (kt) r.k[kk] = w;
-        }
-        const bool vt = g == (o >> 2);
-        const uint32_t sh = (o & 1) * 16;
-        const uint32_t keep = ~(0xFFFFu << sh);
+            for (int i = 0; i < D / 64; ++i) {
+                const uint4 w = reinterpret_cast<const uint4*>(row)[4 * i + g];
+                if (kt) r.k[i] = w;
+            }
+            const uint32_t sh = (o & 3) * 8;
+            const uint32_t keep = ~(0xFFu << sh);
 #pragma unroll
-        for (int c = 0; c < D / 16; ++c) {
-            const uint32_t x = (uint32_t)row[D + 16 * c + (lane & 15)] << sh;
-            if (vt) {
-                if (o & 2) r.v[c].y = (r.v[c].y & keep) | x;
-                else r.v[c].x = (r.v[c].x & keep) | x;
+            for (int i = 0; i < D / 64; ++i) {
+                const uint32_t x = (uint32_t)row[D + 64 * i + lane] << sh;
+                switch (o >> 2) {  // the same in every lane
+                    case 0: r.v[i].x = (r.v[i].x & keep) | x; break;
+                    case 1: r.v[i].y = (r.v[i].y & keep) | x; break;
+                    case 2: r.v[i].z = (r.v[i].z & keep) | x; break;
+                    default: r.v[i].w = (r.v[i].w & keep) | x; break;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < D / 32; ++kk) {
+                const uint4 w = reinterpret_cast<const uint4*>(row)[4 * kk + g];
+                if (kt) r.k[kk] = w;
+            }
+            const bool vt = g == (o >> 2);
+            const uint32_t sh = (o & 1) * 16;
+            const uint32_t keep = ~(0xFFFFu << sh);
+#pragma unroll
+            for (int c = 0; c < D / 16; ++c) {
+                const uint32_t x = (uint32_t)row[D + 16 * c + (lane & 15)] << sh;
+                if (vt) {
+                    if (o & 2) r.v[c].y = (r.v[c].y & keep) | x;
+                    else r.v[c].x = (r.v[c].x & keep) | x;
+                }
             }
         }
     };
@@ -609,10 +672,10 @@ __global__ __launch_bounds__(64 * kMaxWavesPerGroup) void decode_bf16_balanced_k
     // acknowledgement of a store under the full read stream stalls the
     // wait that first covers it.
     auto store_token = [&](int j, int pb, int o) {
-        const Row* row = ap_rows + j * 2 * D;
-        Row* kc = kc_base + (int64_t)pb * block_stride;
-        Row* vc = vc_base + (int64_t)pb * block_stride;
-        if (lane < D / 8)
+        const Elem* row = ap_rows + j * 2 * D;
+        Elem* kc = kc_base + (int64_t)pb * block_stride;
+        Elem* vc = vc_base + (int64_t)pb * block_stride;
+        if (lane < kRowChunks)
             __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, reinterpret_cast<const uint4*>(row)[lane]),
                                         reinterpret_cast<u32x4_t*>(kc) + lane * kBlockSize + o);
 #pragma unroll
@@ -747,9 +810,7 @@ __global__ __launch_bounds__(64 * kMaxWavesPerGroup) void decode_bf16_balanced_k
     SlotInfo next_info[kDepth];
 #pragma unroll
     for (int d = 0; d < kDepth; ++d) fetch(d, pend[d]);
-    if constexpr (!kFp8) {
-        if (appending) append_overflow();
-    }
+    if (appending) append_overflow();
 #pragma unroll
     for (int d = 0; d < kDepth; ++d) accept(pend[d], next_pb[d], next_info[d]);
 #pragma unroll
@@ -759,9 +820,7 @@ __global__ __launch_bounds__(64 * kMaxWavesPerGroup) void decode_bf16_balanced_k
         load_slot(d, next_pb[d], next_info[d]);
         __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (!kFp8) {
-        if (appending) append_rows_to_lds();
-    }
+    if (appending) append_rows_to_lds();
     __builtin_amdgcn_sched_barrier(0);
     // One round: compute the kDepth blocks in the ring, refilling each slot
     // with the block kDepth positions further on.  In the last rounds the
@@ -795,26 +854,22 @@ __global__ __launch_bounds__(64 * kMaxWavesPerGroup) void decode_bf16_balanced_k
             if (!kFinal || i + d < K) {
                 // fused append: the block that holds a sequence's new token
                 bool patched = false;
-                if constexpr (!kFp8) {
-                    if (info[d].meta & kSeqEnd) {
-                        const int nv = info[d].meta & 31;
-                        patched = ap_used < ap_count && nv > 0;
-                        if (patched) patch_slot(ring[d], ap_used, nv - 1);
-                        ++ap_used;
-                    }
+                if (info[d].meta & kSeqEnd) {
+                    const int nv = info[d].meta & 31;
+                    patched = ap_used < ap_count && nv > 0;
+                    if (patched) patch_slot(ring[d], ap_used, nv - 1);
+                    ++ap_used;
                 }
                 compute_block<D, kPackLo>(ring[d], acc, st, info[d].meta & 31, score_scale, g, lo_mask);
                 if (info[d].meta & kSegLast) {
                     finish_segment(info[d].seq, info[d].slot);
-                    if constexpr (!kFp8) {
-                        if (patched) {  // stored after the walk
+                    if (patched) {  // stored after the walk
 #pragma unroll
-                            for (int j = 0; j < kAppendSlots; ++j)
-                                if (j == ap_used - 1) {
-                                    ap_pb[j] = info[d].pb;
-                                    ap_o[j] = (info[d].meta & 31) - 1;
-                                }
-                        }
+                        for (int j = 0; j < kAppendSlots; ++j)
+                            if (j == ap_used - 1) {
+                                ap_pb[j] = info[d].pb;
+                                ap_o[j] = (info[d].meta & 31) - 1;
+                            }
                     }
                 }
             }
@@ -827,11 +882,9 @@ __global__ __launch_bounds__(64 * kMaxWavesPerGroup) void decode_bf16_balanced_k
     for (; i + 2 * kDepth <= K; i += kDepth) round(i, std::false_type{});
     for (; i < K; i += kDepth) round(i, std::true_type{});
     // fused append: the new tokens patched in above, into the pool
-    if constexpr (!kFp8) {
 #pragma unroll
-        for (int j = 0; j < kAppendSlots; ++j)
-            if (ap_pb[j] >= 0) store_token(j, ap_pb[j], ap_o[j]);
-    }
+    for (int j = 0; j < kAppendSlots; ++j)
+        if (ap_pb[j] >= 0) store_token(j, ap_pb[j], ap_o[j]);
 
 }
 
@@ -840,9 +893,9 @@ __global__ __launch_bounds__(64 * kMaxWavesPerGroup) void decode_bf16_balanced_k
 size_t balanced_lds_bytes(int32_t num_seqs) { return (size_t)(2 * num_seqs + 1) * sizeof(int32_t); }
 
 size_t balanced_lds_bytes(const DecodeParams& p) {
-    if (p.k_new == nullptr || p.kv_fp8) return balanced_lds_bytes(p.num_seqs);
+    if (p.k_new == nullptr) return balanced_lds_bytes(p.num_seqs);
     return (size_t)append_rows_offset(p.num_seqs) * sizeof(int32_t) +
-           (size_t)p.waves_per_group * kAppendSlots * 2 * p.head_dim * sizeof(uint16_t);
+           (size_t)p.waves_per_group * kAppendSlots * 2 * p.head_dim * (p.kv_fp8 ? 1 : sizeof(uint16_t));
 }
 
 const void* balanced_kernel(int32_t head_dim) {

@@ -301,12 +301,14 @@ pkv_status prepare_append(const void* q, const void* k_new, const void* v_new, v
                           int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                           int32_t block_size, int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
                           int32_t partition_size, void* workspace, size_t workspace_bytes, pkv_dtype kv_dtype,
-                          pkv_dtype out_dtype, uint32_t flags, Call* c) {
-    if (kv_dtype != PKV_BF16)
-        return fail(PKV_ERR_UNSUPPORTED, "the fused append takes bf16 pools (use pkv_reshape_and_cache and the decode)");
+                          pkv_dtype out_dtype, uint32_t flags, const float* k_scale, const float* v_scale, Call* c) {
+    if (kv_dtype != PKV_BF16 && kv_dtype != PKV_FP8_E4M3)
+        return fail(PKV_ERR_UNSUPPORTED, "the fused append takes bf16 or fp8 pools (use pkv_reshape_and_cache and the decode)");
+    if (kv_dtype == PKV_FP8_E4M3 && num_seqs > 0 && (!k_scale || !v_scale))
+        return fail(PKV_ERR_INVALID_ARG, "an fp8 cache needs k_scale and v_scale");
     pkv_status st = prepare(q, k_cache, v_cache, block_tables, context_lens, scale, out, num_seqs, num_q_heads,
                             num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len,
-                            partition_size, workspace, workspace_bytes, kv_dtype, out_dtype, flags, nullptr, nullptr,
+                            partition_size, workspace, workspace_bytes, kv_dtype, out_dtype, flags, k_scale, v_scale,
                             c);
     if (st != PKV_OK) return st;
     if (c->plan.n_head_groups != 1)
@@ -324,7 +326,7 @@ pkv_status prepare_append(const void* q, const void* k_new, const void* v_new, v
 
 extern "C" {
 
-int32_t pkv_abi_version(void) { return 6; }
+int32_t pkv_abi_version(void) { return 7; }
 
 const char* pkv_status_string(pkv_status status) {
     switch (status) {
@@ -436,11 +438,13 @@ pkv_status pkv_paged_attention_decode_append(const void* q, const void* k_new, c
                                              int32_t partition_size, void* workspace, size_t workspace_bytes,
                                              pkv_dtype kv_dtype, pkv_dtype out_dtype, uint32_t flags, void* stream) {
     g_last_error[0] = 0;
+    if (kv_dtype == PKV_FP8_E4M3)
+        return fail(PKV_ERR_UNSUPPORTED, "an fp8 cache needs its scales: use pkv_paged_attention_decode_append_fp8");
     Call c;
     pkv_status st = prepare_append(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, out, num_seqs,
                                    num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                                    max_context_len, partition_size, workspace, workspace_bytes, kv_dtype, out_dtype,
-                                   flags, &c);
+                                   flags, nullptr, nullptr, &c);
     if (st != PKV_OK) return st;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     st = run_decode_kernels(c, s);
@@ -458,11 +462,13 @@ pkv_status pkv_paged_attention_decode_append_partitions(const void* q, const voi
                                                         size_t workspace_bytes, pkv_dtype kv_dtype,
                                                         pkv_dtype out_dtype, uint32_t flags, void* stream) {
     g_last_error[0] = 0;
+    if (kv_dtype == PKV_FP8_E4M3)
+        return fail(PKV_ERR_UNSUPPORTED, "an fp8 cache needs its scales: use pkv_paged_attention_decode_append_fp8");
     Call c;
     pkv_status st = prepare_append(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, out, num_seqs,
                                    num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                                    max_context_len, partition_size, workspace, workspace_bytes, kv_dtype, out_dtype,
-                                   flags, &c);
+                                   flags, nullptr, nullptr, &c);
     if (st != PKV_OK) return st;
     return run_decode_kernels(c, static_cast<hipStream_t>(stream));
 }
@@ -609,6 +615,43 @@ pkv_status pkv_paged_attention_decode_partitions_fp8(const void* q, const void* 
                             num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len,
                             partition_size, workspace, workspace_bytes, PKV_FP8_E4M3, out_dtype, flags, k_scale,
                             v_scale, &c);
+    if (st != PKV_OK) return st;
+    return run_decode_kernels(c, static_cast<hipStream_t>(stream));
+}
+
+pkv_status pkv_paged_attention_decode_append_fp8(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                                                 void* v_cache, const float* k_scale, const float* v_scale,
+                                                 const int32_t* block_tables, const int32_t* context_lens, float scale,
+                                                 void* out, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                                 int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                                 int32_t max_blocks_per_seq, int32_t max_context_len,
+                                                 int32_t partition_size, void* workspace, size_t workspace_bytes,
+                                                 pkv_dtype out_dtype, uint32_t flags, void* stream) {
+    g_last_error[0] = 0;
+    Call c;
+    pkv_status st = prepare_append(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, out, num_seqs,
+                                   num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                                   max_context_len, partition_size, workspace, workspace_bytes, PKV_FP8_E4M3,
+                                   out_dtype, flags, k_scale, v_scale, &c);
+    if (st != PKV_OK) return st;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    st = run_decode_kernels(c, s);
+    if (st != PKV_OK) return st;
+    return run_reduce_kernels(c, s);
+}
+
+pkv_status pkv_paged_attention_decode_append_partitions_fp8(
+    const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache, const float* k_scale,
+    const float* v_scale, const int32_t* block_tables, const int32_t* context_lens, float scale, void* out,
+    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len, int32_t partition_size, void* workspace,
+    size_t workspace_bytes, pkv_dtype out_dtype, uint32_t flags, void* stream) {
+    g_last_error[0] = 0;
+    Call c;
+    pkv_status st = prepare_append(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, out, num_seqs,
+                                   num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                                   max_context_len, partition_size, workspace, workspace_bytes, PKV_FP8_E4M3,
+                                   out_dtype, flags, k_scale, v_scale, &c);
     if (st != PKV_OK) return st;
     return run_decode_kernels(c, static_cast<hipStream_t>(stream));
 }

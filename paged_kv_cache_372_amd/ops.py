@@ -56,6 +56,12 @@ _SIGNATURES = {
     "pkv_paged_attention_decode_partitions_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _i32, _i32,
                                                          _i32, _i32, _i32, _i64, _i32, _i32, _i32, _vp, _sz, _i32,
                                                          _u32, _vp]),
+    "pkv_paged_attention_decode_append_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _i32, _i32,
+                                                     _i32, _i32, _i32, _i64, _i32, _i32, _i32, _vp, _sz, _i32, _u32,
+                                                     _vp]),
+    "pkv_paged_attention_decode_append_partitions_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp,
+                                                                _i32, _i32, _i32, _i32, _i32, _i64, _i32, _i32, _i32,
+                                                                _vp, _sz, _i32, _u32, _vp]),
     "pkv_copy_blocks": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _vp]),
     "pkv_paged_attention_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                            _i64, _i32, _i32, _i32, _i32, _vp]),
@@ -214,17 +220,23 @@ class _DecodeArgs:
         self.ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
         flags = DECODE_SHARED_BLOCKS if shared_blocks else 0
         if self.append:
-            _require(not self.fp8 and k_cache.dtype == torch.bfloat16, "the fused append takes bf16 pools")
+            _require(self.fp8 or k_cache.dtype == torch.bfloat16, "the fused append takes bf16 or fp8 pools")
             _require(k_new is not None and v_new is not None, "the fused append needs both k_new and v_new")
             _check_tensor(k_new, "k_new", dev)
             _check_tensor(v_new, "v_new", dev)
             _require(tuple(k_new.shape) == (B, hkv, D) and tuple(v_new.shape) == (B, hkv, D),
                      f"k_new and v_new must be [B, {hkv}, {D}]")
-            _require(k_new.dtype == k_cache.dtype and v_new.dtype == k_cache.dtype, "new K/V dtype must match the pools")
-            self.args = (_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
-                         _ptr(context_lens), float(scale), _ptr(out), B, hq, hkv, D, BLOCK_SIZE, nb,
-                         block_tables.shape[1], self.max_context_len, self.partition_size, self.ws_ptr,
-                         self.ws_bytes, _dtype_code(k_cache), _dtype_code(out), flags, _stream(dev))
+            _require(k_new.dtype == torch.bfloat16 and v_new.dtype == torch.bfloat16, "new K/V rows must be bf16")
+            if self.fp8:
+                self.args = (_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                             _ptr(v_scale), _ptr(block_tables), _ptr(context_lens), float(scale), _ptr(out), B, hq,
+                             hkv, D, BLOCK_SIZE, nb, block_tables.shape[1], self.max_context_len,
+                             self.partition_size, self.ws_ptr, self.ws_bytes, _dtype_code(out), flags, _stream(dev))
+            else:
+                self.args = (_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                             _ptr(context_lens), float(scale), _ptr(out), B, hq, hkv, D, BLOCK_SIZE, nb,
+                             block_tables.shape[1], self.max_context_len, self.partition_size, self.ws_ptr,
+                             self.ws_bytes, _dtype_code(k_cache), _dtype_code(out), flags, _stream(dev))
         elif self.fp8:
             self.args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
                          _ptr(context_lens), float(scale), _ptr(out), B, hq, hkv, D, BLOCK_SIZE, nb,
@@ -271,6 +283,21 @@ def paged_attention_decode_append(q: torch.Tensor, k_new: torch.Tensor, v_new: t
     a = _DecodeArgs(q, k_cache, v_cache, block_tables, context_lens, scale, out, partition_size, max_context_len,
                     workspace, shared_blocks, k_new=k_new, v_new=v_new)
     _check(load_library().pkv_paged_attention_decode_append(*a.args), "paged_attention_decode_append")
+
+
+def paged_attention_decode_append_fp8(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                                      k_cache: torch.Tensor, v_cache: torch.Tensor, k_scale: torch.Tensor,
+                                      v_scale: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+                                      scale: float, out: torch.Tensor, *, partition_size: int = 0,
+                                      max_context_len: Optional[int] = None, workspace: Optional[torch.Tensor] = None,
+                                      shared_blocks: bool = False) -> None:
+    """``paged_attention_decode_append`` over fp8 (E4M3) pools: the bf16 rows ``k_new``/``v_new``
+    ``[B, Hkv, D]`` are stored as the codes ``reshape_and_cache_fp8`` would store (per-KV-head
+    ``k_scale``/``v_scale``), then the step attends as ``paged_attention_decode_fp8``; pools and output
+    equal those two calls, bit for bit."""
+    a = _DecodeArgs(q, k_cache, v_cache, block_tables, context_lens, scale, out, partition_size, max_context_len,
+                    workspace, shared_blocks, k_scale, v_scale, k_new=k_new, v_new=v_new)
+    _check(load_library().pkv_paged_attention_decode_append_fp8(*a.args), "paged_attention_decode_append_fp8")
 
 
 NOALLOC_SCRATCH_BYTES = 64 << 20   # the library's fixed decode scratch (PKV_NOALLOC_SCRATCH_BYTES)
@@ -322,7 +349,9 @@ def prepare_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out, 
 
 def run_decode(a: _DecodeArgs) -> None:
     lib = load_library()
-    if a.append:
+    if a.append and a.fp8:
+        _check(lib.pkv_paged_attention_decode_append_fp8(*a.args), "paged_attention_decode_append_fp8")
+    elif a.append:
         _check(lib.pkv_paged_attention_decode_append(*a.args), "paged_attention_decode_append")
     elif a.fp8:
         _check(lib.pkv_paged_attention_decode_fp8(*a.args), "paged_attention_decode_fp8")
@@ -332,7 +361,10 @@ def run_decode(a: _DecodeArgs) -> None:
 
 def run_partitions(a: _DecodeArgs) -> None:
     lib = load_library()
-    if a.append:
+    if a.append and a.fp8:
+        _check(lib.pkv_paged_attention_decode_append_partitions_fp8(*a.args),
+               "paged_attention_decode_append_partitions_fp8")
+    elif a.append:
         _check(lib.pkv_paged_attention_decode_append_partitions(*a.args), "paged_attention_decode_append_partitions")
     elif a.fp8:
         _check(lib.pkv_paged_attention_decode_partitions_fp8(*a.args), "paged_attention_decode_partitions_fp8")

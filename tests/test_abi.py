@@ -51,7 +51,7 @@ def test_single_hip_runtime_in_process(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pkv_abi_version() == 6
+    assert lib.pkv_abi_version() == 7
     for code in range(5):
         assert lib.pkv_status_string(code)
     assert lib.pkv_status_string(99) == b"unknown status"
@@ -121,6 +121,38 @@ def test_decode_append_validation(lib, partitions):
     assert dec_append(lib, partitions, ws=None) == WORKSPACE
     # an empty batch launches nothing
     assert dec_append(lib, partitions, B=0, kn=None, vn=None) == OK
+
+
+def dec_append_fp8(lib, partitions=False, **kw):
+    a = dict(q=FAKE, kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, ks=FAKE, vs=FAKE, bt=FAKE, lens=FAKE, scale=0.1, out=FAKE, B=4,
+             hq=32, hkv=8, D=128, bs=16, nb=100, maxblk=128, maxctx=2000, ps=0, ws=FAKE, wsb=0, outd=BF16, flags=0)
+    a.update(kw)
+    fn = (lib.pkv_paged_attention_decode_append_partitions_fp8 if partitions
+          else lib.pkv_paged_attention_decode_append_fp8)
+    return fn(a["q"], a["kn"], a["vn"], a["kc"], a["vc"], a["ks"], a["vs"], a["bt"], a["lens"], a["scale"], a["out"],
+              a["B"], a["hq"], a["hkv"], a["D"], a["bs"], a["nb"], a["maxblk"], a["maxctx"], a["ps"], a["ws"], a["wsb"],
+              a["outd"], a["flags"], None)
+
+
+@pytest.mark.parametrize("partitions", [False, True])
+def test_decode_append_fp8_validation(lib, partitions):
+    need = lib.pkv_decode_workspace_bytes(4, 32, 8, 128, 2000, 0, FP8)
+    ok = dict(wsb=need)
+    # the bf16 entry points point fp8 pools here
+    assert dec_append(lib, partitions, kvd=FP8, wsb=need) == UNSUPPORTED
+    assert b"append_fp8" in lib.pkv_last_error()
+    assert dec_append_fp8(lib, partitions, ks=None, **ok) == INVALID
+    assert b"k_scale" in lib.pkv_last_error()
+    assert dec_append_fp8(lib, partitions, vs=None, **ok) == INVALID
+    need17 = lib.pkv_decode_workspace_bytes(4, 8 * 17, 8, 128, 2000, 0, FP8)
+    assert dec_append_fp8(lib, partitions, hq=8 * 17, wsb=need17) == UNSUPPORTED
+    assert b"query heads per KV head" in lib.pkv_last_error()
+    assert dec_append_fp8(lib, partitions, kn=None, **ok) == INVALID
+    assert dec_append_fp8(lib, partitions, kn=FAKE + 8, **ok) == INVALID  # misaligned
+    assert dec_append_fp8(lib, partitions, D=96, **ok) == UNSUPPORTED
+    assert dec_append_fp8(lib, partitions, ws=None) == WORKSPACE
+    # an empty batch launches nothing, and needs no scales
+    assert dec_append_fp8(lib, partitions, B=0, kn=None, vn=None, ks=None, vs=None) == OK
 
 
 def test_decode_validation(lib):
