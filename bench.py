@@ -14,7 +14,10 @@ paged_attention_decode(_fp8), is timed beside it and reported under
 (fp32, continuous batching with prompt writes) take the two calls.  The default workload is the
 Llama-3-8B-shaped decode layer (64 sequences, 32 q / 8 KV heads, head_dim 128,
 bf16 KV, context lengths uniform on [128, 4096]).  Inputs are resident in HBM
-before timing starts.  To keep the 256 MB Infinity Cache from serving KV
+before timing starts, and before the W warmup steps the step runs untimed for
+at least --settle-ms (default 200 ms) so that the timed steps see the GPU's
+steady clock (with 20 warmup steps alone, about 1 ms of work, the fp8 decode
+step measured about 4 % slower).  To keep the 256 MB Infinity Cache from serving KV
 across steps, several copies of the pool are used in rotation, so a step never
 reads data a recent step read.
 
@@ -57,6 +60,17 @@ def family(workload: str) -> str:
 
 # static bf16 and fp8 decode workloads whose step can take the fused append
 FUSABLE_CONFIGS = ("llama3_8b_decode", "shared_prefix", "long_context", "llama3_8b_decode_fp8", "long_context_fp8")
+
+
+def settle(step, ms: float) -> None:
+    """Run ``step()`` untimed for at least ``ms`` milliseconds of wall time, the GPU kept busy, so that
+    what is timed next runs at the GPU's steady clock rather than while it ramps up."""
+    import torch
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(8):
+            step()
+        torch.cuda.synchronize()
 
 
 def traffic_file(workload: str, fused: bool = False) -> str:
@@ -420,6 +434,7 @@ def run_prefill(args):
         if ev is not None:
             ev[1].record()
 
+    settle(step, args.settle_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -440,7 +455,7 @@ def run_prefill(args):
     traffic = measured_traffic(b.name, "none")
     rec = {
         "metric": PREFILL_METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "settle_ms": args.settle_ms, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": b.name, "seed": b.seed, "num_seqs": b.num_seqs, "num_tokens": b.num_tokens,
                    "num_q_heads": b.num_q_heads, "num_kv_heads": b.num_kv_heads, "head_dim": b.head_dim,
@@ -508,6 +523,7 @@ def run_copy(args):
             if ev is not None:
                 ev[1].record()
         launches = 2
+    settle(step, args.settle_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -534,7 +550,7 @@ def run_copy(args):
                 "frac": round(per_dir / PEAK_HOST_LINK_GBS, 4), "traffic": None, "kernel": "copy_blocks_kernel",
                 "bytes_per_launch": moved // 2}
     rec = {"metric": COPY_METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-           "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+           "warmup": args.warmup, "settle_ms": args.settle_ms, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": args.config, "pairs_per_launch": n, "launches_per_step": launches,
                       "num_kv_heads": hkv, "head_dim": D, "block_bytes_per_pool": block_bytes,
@@ -770,6 +786,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="untimed run of the step before the warmup steps, in ms of wall time (0: none)")
     ap.add_argument("--config", default="llama3_8b_decode")
     ap.add_argument("--partition-size", type=int, default=-1,
                     help="0 = the library's balanced split; default: the workload's own (512 for long_context)")
@@ -1004,6 +1022,14 @@ def run_decode(args, config, partition_arg, steps, warmup, fused_flag, compare_f
 
     step = step_fused if fused else step_two_call
 
+    n_settle = [0]
+
+    def settle_step():
+        step(n_settle[0])
+        if compare:
+            (step_two_call if fused else step_fused)(n_settle[0])
+        n_settle[0] += 1
+    settle(settle_step, args.settle_ms)
     for i in range(warmup):
         step(i)
         if compare:
@@ -1058,6 +1084,7 @@ def run_decode(args, config, partition_arg, steps, warmup, fused_flag, compare_f
         "n_gpus": 1,
         "steps": steps,
         "warmup": warmup,
+        "settle_ms": args.settle_ms,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
