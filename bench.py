@@ -877,7 +877,7 @@ def main():
         lc = run_decode(args, "long_context", 512, args.steps, args.warmup, not args.two_call, True, False,
                         args.cpu_budget)
         keep = ("value", "unit", "ms_per_step", "step_ms_median", "step_ms_p10", "step_ms_p90", "frac_of_peak",
-                "host_enqueue_ms_per_step", "two_call", "fused",
+                "host_enqueue_ms_per_step", "two_call", "fused", "host_pack_h2d_ms", "tokens_per_s_with_host",
                 "tokens_per_s", "decode_kernel_ms", "decode_kernel_ms_median", "roofline", "step", "config",
                 "cpu_baseline", "input_generation_s")
         rec["long_context"] = {k: lc[k] for k in keep if k in lc}
@@ -1150,6 +1150,9 @@ def run_decode(args, config, partition_arg, steps, warmup, fused_flag, compare_f
         rec["identity_table"] = identity_table_comparison(b, kcs, vcs, gpu_steps[0], ps, steps, warmup, dec)
     try:
         rec["host_pack_h2d_ms"] = round(host_pack_ms(b), 4)
+        # with the host's packing and copies done before each step and not
+        # overlapped with the GPU (the serial case)
+        rec["tokens_per_s_with_host"] = round(b.num_seqs / ((ms_per_step + rec["host_pack_h2d_ms"]) / 1e3), 1)
     except Exception as e:  # aux figure only
         rec["host_pack_h2d_ms"] = f"unavailable: {e}"
     if not args.no_cpu_baseline:
