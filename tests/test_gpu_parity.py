@@ -284,6 +284,7 @@ def test_head_groupings(dtype, hq, hkv, D):
 
 @pytest.mark.parametrize("dtype,hq,hkv,D,ps,kind", [
     ("bf16", 8, 2, 128, 0, "skew"), ("bf16", 8, 2, 64, 0, "skew"), ("bf16", 6, 2, 128, 0, "short"),
+    ("bf16", 6, 2, 64, 0, "short"),
     ("f32", 3, 3, 64, 16, "short"), ("f32", 3, 3, 64, 64, "short")])
 def test_reduce_shapes(dtype, hq, hkv, D, ps, kind):
     """The split-K merge in each of its forms (for a part with 128 to 1024
