@@ -282,3 +282,21 @@ def test_kernel_source_hash_ignores_comments_only():
     assert bench._code_only(base) == bench._code_only(same)
     assert bench._code_only(base) != bench._code_only(diff)
     assert bench._code_only(base) != bench._code_only(lit)
+
+
+def test_committed_records_match_the_kernel_code():
+    """Every HBM-traffic record under profiles/ was taken on the kernel code in
+    the tree (bench.py drops a record whose key differs), and each has its
+    summary beside it."""
+    import glob
+    import json
+    import os
+
+    import bench
+    files = sorted(glob.glob(os.path.join(bench.ROOT, "profiles", "*_traffic_*.json")))
+    assert files, "no traffic records"
+    for f in files:
+        rec = json.load(open(f))
+        assert rec["source_sha256"] == bench.kernel_source_hash(rec["workload"]), f"{f} is stale"
+        summary = f.replace("_traffic_", "_").replace(".json", ".md")
+        assert os.path.exists(summary), f"{summary} missing"
